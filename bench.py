@@ -1,0 +1,289 @@
+#!/usr/bin/env python3
+"""Benchmark of the rotated low-bit linear layer on one MI355X.
+
+Headline workload: the online W8A8 rotated linear at DiT image shape -- 4608 tokens (4096 latent
+patches + 512 text tokens) x d_in 4096 -> d_out 16384 (the MLP-up linear of a 7B, 32-layer
+single-stream DiT), bf16 activations in, bf16 out, INT8 weights rotated and quantised offline with
+the same RPBH descriptor.  One step = one pass of the online path over one batch:
+    rtq_quantize_rows (gather + sign + FWHT-64 + per-token INT8)   [HBM-bound]
+    rtq_qgemm         (INT8 MFMA product + scale epilogue)          [MFMA-bound]
+which is exactly the pair of launches rtq_rotated_qlinear makes; they are issued separately so
+HIP events on the same stream time each kernel inside the timed region.
+
+value      = 2*T*d_in*d_out per step / step time, in TFLOP/s (integer ops, i.e. TOP/s).
+roofline   = the INT8 GEMM against the dense INT8 MFMA peak (5.0 POP/s); the RPBH+quantise kernel
+             is reported against HBM (8 TB/s) in rpbh_roofline.
+cpu_baseline = the CPU oracle (dense Pi product, int64 triple loop) on a bounded token sample,
+             scaled linearly to the full step.
+Also reported: the offline weight rotate-quantise of one DiT block's four linears, and the W4A4
+(4608x4096->4096) and W2A4 (4608x16384->4096) codebook layers.
+Inputs are synthetic (seeded; see workloads/), resident in HBM before timing; the activations
+rotate over enough copies (> 512 MB) that the 256 MB Infinity Cache cannot serve them.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "rotated W8A8 qlinear TFLOP/s (% INT8 MFMA peak) + RPBH-quantize GB/s (% HBM)"
+PEAK_INT8_TOPS = 5000.0     # dense INT8 MFMA, MI355X
+PEAK_F16_TFLOPS = 2500.0    # dense fp16/bf16 MFMA, MI355X
+PEAK_HBM_GBPS = 8000.0      # HBM3E
+
+
+def _bf16_dev(bits, torch):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def _copies(t, min_bytes, torch):
+    n = max(3, -(-min_bytes // (t.numel() * t.element_size())))
+    return [t.clone() for _ in range(n)]
+
+
+def _time_pairs(steps, launch_a, launch_b, torch):
+    """Run `steps` iterations of (a, b) with events around each launch on the current stream."""
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record()
+        launch_a(i)
+        ev[i][1].record()
+        launch_b(i)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ta = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(steps)])  # ms
+    tb = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(steps)])
+    return wall, ta, tb
+
+
+def bench_w8a8(args, torch, rtq, workloads):
+    d, N = workloads.DIT_HIDDEN, workloads.DIT_MLP
+    xh = workloads.dit_activations_bf16(d)
+    T = xh.shape[0]
+    wh = workloads.dit_weight_bf16("mlp_up")
+    R = rtq.Rpbh.from_seed(workloads.RPBH_SEED[d], d)
+    w = _bf16_dev(wh, torch)
+    wq = torch.empty((N, d), dtype=torch.int8, device="cuda")
+    ws = torch.empty(N, dtype=torch.bfloat16, device="cuda")
+    rtq.quantize_rows(w, wq, ws, R, rtq.RTQ_INT8)           # offline, not timed here
+    del w
+    xs = _copies(_bf16_dev(xh, torch), 512 << 20, torch)
+    codes = torch.empty((T, d), dtype=torch.int8, device="cuda")
+    scale = torch.empty(T, dtype=torch.float32, device="cuda")
+    y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+
+    def quant(i):
+        rtq.quantize_rows(xs[i % len(xs)], codes, scale, R, rtq.RTQ_INT8)
+
+    def gemm(i):
+        rtq.qgemm(codes, scale, wq, ws, y, d)
+
+    for i in range(args.warmup):
+        quant(i)
+        gemm(i)
+    wall, tq, tg = _time_pairs(args.steps, quant, gemm, torch)
+    # cross-check: the fused entry point does the same two launches
+    ws_bytes = rtq.rotated_qlinear_workspace(T, d)
+    work = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    for i in range(3):
+        rtq.rotated_qlinear(xs[i % len(xs)], R, wq, ws, y, workspace=work)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        rtq.rotated_qlinear(xs[i % len(xs)], R, wq, ws, y, workspace=work)
+    torch.cuda.synchronize()
+    fused_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    flops = 2.0 * T * d * N
+    q_bytes = T * (2 * d + d + 4)                           # bf16 in, int8 codes out, fp32 scale out
+    return {
+        "T": T, "d": d, "N": N, "wall_s": wall, "step_ms": wall * 1e3 / args.steps,
+        "quant_ms": float(tq.mean()), "gemm_ms": float(tg.mean()),
+        "quant_ms_median": float(np.median(tq)), "gemm_ms_median": float(np.median(tg)),
+        "flops": flops, "quant_bytes": q_bytes, "fused_step_ms": fused_ms,
+    }
+
+
+def bench_offline(args, torch, rtq, workloads):
+    """Offline rotate + INT8 quantise of one DiT block's four linears (bf16 in, int8 + bf16 scale out)."""
+    mats = []
+    total = 0
+    for name, n_out, d_in in workloads.DIT_LINEARS:
+        w = _bf16_dev(workloads.dit_weight_bf16(name), torch)
+        R = rtq.Rpbh.from_seed(workloads.RPBH_SEED[d_in], d_in)
+        q = torch.empty((n_out, d_in), dtype=torch.int8, device="cuda")
+        s = torch.empty(n_out, dtype=torch.bfloat16, device="cuda")
+        mats.append((w, R, q, s))
+        total += n_out * d_in * 3 + n_out * 2
+
+    def run():
+        for w, R, q, s in mats:
+            rtq.quantize_rows(w, q, s, R, rtq.RTQ_INT8)
+
+    for _ in range(max(1, args.warmup // 2)):
+        run()
+    reps = max(3, args.steps // 5)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return {"bytes": total, "ms": ms, "GB/s": total / (ms * 1e-3) / 1e9}
+
+
+def bench_codebook(args, torch, rtq, workloads, variant):
+    if variant == "w4a4":
+        d, N, bits_w = workloads.DIT_HIDDEN, workloads.DIT_HIDDEN, 4
+        wh = workloads.w4a4_weight_bf16()
+    else:
+        d, N, bits_w = workloads.DIT_MLP, workloads.DIT_HIDDEN, 2
+        wh = workloads.w2a4_weight_bf16()
+    xh = workloads.dit_activations_bf16(d)
+    T = xh.shape[0]
+    R = rtq.Rpbh.from_seed(workloads.RPBH_SEED[d], d)
+    cb_a, cb_w = rtq.Codebook.for_dim(d, 4), rtq.Codebook.for_dim(d, bits_w)
+    w = _bf16_dev(wh, torch)
+    wc = torch.empty((N, d * bits_w // 8), dtype=torch.uint8, device="cuda")
+    wn = torch.empty(N, dtype=torch.bfloat16, device="cuda")
+    rtq.quantize_rows(w, wc, wn, R, rtq.RTQ_CODEBOOK, cb_w, 0.0)
+    del w
+    xs = _copies(_bf16_dev(xh, torch), 512 << 20, torch)
+    codes = torch.empty((T, d // 2), dtype=torch.uint8, device="cuda")
+    norm = torch.empty(T, dtype=torch.float32, device="cuda")
+    y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+
+    def quant(i):
+        rtq.quantize_rows(xs[i % len(xs)], codes, norm, R, rtq.RTQ_CODEBOOK, cb_a, 1e-8)
+
+    def gemm(i):
+        rtq.qgemm(codes, norm, wc, wn, y, d, rtq.RTQ_CODEBOOK, cb_a, cb_w)
+
+    for i in range(args.warmup):
+        quant(i)
+        gemm(i)
+    steps = max(5, args.steps // 2)
+    wall, tq, tg = _time_pairs(steps, quant, gemm, torch)
+    flops = 2.0 * T * d * N
+    q_bytes = T * (2 * d + d // 2 + 4)
+    return {"T": T, "d": d, "N": N, "step_ms": wall * 1e3 / steps, "quant_ms": float(tq.mean()),
+            "gemm_ms": float(tg.mean()), "TFLOP/s": flops / (wall / steps) / 1e12,
+            "gemm_TFLOP/s": flops / (tg.mean() * 1e-3) / 1e12, "gemm_frac_f16_peak":
+            flops / (tg.mean() * 1e-3) / 1e12 / PEAK_F16_TFLOPS,
+            "rpbh_GB/s": q_bytes / (tq.mean() * 1e-3) / 1e9}
+
+
+def cpu_baseline(workloads):
+    """The oracle, as written, on a bounded token sample of the W8A8 step, scaled to the full step:
+    per-token online cost (dense Pi rotation + INT8 quantise) and per-(token, channel) GEMM cost are
+    measured on the sample and extrapolated linearly to 4608 tokens x 16384 channels."""
+    import oracle
+    d, N = workloads.DIT_HIDDEN, workloads.DIT_MLP
+    xh = workloads.dit_activations_bf16(d)
+    T = xh.shape[0]
+    perm, signs = oracle.rpbh_descriptor(workloads.RPBH_SEED[d], d)
+    pi = oracle.rpbh_dense(d, 64, perm, signs)              # set-up, once per d: not timed
+    tok = 32
+    ch = 2048
+    wsamp = workloads.bf16_bits_to_f32(workloads.dit_weight_bf16("mlp_up")[:ch])
+    wq = oracle.weights_int8(wsamp, pi, True)               # offline: not timed
+    x = workloads.bf16_bits_to_f32(xh[:tok])
+    t0 = time.perf_counter()
+    act = oracle.activations_int8(x, pi)
+    t1 = time.perf_counter()
+    acc = oracle.gemm_int8(act["q"], wq["q"])
+    oracle.rescale_int8(acc, act["scale"], wq["scale"])
+    t2 = time.perf_counter()
+    per_token = (t1 - t0) / tok
+    per_dot = (t2 - t1) / (tok * ch)
+    full = T * per_token + T * N * per_dot
+    return {"value": 2.0 * T * d * N / full / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{tok} tokens through the oracle's online W8A8 path (dense Pi product, INT8 quantise, "
+                      f"int64 triple-loop GEMM against {ch} of the 16384 weight rows, rescale); per-token and "
+                      f"per-output costs scaled linearly to 4608 x 16384 (est. {full:.1f} s per step)",
+            "sample_seconds": t2 - t0}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
+    ap.add_argument("--only", choices=["w8a8", "all"], default="all",
+                    help="w8a8: time only the headline step (profiling runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the rotated linear is measured at "
+                                   "its single-GPU shape; multi-GPU sharding is not part of this build",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import rotation_then_quantize_amd as rtq
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    rtq.load_library()
+
+    r = bench_w8a8(args, torch, rtq, workloads)
+    extra = {}
+    if args.only == "all":
+        extra["offline_weight_rotate_quantize"] = bench_offline(args, torch, rtq, workloads)
+        extra["w4a4_dit_attn_out_4608x4096x4096"] = bench_codebook(args, torch, rtq, workloads, "w4a4")
+        extra["w2a4_dit_mlp_down_4608x16384x4096"] = bench_codebook(args, torch, rtq, workloads, "w2a4")
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(workloads)
+
+    step_s = r["step_ms"] * 1e-3
+    value = r["flops"] / step_s / 1e12
+    gemm_tops = r["flops"] / (r["gemm_ms"] * 1e-3) / 1e12
+    q_gbps = r["quant_bytes"] / (r["quant_ms"] * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["step_ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "w8a8_dit_mlp_up_4608x4096x16384_bf16", "tokens": r["T"], "d_in": r["d"],
+                   "d_out": r["N"], "io": "bf16", "weights": "int8 per-row, bf16 scales",
+                   "activations": "int8 per-token, fp32 scales", "rotation": "RPBH h=64"},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
+                     "frac": round(gemm_tops / PEAK_INT8_TOPS, 4), "traffic": None,
+                     "kernel": "gemm_i8_kernel", "work_per_launch": r["flops"], "avg_ms": round(r["gemm_ms"], 5)},
+        "rpbh_roofline": {"bound": "hbm", "achieved": round(q_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                          "frac": round(q_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                          "kernel": "rpbh_rows_kernel (int8)", "bytes_per_launch": r["quant_bytes"],
+                          "avg_ms": round(r["quant_ms"], 5)},
+        "fused_entry_ms_per_step": round(r["fused_step_ms"], 4),
+        "cpu_baseline": None if cpu is None else {k: (round(v, 6) if isinstance(v, float) else v)
+                                                 for k, v in cpu.items()},
+    }
+    if extra:
+        out["extra"] = extra
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

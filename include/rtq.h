@@ -1,0 +1,157 @@
+/*
+ * rtq.h -- C ABI of librtq: rotate-then-quantize linear layers on AMD MI355X (gfx950).
+ *
+ * The method (OrbitQuant article, hotelren.com/news/3376620, sections 2.1-2.3):
+ *   offline   W' = W Pi_d^T; each row of W' is quantised (INT8 with a per-row scale, or a bf16
+ *             row norm r' plus Lloyd-Max codes of the direction w'/r');
+ *   online    x' = Pi_d x; per token the scale (INT8) or norm s = ||x'|| (codebook) is taken,
+ *             x' is quantised, and the quantised product W'x' is formed; Pi^T Pi = I cancels,
+ *             so no inverse rotation runs at inference time;
+ *   Pi_d      = blkdiag(H_64 D_1, ..., H_64 D_{d/64}) P_pi  (random-permutation block Hadamard,
+ *             RPBH), with H_64 the natural-order Walsh-Hadamard matrix scaled by 1/8, D_i
+ *             Rademacher sign matrices and P_pi a permutation acting as a gather,
+ *             (P_pi x)_j = x[perm[j]].
+ * The uniform INT8 variant (q = round(v/s), s = max|v|/127, symmetric) follows
+ * "量化旋转主模型是什么？一文读懂低比特图像生成模型" (cloud.baidu.com/article/9432521), section 4.
+ *
+ * Conventions shared by every call
+ *   - Row-major storage.  x is [rows][d]; weights are [N][d] as in y = W x; y is [T][N].
+ *   - Device pointers are allocated and freed by the caller; the library allocates no device
+ *     memory and keeps no state besides a thread-local error string and per-device kernel
+ *     attributes.  Device pointers must be 16-byte aligned (else RTQ_ERR_MISALIGNED).
+ *   - Device calls are asynchronous on `stream` (a hipStream_t passed as void*, NULL = the
+ *     default stream).  Arguments are checked on the host before anything is enqueued; on any
+ *     non-OK status nothing was enqueued and rtq_last_error() describes the problem.  Faults
+ *     during execution surface at the caller's next synchronisation.
+ *   - d must be a multiple of 64 with d/64 a power of two, 64 <= d <= 16384 (the block size h is
+ *     64); other shapes return RTQ_ERR_UNSUPPORTED.
+ *   - Inputs are finite.  perm must be a permutation of 0..d-1 and signs must be +1/-1; other
+ *     values give unspecified results (never an out-of-bounds access).
+ */
+#ifndef RTQ_H
+#define RTQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RTQ_OK = 0,
+    RTQ_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, inconsistent arguments    */
+    RTQ_ERR_UNSUPPORTED = -2, /* valid but not implemented: d shape, dtype combination, bits */
+    RTQ_ERR_MISALIGNED = -3,  /* a device pointer is not 16-byte aligned                     */
+    RTQ_ERR_HIP = -4          /* the HIP runtime refused a call (message from hipGetErrorString) */
+} rtq_status;
+
+typedef enum {
+    RTQ_F32 = 0,  /* IEEE binary32                                               */
+    RTQ_BF16 = 1, /* bfloat16 bit patterns (uint16), rounded to nearest-even      */
+    RTQ_I32 = 2   /* int32 accumulators: rtq_qgemm output in INT8 mode only      */
+} rtq_dtype;
+
+typedef enum {
+    RTQ_INT8 = 0,     /* symmetric INT8, scale = max|v|/127, codes in [-127, 127]       */
+    RTQ_CODEBOOK = 1  /* L2 norm + Lloyd-Max direction codes of `bits` bits, packed     */
+} rtq_qmode;
+
+/* RPBH descriptor (OrbitQuant article, section 2.3).  perm (int32[d]) and signs (int8[d], +-1)
+ * are DEVICE pointers; h must be 64.  The same descriptor must rotate a layer's weights offline
+ * and its activations online (section 2.2: the two rotations cancel only if they are equal). */
+typedef struct {
+    int32_t d;
+    int32_t h;
+    const int32_t* perm;
+    const int8_t* signs;
+} rtq_rpbh;
+
+/* Lloyd-Max codebook for N(0, 1/d) (OrbitQuant article, sections 1 and 4.2).  centroids holds
+ * 2^bits ascending fp32 values, boundaries the 2^bits - 1 fp32 cell edges; DEVICE pointers.
+ * Code k stands for centroids[k]; a value u gets code #{k : boundaries[k] < u}. */
+typedef struct {
+    int32_t bits;
+    const float* centroids;
+    const float* boundaries;
+} rtq_codebook;
+
+/* ---------------------------------------------------------------- host-only helpers */
+
+/* Build an RPBH descriptor from a seed (OrbitQuant article, section 6.3 asks for a standardised
+ * generator).  SplitMix64 stream from `seed`; perm starts as the identity and is shuffled by
+ * Fisher-Yates from index d-1 down to 1 (j = next() mod (i+1)); then signs[k] = -1 if the top bit
+ * of next() is set, else +1.  perm_out (int32[d]) and signs_out (int8[d]) are HOST pointers.
+ * Errors: RTQ_ERR_INVALID_ARG for null pointers or d <= 0 or d % h != 0; h must be 64. */
+rtq_status rtq_rpbh_make(uint64_t seed, int32_t d, int32_t h, int32_t* perm_out, int8_t* signs_out);
+
+/* Lloyd-Max codebook for N(0, 1/d) with 2^bits levels (OrbitQuant article, section 4.2: one
+ * codebook per input dimension, computed offline).  Computed in double on N(0,1), made exactly
+ * symmetric, scaled by 1/sqrt(d) and rounded to fp32; each boundary is the fp32 rounding of the
+ * midpoint of the two neighbouring scaled centroids.  centroids_out (float[2^bits]) and
+ * boundaries_out (float[2^bits - 1]) are HOST pointers.  bits in 1..8. */
+rtq_status rtq_lloyd_max(int32_t d, int32_t bits, float* centroids_out, float* boundaries_out);
+
+/* ---------------------------------------------------------------- device calls */
+
+/* y = Pi x for each row (inverse = 0), or x = Pi^T y (inverse = 1): the RPBH rotation alone
+ * (OrbitQuant article, sections 2.2-2.3).  x: [rows][R->d] of xt (F32 or BF16); y: [rows][R->d] of
+ * yt (F32 or BF16).  The transform is evaluated exactly in double and rounded once to fp32; a
+ * BF16 output is that fp32 value rounded to nearest-even.  rows == 0 is a no-op. */
+rtq_status rtq_rpbh_rotate(const void* x, rtq_dtype xt, void* y, rtq_dtype yt, int64_t rows,
+                           const rtq_rpbh* R, int32_t inverse, void* stream);
+
+/* Rotate (when R != NULL) and quantise rows (OrbitQuant article, section 2.1 steps 1-3 for weights,
+ * section 2.2 steps 1-4 for activations; the INT8 rule of cloud.baidu.com/article/9432521, section 4).
+ *   x      [rows][d] of xt (F32 or BF16).  R == NULL: x is already rotated.  R != NULL: R->d == d.
+ *   INT8:      s = max_j |x'_j| / 127 in fp32, stored as scale_t (F32 or BF16); the STORED value
+ *              divides: q_j = round-half-even(x'_j / s), clamped to [-127, 127]; s == 0 gives q = 0.
+ *              codes: int8[rows][d].  cb must be NULL.  eps is ignored.
+ *   CODEBOOK:  s = ||x'||_2 (summed in double, rounded to fp32); u_j = x'_j / (s + eps) in fp32
+ *              (0 when s + eps == 0); code_j = #{k : boundaries[k] < u_j}.  The norm s is stored as
+ *              scale_t: BF16 for weights (eps = 0), F32 for activations (eps > 0, e.g. 1e-8).
+ *              codes: uint8[rows][d * bits / 8], element j at byte j*bits/8, bit (j mod 8/bits)*bits
+ *              (least significant first).  cb->bits must be 2 or 4.
+ *   scale  [rows] of scale_t.
+ * rows == 0 is a no-op. */
+rtq_status rtq_quantize_rows(const void* x, rtq_dtype xt, int64_t rows, int32_t d, const rtq_rpbh* R,
+                             rtq_qmode mode, const rtq_codebook* cb, float eps, void* codes, void* scale,
+                             rtq_dtype scale_t, void* stream);
+
+/* The quantised product in which the rotation has cancelled (OrbitQuant article, section 2.2:
+ * W'x' = W Pi^T Pi x).
+ *   a_codes [T][d] (INT8) or [T][d*bits_a/8] packed (CODEBOOK), a_scale fp32[T] (INT8 scale or
+ *   token norm); w_codes [N][d] or [N][d*bits_w/8], w_scale [N] of w_scale_t (F32 or BF16).
+ *   INT8:      acc[t][n] = sum_j a[t][j] w[n][j] exactly in int32 (|acc| <= 127^2 d);
+ *              y = acc * a_scale[t] * w_scale[n] (fp32 arithmetic), stored as yt (F32 or BF16);
+ *              yt == RTQ_I32 stores acc itself.  cb_a and cb_w must be NULL.
+ *   CODEBOOK:  y = w_scale[n] * a_scale[t] * sum_j cb_w->centroids[qw] * cb_a->centroids[qa],
+ *              accumulated in fp32 from fp16 copies of the centroids; yt F32 or BF16.
+ *              cb_a->bits must be 4; cb_w->bits 2 or 4.
+ * T == 0 is a no-op. */
+rtq_status rtq_qgemm(const void* a_codes, const float* a_scale, int64_t T, const void* w_codes,
+                     const void* w_scale, rtq_dtype w_scale_t, int64_t N, int32_t d, rtq_qmode mode,
+                     const rtq_codebook* cb_a, const rtq_codebook* cb_w, void* y, rtq_dtype yt, void* stream);
+
+/* The online layer: rtq_quantize_rows(x, R, mode, cb_a, eps = 1e-8 (CODEBOOK) ...) into `workspace`
+ * followed by rtq_qgemm on the same stream (OrbitQuant article, section 2.2, steps 1-5 and the
+ * cancellation).  Weights come from rtq_quantize_rows with the SAME descriptor R.
+ *   workspace: device memory of at least rtq_rotated_qlinear_workspace(T, R->d, mode, bits_a) bytes,
+ *   16-byte aligned; its contents on return are the activation codes and scales. */
+rtq_status rtq_rotated_qlinear(const void* x, rtq_dtype xt, int64_t T, const rtq_rpbh* R, const void* w_codes,
+                               const void* w_scale, rtq_dtype w_scale_t, int64_t N, rtq_qmode mode,
+                               const rtq_codebook* cb_a, const rtq_codebook* cb_w, void* y, rtq_dtype yt,
+                               void* workspace, size_t ws_bytes, void* stream);
+
+/* Bytes of workspace rtq_rotated_qlinear needs (codes + fp32 scales, each 256-byte aligned).
+ * bits_a is ignored for RTQ_INT8.  Returns 0 for invalid arguments. */
+size_t rtq_rotated_qlinear_workspace(int64_t T, int32_t d, rtq_qmode mode, int32_t bits_a);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* rtq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RTQ_H */

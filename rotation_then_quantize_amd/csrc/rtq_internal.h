@@ -1,0 +1,71 @@
+// rtq_internal.h -- launchers shared between the C-ABI layer and the HIP kernels of librtq.
+// Not part of the public interface (include/rtq.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rtq {
+
+// What the RPBH row kernel writes for each row.
+enum RowOut : int {
+    kRowRotF32 = 0,   // rotated row, fp32
+    kRowRotBF16 = 1,  // rotated row, bf16 (RNE of the fp32 value)
+    kRowInt8 = 2,     // symmetric INT8 codes + per-row scale
+    kRowCode4 = 3,    // 4-bit Lloyd-Max codes (packed) + row norm
+    kRowCode2 = 4,    // 2-bit Lloyd-Max codes (packed) + row norm
+};
+
+struct RowArgs {
+    const void* x;          // [rows][d] fp32 or bf16
+    bool x_bf16;
+    int64_t rows;
+    int d;
+    const int32_t* perm;    // nullptr: rows are already rotated
+    const int8_t* signs;
+    RowOut out_kind;
+    void* out;              // rotated rows or codes
+    void* scale;            // [rows] fp32 or bf16 (quantising kinds only)
+    bool scale_bf16;
+    const float* bounds;    // codebook boundaries (device), 2^bits - 1 entries
+    float eps;
+};
+
+hipError_t launch_rpbh_rows(const RowArgs& a, hipStream_t stream);
+
+// x = Pi^T y for each row (rotation inverse), fp32/bf16 in and out.
+hipError_t launch_rpbh_inverse(const void* y, bool y_bf16, void* x, bool x_bf16, int64_t rows, int d,
+                               const int32_t* perm, const int8_t* signs, hipStream_t stream);
+
+struct GemmI8Args {
+    const int8_t* a;        // [T][d]
+    const float* a_scale;   // [T]
+    const int8_t* w;        // [N][d]
+    const void* w_scale;    // [N] fp32 or bf16
+    bool w_scale_bf16;
+    int64_t T, N;
+    int d;
+    void* y;                // [T][N]
+    int y_kind;             // 0 fp32, 1 bf16, 2 raw int32
+};
+
+hipError_t launch_gemm_i8(const GemmI8Args& g, hipStream_t stream);
+
+struct GemmLutArgs {
+    const uint8_t* a;         // [T][d*bits_a/8] packed codes
+    const float* a_scale;     // [T] token norms
+    const uint8_t* w;         // [N][d*bits_w/8] packed codes
+    const void* w_scale;      // [N] fp32 or bf16 row norms
+    bool w_scale_bf16;
+    const float* ca;          // activation centroids (device), 2^bits_a
+    const float* cw;          // weight centroids (device), 2^bits_w
+    int bits_a, bits_w;
+    int64_t T, N;
+    int d;
+    void* y;                  // [T][N]
+    int y_kind;               // 0 fp32, 1 bf16
+};
+
+hipError_t launch_gemm_lut(const GemmLutArgs& g, hipStream_t stream);
+
+}  // namespace rtq

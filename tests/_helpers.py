@@ -1,0 +1,61 @@
+"""Shared helpers for the GPU parity tests (marshalling and comparison only)."""
+import functools
+import math
+
+import numpy as np
+
+import oracle
+
+
+def to_dev(a, dtype=None):
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def bf16_host(t):
+    """bf16 device tensor -> uint16 bit patterns on the host."""
+    import torch
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@functools.lru_cache(maxsize=4)
+def dense_pi(seed: int, d: int):
+    perm, signs = oracle.rpbh_descriptor(seed, d)
+    return oracle.rpbh_dense(d, 64, perm, signs)
+
+
+def int8_mismatches_allowed(q_gpu, q_orc, pre_orc):
+    """North-star allowance for INT8 codes: equal, or one step apart where the oracle's fp32
+    pre-rounding value lies within 1e-6 relative of the rounding boundary k + 1/2."""
+    diff = q_gpu.astype(np.int32) - q_orc.astype(np.int32)
+    bad = diff != 0
+    if not bad.any():
+        return 0, 0
+    t = pre_orc[bad].astype(np.float64)
+    half = np.floor(t) + 0.5
+    near = np.abs(t - half) <= 1e-6 * np.maximum(np.abs(half), 1.0)
+    ok = (np.abs(diff[bad]) == 1) & near
+    return int(bad.sum()), int((~ok).sum())
+
+
+def codebook_mismatches_allowed(c_gpu, c_orc, u_orc, bounds, d):
+    """Codes equal, or one cell apart where the oracle's u lies within 1e-6 * max(|t_k|, 1/sqrt(d))
+    of the boundary t_k between them."""
+    diff = c_gpu.astype(np.int32) - c_orc.astype(np.int32)
+    bad = diff != 0
+    if not bad.any():
+        return 0, 0
+    u = u_orc[bad].astype(np.float64)
+    tb = bounds.astype(np.float64)
+    k = np.argmin(np.abs(u[:, None] - tb[None, :]), axis=1)
+    tol = 1e-6 * np.maximum(np.abs(tb[k]), 1.0 / math.sqrt(d))
+    ok = (np.abs(diff[bad]) == 1) & (np.abs(u - tb[k]) <= tol)
+    return int(bad.sum()), int((~ok).sum())
+
+
+def rel_fro(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))

@@ -1,0 +1,179 @@
+"""CPU tests of librtq's C ABI: exported symbols, host-only helpers against the oracle, and
+argument validation (which runs before any HIP call, so no GPU is needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+import rotation_then_quantize_amd as rtq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rtq.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rtq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = rtq.load_library()
+    names = _declared()
+    assert set(names) == set(rtq.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", rtq.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s(rtq_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_library_is_built_for_gfx950():
+    sec = subprocess.run(["readelf", "-S", rtq.LIB_PATH], capture_output=True, text=True).stdout
+    assert ".hip_fatbin" in sec
+    blob = open(rtq.LIB_PATH, "rb").read()
+    assert b"amdgcn-amd-amdhsa--gfx950" in blob
+
+
+@pytest.mark.parametrize("d", [64, 256, 4096, 16384])
+def test_rpbh_make_matches_oracle_generator(d):
+    for seed in (0, 1, 2003, 2013, 0xFFFFFFFFFFFFFFFF):
+        p1, s1 = rtq.rpbh_make(seed, d)
+        p2, s2 = oracle.rpbh_descriptor(seed, d)
+        assert np.array_equal(p1, p2) and np.array_equal(s1, s2)
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("d", [256, 4096, 16384, 1000])
+def test_lloyd_max_matches_oracle_within_one_ulp(d, bits):
+    c, t = rtq.lloyd_max(d, bits)
+    ref = oracle.lloyd_max(bits, d)
+    ulp_c = np.spacing(np.abs(ref["centroids"]))
+    assert np.all(np.abs(c - ref["centroids"]) <= ulp_c)
+    tb = ref["boundaries"]
+    ulp_t = np.spacing(np.maximum(np.abs(tb), np.float32(1e-30)))
+    assert np.all(np.abs(t - tb) <= ulp_t)
+    # in practice they agree bit for bit
+    assert np.array_equal(c, ref["centroids"]) and np.array_equal(t, tb)
+
+
+_R = rtq._Rpbh
+_C = rtq._Codebook
+
+
+A = 0x10000  # a fake, 16-byte aligned "device" address: never dereferenced by the host checks
+
+
+def test_host_helper_errors():
+    lib = rtq.load_library()
+    perm = np.empty(64, np.int32)
+    signs = np.empty(64, np.int8)
+    assert lib.rtq_rpbh_make(1, 64, 32, perm.ctypes.data, signs.ctypes.data) == rtq.RTQ_ERR_UNSUPPORTED
+    assert lib.rtq_rpbh_make(1, 100, 64, perm.ctypes.data, signs.ctypes.data) == rtq.RTQ_ERR_INVALID_ARG
+    assert lib.rtq_rpbh_make(1, 64, 64, None, signs.ctypes.data) == rtq.RTQ_ERR_INVALID_ARG
+    assert "NULL" in rtq.last_error()
+    c = np.empty(16, np.float32)
+    t = np.empty(15, np.float32)
+    assert lib.rtq_lloyd_max(256, 9, c.ctypes.data, t.ctypes.data) == rtq.RTQ_ERR_INVALID_ARG
+    assert lib.rtq_lloyd_max(0, 4, c.ctypes.data, t.ctypes.data) == rtq.RTQ_ERR_INVALID_ARG
+    assert lib.rtq_lloyd_max(256, 4, c.ctypes.data, t.ctypes.data) == rtq.RTQ_OK
+    assert rtq.last_error() == ""
+
+
+def test_quantize_rows_validation():
+    lib = rtq.load_library()
+    R = _R(256, 64, A, A)
+    cb = _C(4, A, A)
+    q = lib.rtq_quantize_rows
+    ok_args = dict(x=A, xt=rtq.RTQ_BF16, rows=8, d=256, R=ctypes.byref(R), mode=rtq.RTQ_INT8, cb=None, eps=0.0,
+                   codes=A, scale=A, st=rtq.RTQ_F32)
+
+    def call(**kw):
+        a = dict(ok_args, **kw)
+        return q(a["x"], a["xt"], a["rows"], a["d"], a["R"], a["mode"], a["cb"], ctypes.c_float(a["eps"]),
+                 a["codes"], a["scale"], a["st"], None)
+
+    assert call(d=100) == rtq.RTQ_ERR_INVALID_ARG                      # d % 64
+    assert call(d=192, R=None) == rtq.RTQ_ERR_UNSUPPORTED              # 3 blocks: not a power of two
+    assert call(d=32768, R=None) == rtq.RTQ_ERR_UNSUPPORTED            # beyond 16384
+    assert call(d=512) == rtq.RTQ_ERR_INVALID_ARG                      # descriptor d mismatch
+    assert call(x=None) == rtq.RTQ_ERR_INVALID_ARG
+    assert call(x=A + 8) == rtq.RTQ_ERR_MISALIGNED
+    assert call(codes=A + 4) == rtq.RTQ_ERR_MISALIGNED
+    assert call(xt=rtq.RTQ_I32) == rtq.RTQ_ERR_UNSUPPORTED
+    assert call(rows=-1) == rtq.RTQ_ERR_INVALID_ARG
+    assert call(cb=ctypes.byref(cb)) == rtq.RTQ_ERR_INVALID_ARG         # INT8 takes no codebook
+    assert call(mode=rtq.RTQ_CODEBOOK) == rtq.RTQ_ERR_INVALID_ARG       # codebook missing
+    assert call(mode=rtq.RTQ_CODEBOOK, cb=ctypes.byref(_C(3, A, A))) == rtq.RTQ_ERR_UNSUPPORTED
+    assert call(mode=rtq.RTQ_CODEBOOK, cb=ctypes.byref(cb), eps=-1.0) == rtq.RTQ_ERR_INVALID_ARG
+    assert call(mode=7) == rtq.RTQ_ERR_INVALID_ARG
+    R_bad_h = _R(256, 32, A, A)
+    assert call(R=ctypes.byref(R_bad_h)) == rtq.RTQ_ERR_UNSUPPORTED
+    R_misaligned = _R(256, 64, A + 2, A)
+    assert call(R=ctypes.byref(R_misaligned)) == rtq.RTQ_ERR_MISALIGNED
+    # zero rows: valid, nothing launched, no GPU needed
+    assert call(rows=0) == rtq.RTQ_OK
+
+
+def test_qgemm_and_qlinear_validation():
+    lib = rtq.load_library()
+    cb4 = _C(4, A, A)
+    cb2 = _C(2, A, A)
+    g = lib.rtq_qgemm
+    base = [A, A, 16, A, A, rtq.RTQ_BF16, 32, 256, rtq.RTQ_INT8, None, None, A, rtq.RTQ_BF16, None]
+
+    def call(idx_vals):
+        a = list(base)
+        for i, v in idx_vals.items():
+            a[i] = v
+        return g(*a)
+
+    assert call({6: 0}) == rtq.RTQ_ERR_INVALID_ARG                       # N = 0
+    assert call({7: 100}) == rtq.RTQ_ERR_INVALID_ARG                     # d % 64
+    assert call({11: A + 1}) == rtq.RTQ_ERR_MISALIGNED                   # y
+    assert call({9: ctypes.byref(cb4)}) == rtq.RTQ_ERR_INVALID_ARG        # codebooks with INT8
+    assert call({8: rtq.RTQ_CODEBOOK}) == rtq.RTQ_ERR_INVALID_ARG         # codebooks missing
+    assert call({8: rtq.RTQ_CODEBOOK, 9: ctypes.byref(cb2), 10: ctypes.byref(cb2)}) == rtq.RTQ_ERR_UNSUPPORTED
+    assert call({8: rtq.RTQ_CODEBOOK, 9: ctypes.byref(cb4), 10: ctypes.byref(cb2), 12: rtq.RTQ_I32}) == \
+        rtq.RTQ_ERR_UNSUPPORTED
+    assert call({2: 0}) == rtq.RTQ_OK                                    # T = 0 is a no-op
+    # workspace sizing and checks of the fused call
+    ws = lib.rtq_rotated_qlinear_workspace
+    assert ws(4608, 4096, rtq.RTQ_INT8, 8) == 4608 * 4096 + 4608 * 4 + (256 - (4608 * 4) % 256) % 256
+    assert ws(4608, 4096, rtq.RTQ_CODEBOOK, 4) == 4608 * 2048 + 18432
+    assert ws(10, 4096, rtq.RTQ_CODEBOOK, 3) == 0
+    R = _R(256, 64, A, A)
+    ql = lib.rtq_rotated_qlinear
+    args = [A, rtq.RTQ_BF16, 16, ctypes.byref(R), A, A, rtq.RTQ_BF16, 32, rtq.RTQ_INT8, None, None, A, rtq.RTQ_BF16,
+            A, 1 << 20, None]
+    a = list(args); a[14] = 16
+    assert ql(*a) == rtq.RTQ_ERR_INVALID_ARG and "workspace too small" in rtq.last_error()
+    a = list(args); a[12] = rtq.RTQ_I32
+    assert ql(*a) == rtq.RTQ_ERR_UNSUPPORTED
+    a = list(args); a[2] = 0
+    assert ql(*a) == rtq.RTQ_OK
+
+
+def test_rotate_validation():
+    lib = rtq.load_library()
+    R = _R(256, 64, A, A)
+    r = lib.rtq_rpbh_rotate
+    assert r(A, rtq.RTQ_F32, A, rtq.RTQ_F32, 4, None, 0, None) == rtq.RTQ_ERR_INVALID_ARG
+    assert r(A, rtq.RTQ_F32, A, rtq.RTQ_F32, 4, ctypes.byref(R), 2, None) == rtq.RTQ_ERR_INVALID_ARG
+    assert r(A, rtq.RTQ_F32, A, rtq.RTQ_I32, 4, ctypes.byref(R), 0, None) == rtq.RTQ_ERR_UNSUPPORTED
+    assert r(A, rtq.RTQ_F32, A, rtq.RTQ_F32, 0, ctypes.byref(R), 0, None) == rtq.RTQ_OK
+
+
+def test_product_path_has_no_oracle_or_fallback():
+    # The product package never imports the oracle and has no CPU compute path.
+    pkg = os.path.join(ROOT, "rotation_then_quantize_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "oracle.c" not in text and "liboracle" not in text, f

@@ -1,0 +1,117 @@
+"""GPU parity of the quantised products (INT8 MFMA and codebook-LUT MFMA) against the oracle.
+
+INT8 accumulators must be bit-exact; rescaled outputs within the stated relative Frobenius bounds
+(1e-4 fp32 output; 2e-2 bf16 output, spec tolerance) and, where both sides round the same
+fp32/fp64 value to bf16, within one bf16 ulp elementwise."""
+import numpy as np
+import pytest
+
+import oracle
+import rotation_then_quantize_amd as rtq
+from _helpers import bf16_host, rel_fro, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    rtq.load_library()
+
+
+def _codes(seed, rows, d, lo=-127, hi=127):
+    return np.random.default_rng(seed).integers(lo, hi + 1, size=(rows, d)).astype(np.int8)
+
+
+@pytest.mark.parametrize("T,N,d", [(130, 200, 256), (1, 1, 64), (257, 129, 128), (64, 384, 4096),
+                                   (33, 70, 16384)])
+def test_int8_accumulators_bit_exact(T, N, d):
+    a = _codes(1 + T, T, d)
+    w = _codes(2 + N, N, d)
+    a_s = np.ones(T, np.float32)
+    w_s = np.ones(N, np.float32)
+    acc = torch.empty((T, N), dtype=torch.int32, device="cuda")
+    rtq.qgemm(to_dev(a), to_dev(a_s), to_dev(w), to_dev(w_s), acc, d)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), oracle.gemm_int8(a, w))
+
+
+def test_int8_accumulator_extremes():
+    # |acc| reaches 127^2 * d at d = 16384 (264,257,536 < 2^31)
+    d = 16384
+    a = np.full((3, d), 127, np.int8)
+    a[1] = -127
+    w = np.full((2, d), 127, np.int8)
+    w[1] = -127
+    acc = torch.empty((3, 2), dtype=torch.int32, device="cuda")
+    rtq.qgemm(to_dev(a), to_dev(np.ones(3, np.float32)), to_dev(w), to_dev(np.ones(2, np.float32)), acc, d)
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), oracle.gemm_int8(a, w))
+    assert acc[0, 0].item() == 127 * 127 * d
+
+
+@pytest.mark.parametrize("yt", ["f32", "bf16"])
+def test_int8_rescale_epilogue(yt):
+    T, N, d = 150, 300, 512
+    a = _codes(7, T, d)
+    w = _codes(8, N, d)
+    rng = np.random.default_rng(9)
+    a_s = (rng.random(T) * 0.1 + 0.01).astype(np.float32)
+    w_sb = oracle.to_bf16_bits(rng.random(N) * 1e-3 + 1e-4)
+    w_s = oracle.bf16_bits_to_f32(w_sb)
+    y = torch.empty((T, N), dtype=torch.float32 if yt == "f32" else torch.bfloat16, device="cuda")
+    rtq.qgemm(to_dev(a), to_dev(a_s), to_dev(w), to_dev(w_sb, "bf16"), y, d)
+    ref = oracle.rescale_int8(oracle.gemm_int8(a, w), a_s, w_s)
+    if yt == "f32":
+        got = y.cpu().numpy()
+        assert rel_fro(got, ref) <= 1e-6
+    else:
+        got = oracle.bf16_bits_to_f32(bf16_host(y))
+        refb = oracle.bf16_bits_to_f32(oracle.to_bf16_bits(ref))
+        assert rel_fro(got, ref) <= 2e-2
+        # same value rounded on both sides: at most one bf16 ulp apart
+        ulp = np.spacing(np.abs(refb).astype(np.float32)) * 65536
+        assert np.all(np.abs(got - refb) <= ulp)
+
+
+@pytest.mark.parametrize("bits_w", [4, 2])
+@pytest.mark.parametrize("yt", ["f32", "bf16"])
+def test_codebook_gemm_matches_oracle(bits_w, yt):
+    T, N, d = 140, 260, 1024
+    rng = np.random.default_rng(10 + bits_w)
+    qa = rng.integers(0, 16, size=(T, d)).astype(np.uint8)
+    qw = rng.integers(0, 1 << bits_w, size=(N, d)).astype(np.uint8)
+    cb_a = rtq.Codebook.for_dim(d, 4)
+    cb_w = rtq.Codebook.for_dim(d, bits_w)
+    ca = oracle.lloyd_max(4, d)["centroids"]
+    cw = oracle.lloyd_max(bits_w, d)["centroids"]
+    s_a = (rng.random(T) * 10 + 1).astype(np.float32)
+    r_wb = oracle.to_bf16_bits(rng.random(N) + 0.5)
+    r_w = oracle.bf16_bits_to_f32(r_wb)
+    y = torch.empty((T, N), dtype=torch.float32 if yt == "f32" else torch.bfloat16, device="cuda")
+    rtq.qgemm(to_dev(oracle.pack(qa, 4)), to_dev(s_a), to_dev(oracle.pack(qw, bits_w)), to_dev(r_wb, "bf16"), y, d,
+              rtq.RTQ_CODEBOOK, cb_a, cb_w)
+    ref = oracle.gemm_codebook(qa, qw, ca, cw, s_a, r_w)
+    got = y.cpu().numpy().astype(np.float64) if yt == "f32" else oracle.bf16_bits_to_f32(bf16_host(y))
+    err = rel_fro(got, ref)
+    # fp16 copies of the centroids (2^-11 relative rounding) bound the error well below this
+    assert err <= (1e-3 if yt == "f32" else 2e-2), err
+
+
+def test_int8_full_shape_sampled():
+    # W8A8 DiT shape in the launch configuration the benchmark times: 4608 x 4096 -> 16384.
+    T, N, d = 4608, 16384, 4096
+    a = _codes(21, T, d)
+    w = _codes(22, N, d)
+    acc = torch.empty((T, N), dtype=torch.int32, device="cuda")
+    rtq.qgemm(to_dev(a), to_dev(np.ones(T, np.float32)), to_dev(w), to_dev(np.ones(N, np.float32)), acc, d)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(23)
+    rows = np.sort(rng.choice(T, 48, replace=False))
+    cols = np.sort(rng.choice(N, 48, replace=False))
+    rows = np.concatenate([rows, [0, T - 1]])
+    cols = np.concatenate([cols, [0, N - 1]])
+    ref = oracle.gemm_int8(a[rows], w[cols])
+    got = acc.cpu().numpy()[np.ix_(rows, cols)].astype(np.int64)
+    assert np.array_equal(got, ref)
