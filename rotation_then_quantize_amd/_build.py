@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librtq.so")
-SOURCES = ["rpbh_rows.hip", "gemm_i8.hip", "gemm_lut.hip", "rtq_api.cpp", "rtq_host.cpp"]
+SOURCES = ["rpbh_rows.hip", "rpbh_quant.hip", "gemm_i8.hip", "gemm_lut.hip", "rtq_api.cpp", "rtq_host.cpp", "launch_cache.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 instructions stay off: the compiler must not form v_pk_{add,mul,fma}_f32.

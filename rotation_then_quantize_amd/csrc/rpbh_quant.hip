@@ -1,0 +1,543 @@
+// rpbh_quant.hip -- the hot RPBH rotate + quantise kernel for bf16 rows on gfx950.
+//
+// Same arithmetic as rpbh_rows.hip (x' = Pi_d x exactly via fp64 butterflies, OrbitQuant article
+// 2.3; INT8 s = max|x'|/127, q = rne(x'/s), cloud.baidu.com/article/9432521 4; Lloyd-Max codes of
+// x'/(||x'|| + eps), OrbitQuant article 2.1-2.2), organised for HBM throughput:
+//
+//  * Scatter on staging.  A 256-thread workgroup moves a group of 16384 bf16 elements (16384/d
+//    whole rows) per iteration.  Thread t always loads the same chunk columns of a row, so the
+//    permutation is applied as it writes: each of its 8 elements per 16-byte chunk goes straight
+//    to the LDS slot of the rotated block it feeds (inverse permutation, precomputed once per
+//    workgroup into 8 * max(1, d/2048) address registers; the row offset is an immediate).  The
+//    Rademacher sign of that slot is XOR-ed into the bf16 sign bit on the way.
+//  * LDS blocks are 128 bytes of data + 16 bytes of padding, so lane l reads its own 64-element
+//    block contiguously (eight 16-byte reads) without bank conflicts.
+//  * Register prefetch: the next group's global loads are issued before the current group is
+//    transformed, so HBM traffic overlaps the butterflies and quantisation.
+//  * Division-free INT8: the correctly rounded quotient x'/s comes from the row's reciprocal and
+//    one fma correction step, then one add of 1.5*2^23 rounds it half-to-even into the low mantissa
+//    bits; branch-free, and bit-identical to rne(fl32(x'/s)).  Only rows whose max |x'| is below
+//    2^-103 (subnormals could round differently) take an IEEE-division path.
+//  * Division-free codebook codes: for each row the exact fp32 thresholds Y_k = min{x' : fl32(x' /
+//    (s+eps)) > t_k} are found once (IEEE divisions, a few ulp steps), so code = #{k : x' >= Y_k}
+//    needs no division.  For 16 levels the candidate boundary comes from a 64-cell grid over the
+//    boundary range (table in lanes, fetched with ds_bpermute) and one compare settles the code;
+//    the grid is built so a cell, widened by the rounding slack, holds at most one boundary.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rtq_internal.h"
+
+namespace rtq {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kH = 64;
+constexpr int kGroup = kThreads * kH;         // 16384 elements per group
+constexpr int kBlockPitch = 144;              // bytes per 64-element bf16 block in LDS (128 + 16 pad)
+constexpr int kRowBuf = kThreads * kBlockPitch;   // 36864
+constexpr int kChunkStride = 32 * kBlockPitch;    // LDS distance of 2048 consecutive elements
+constexpr int kMaxD = 16384;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits) { return __uint_as_float(bits << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float next_up(float y) {
+    if (y == 0.0f) return 0x1p-149f;
+    const int32_t u = __float_as_int(y);
+    return __int_as_float(u >= 0 ? u + 1 : u - 1);
+}
+
+__device__ __forceinline__ float next_down(float y) {
+    if (y == 0.0f) return -0x1p-149f;
+    const int32_t u = __float_as_int(y);
+    return __int_as_float(u >= 0 ? u - 1 : u + 1);
+}
+
+// Smallest fp32 x with fl32(x / den) > t (division is IEEE, so this is the exact switch point of
+// the code decision; x / den is non-decreasing in x).  Starts from fl32(t * den), which is within a
+// couple of ulps of it, and walks one ulp at a time.
+__device__ float exact_threshold(float t, float den) {
+    float y = t * den;
+    if (y / den > t) {
+        for (int i = 0; i < 16; ++i) {
+            const float yd = next_down(y);
+            if (yd / den > t) y = yd; else break;
+        }
+    } else {
+        for (int i = 0; i < 16; ++i) {
+            y = next_up(y);
+            if (y / den > t) break;
+        }
+    }
+    return y;
+}
+
+__device__ __forceinline__ void fwht64(double (&v)[kH]) {
+#pragma unroll
+    for (int span = 1; span < kH; span <<= 1) {
+#pragma unroll
+        for (int i = 0; i < kH; i += 2 * span) {
+#pragma unroll
+            for (int j = i; j < i + span; ++j) {
+                const double a = v[j], b = v[j + span];
+                v[j] = a + b;
+                v[j + span] = a - b;
+            }
+        }
+    }
+}
+
+// My block from LDS (already permuted and signed), widened to fp64 and transformed: v = 8 * x'.
+__device__ __forceinline__ void load_block_fwht(const unsigned char* smem, int tid, double (&acc)[kH]) {
+    const uint4* bp = reinterpret_cast<const uint4*>(smem + tid * kBlockPitch);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const uint4 v = bp[q];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            acc[8 * q + 2 * p] = static_cast<double>(__uint_as_float(w[p] << 16));
+            acc[8 * q + 2 * p + 1] = static_cast<double>(__uint_as_float(w[p] & 0xffff0000u));
+        }
+    }
+    fwht64(acc);
+}
+
+// ---- reductions over the nb = 2^log2nb consecutive lanes that hold one row (DPP inside a
+//      16-lane row, lane reads across rows, LDS across waves).  Every thread of the workgroup
+//      must call these together (the cross-wave step has a barrier); the result reaches every
+//      lane of the row.
+template <int kCtrl, int kRowMask = 0xf>
+__device__ __forceinline__ int dpp(int old, int v) {
+    return __builtin_amdgcn_update_dpp(old, v, kCtrl, kRowMask, 0xf, false);
+}
+
+__device__ __forceinline__ float row_max(float v, int log2nb, float* red) {
+    // quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror
+    if (log2nb >= 1) v = fmaxf(v, __int_as_float(dpp<0xB1>(__float_as_int(v), __float_as_int(v))));
+    if (log2nb >= 2) v = fmaxf(v, __int_as_float(dpp<0x4E>(__float_as_int(v), __float_as_int(v))));
+    if (log2nb >= 3) v = fmaxf(v, __int_as_float(dpp<0x141>(__float_as_int(v), __float_as_int(v))));
+    if (log2nb >= 4) v = fmaxf(v, __int_as_float(dpp<0x140>(__float_as_int(v), __float_as_int(v))));
+    if (log2nb >= 5) {
+        const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 15));
+        const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
+        const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 47));
+        const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+        if (log2nb == 5)
+            v = (threadIdx.x & 32) ? fmaxf(r2, r3) : fmaxf(r0, r1);
+        else
+            v = fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+    }
+    if (log2nb > 6) {
+        const int wave = threadIdx.x >> 6;
+        if ((threadIdx.x & 63) == 0) red[wave] = v;
+        __syncthreads();
+        const int wpr = 1 << (log2nb - 6);
+        const int w0 = wave & ~(wpr - 1);
+        float m = red[w0];
+        for (int i = 1; i < wpr; ++i) m = fmaxf(m, red[w0 + i]);
+        v = m;
+    }
+    return v;
+}
+
+template <int kCtrl>
+__device__ __forceinline__ double dpp_add_f64(double v) {
+    const int lo = __double2loint(v), hi = __double2hiint(v);
+    return v + __hiloint2double(dpp<kCtrl>(0, hi), dpp<kCtrl>(0, lo));
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), lane),
+                            __builtin_amdgcn_readlane(__double2loint(v), lane));
+}
+
+__device__ __forceinline__ double row_sum(double v, int log2nb, double* red) {
+    if (log2nb >= 1) v = dpp_add_f64<0xB1>(v);
+    if (log2nb >= 2) v = dpp_add_f64<0x4E>(v);
+    if (log2nb >= 3) v = dpp_add_f64<0x141>(v);
+    if (log2nb >= 4) v = dpp_add_f64<0x140>(v);
+    if (log2nb >= 5) {
+        const double r0 = readlane_f64(v, 15), r1 = readlane_f64(v, 31);
+        const double r2 = readlane_f64(v, 47), r3 = readlane_f64(v, 63);
+        if (log2nb == 5)
+            v = (threadIdx.x & 32) ? r2 + r3 : r0 + r1;
+        else
+            v = (r0 + r1) + (r2 + r3);
+    }
+    if (log2nb > 6) {
+        const int wave = threadIdx.x >> 6;
+        if ((threadIdx.x & 63) == 0) red[wave] = v;
+        __syncthreads();
+        const int wpr = 1 << (log2nb - 6);
+        const int w0 = wave & ~(wpr - 1);
+        double m = red[w0];
+        for (int i = 1; i < wpr; ++i) m += red[w0 + i];
+        v = m;
+    }
+    return v;
+}
+
+// kNC: distinct 16-byte chunk columns a thread stages per group = max(1, d / 2048).
+template <int kNC, int kOut>
+__global__ void __launch_bounds__(kThreads, 2)
+rpbh_quant_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int log2d, int log2nb,
+                       const int32_t* __restrict__ perm, const int8_t* __restrict__ signs, void* __restrict__ out,
+                       void* __restrict__ scale_out, int scale_bf16, const float* __restrict__ bounds, float eps) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    // LDS: [row buffer(s) | prologue scratch overlaid][sign masks, d x u16 (kNC >= 4)][reduction]
+    // d <= 4096: two row buffers, so staging group g+1 never waits for readers of group g
+    // (one barrier per group).  d >= 8192: one buffer plus the persistent sign-mask table.
+    constexpr bool kMaskInLds = kNC >= 4;
+    constexpr int kBufs = kMaskInLds ? 1 : 2;
+    uint16_t* sg = reinterpret_cast<uint16_t*>(smem + (kMaskInLds ? kRowBuf : 2 * d));
+    double* red = reinterpret_cast<double*>(smem + kBufs * kRowBuf + (kMaskInLds ? 2 * d : 0));
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int rpg = kThreads >> log2nb;
+    const int rg = tid >> log2nb;
+    const int blk = tid & ((1 << log2nb) - 1);
+    const uint32_t dmask = static_cast<uint32_t>(d - 1);
+
+    // ---- once per workgroup: inverse permutation and source-side signs.  All loads are issued
+    //      before any LDS store so their latencies overlap.
+    // scatter addresses (LDS byte offsets < 65536); at d = 16384 they are kept as 16-bit pairs
+    constexpr bool kPackAddr = kNC >= 8;
+    uint32_t addr[kPackAddr ? kNC * 4 : kNC * 8];
+    uint4 msk[kMaskInLds ? 1 : kNC];
+    {
+        uint16_t* inv = reinterpret_cast<uint16_t*>(smem);     // overlays the row buffer
+        constexpr int kPer = kMaxD / 4 / kThreads;             // int4 perm loads per thread at d = 16384
+        int4 pv[kPer];
+        uint32_t sv[kPer];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int j = 4 * (tid + i * kThreads);
+            if (j < d) {
+                pv[i] = *reinterpret_cast<const int4*>(perm + j);
+                sv[i] = *reinterpret_cast<const uint32_t*>(signs + j);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int j = 4 * (tid + i * kThreads);
+            if (j < d) {
+                const int pj[4] = {pv[i].x, pv[i].y, pv[i].z, pv[i].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t p = static_cast<uint32_t>(pj[e]) & dmask;
+                    inv[p] = static_cast<uint16_t>(j + e);
+                    sg[p] = (sv[i] >> (8 * e + 7)) & 1u ? 0x8000u : 0u;
+                }
+            }
+        }
+        __syncthreads();
+        // For kNC == 1 (d <= 2048) a thread's chunks sit 2048/d rows apart: its first row goes into
+        // the address, the per-chunk row step is an immediate.
+        const uint32_t row_base = kNC == 1 ? ((8u * tid) >> log2d) * static_cast<uint32_t>((d >> 6) * kBlockPitch) : 0u;
+#pragma unroll
+        for (int c = 0; c < kNC; ++c) {
+            const uint32_t col = (8u * tid + 2048u * c) & dmask;
+            const uint4 iv = *reinterpret_cast<const uint4*>(inv + col);
+            const uint32_t iw[4] = {iv.x, iv.y, iv.z, iv.w};
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const uint32_t j = (k & 1) ? (iw[k >> 1] >> 16) : (iw[k >> 1] & 0xffffu);
+                const uint32_t a = row_base + (j >> 6) * kBlockPitch + (j & 63u) * 2u;
+                if (kPackAddr) {
+                    if (k & 1) addr[c * 4 + (k >> 1)] |= a << 16;
+                    else addr[c * 4 + (k >> 1)] = a;
+                } else {
+                    addr[c * 8 + k] = a;
+                }
+            }
+            if (!kMaskInLds) msk[c] = *reinterpret_cast<const uint4*>(sg + col);
+        }
+    }
+
+    // ---- codebook set-up: this lane's boundary, and (4-bit) the lane's cell of the grid
+    constexpr int kBits = kOut == kRowCode4 ? 4 : (kOut == kRowCode2 ? 2 : 8);
+    constexpr int kNB = (1 << kBits) - 1;
+    const int row_lanes = (1 << log2nb) < 64 ? (1 << log2nb) : 64;   // lanes of my row in my wave
+    const int lane_base = lane & ~(row_lanes - 1);
+    const int kidx = lane - lane_base;                                 // my threshold slot
+    float my_t = __builtin_inff();
+    float tb[kBits == 2 ? 3 : 1];
+    uint32_t cell = 0;
+    float grid_k = 0.0f;
+    bool use_grid = false;
+    if (kOut == kRowCode2) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k) tb[k] = bounds[k];
+    }
+    if (kOut == kRowCode4) {
+        if (kidx < kNB) my_t = bounds[kidx];
+        // grid over [-tmax, tmax] with 40 cells of width tmax/20; 64 cells in all (end cells clamp)
+        const float tmax = fmaxf(fabsf(bounds[0]), fabsf(bounds[kNB - 1]));
+        use_grid = row_lanes >= 16 && tmax > 0.0f;
+        if (use_grid) {
+            grid_k = 20.0f / tmax;                 // cell units per unit of u
+            const int j = lane;                    // cell index, 0..63
+            const float slack = 1.0f / 1024.0f;    // in cell units: covers every rounding error
+            const float lo = (j == 0) ? -__builtin_inff() : (static_cast<float>(j - 32) - slack) / grid_k;
+            const float hi = (j == 63) ? __builtin_inff() : (static_cast<float>(j - 31) + slack) / grid_k;
+            int below = 0, inside = 0, kin = kNB;  // slot kNB holds +inf: "no boundary in this cell"
+            for (int k = 0; k < kNB; ++k) {
+                const float t = bounds[k];
+                if (t < lo) ++below;
+                else if (t < hi) { ++inside; kin = k; }
+            }
+            if (inside > 1) use_grid = false;
+            cell = (static_cast<uint32_t>(below) << 8) | (4u * static_cast<uint32_t>(kin));
+        }
+        use_grid = __syncthreads_and(use_grid ? 1 : 0) != 0;
+    }
+
+    const int64_t ngroups = (rows + rpg - 1) / rpg;
+    const int64_t row_elems = static_cast<int64_t>(rows) * d;
+
+    // 8 chunks of 16 bytes per thread per group: chunk i covers group elements 8*tid + 2048*i.
+    uint4 pre[8];
+    auto load_group = [&](int64_t g) {
+        const int64_t e0 = g * kGroup + 8 * tid;
+        if ((g + 1) * kGroup <= row_elems) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) pre[i] = *reinterpret_cast<const uint4*>(x + e0 + 2048 * i);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int64_t e = e0 + 2048 * i;
+                pre[i] = e < row_elems ? *reinterpret_cast<const uint4*>(x + e) : make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+    };
+
+    int64_t g = blockIdx.x;
+    if (g < ngroups) load_group(g);
+    __syncthreads();  // inverse-permutation scratch consumed by every thread
+
+    for (int it = 0; g < ngroups; g += gridDim.x, ++it) {
+        unsigned char* buf = smem + (kBufs == 2 ? (it & 1) * kRowBuf : 0);
+        // ---- stage: signs, then scatter each element to its rotated block slot
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            uint4 m;
+            if (kMaskInLds) {
+                const uint32_t col = (8u * tid + 2048u * (i % kNC)) & dmask;
+                m = *reinterpret_cast<const uint4*>(sg + col);
+            } else {
+                m = msk[i % kNC];
+            }
+            const uint32_t w[4] = {pre[i].x ^ m.x, pre[i].y ^ m.y, pre[i].z ^ m.z, pre[i].w ^ m.w};
+            unsigned char* base = buf + (i - (i % kNC)) * kChunkStride;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const uint16_t h = static_cast<uint16_t>((k & 1) ? (w[k >> 1] >> 16) : (w[k >> 1] & 0xffffu));
+                const uint32_t a = kPackAddr ? ((k & 1) ? (addr[(i % kNC) * 4 + (k >> 1)] >> 16)
+                                                        : (addr[(i % kNC) * 4 + (k >> 1)] & 0xffffu))
+                                             : addr[(i % kNC) * 8 + k];
+                *reinterpret_cast<uint16_t*>(base + a) = h;
+            }
+        }
+        if (g + gridDim.x < ngroups) load_group(g + gridDim.x);
+        __syncthreads();
+
+        double acc[kH];
+        load_block_fwht(buf, tid, acc);
+
+        const int64_t row = g * rpg + rg;
+        const bool valid = row < rows;
+
+        if (kOut == kRowInt8) {
+            // amax = max |x'| = fl32(max |8x'| / 8) exactly (rounding is monotone), reduced over the row
+            double m = 0.0;
+#pragma unroll
+            for (int b = 0; b < kH; ++b) m = fmax(m, fabs(acc[b]));
+            const float amax = row_max(static_cast<float>(m * 0.125), log2nb, reinterpret_cast<float*>(red));
+            float s = amax / 127.0f;
+            if (scale_bf16) s = bf16_to_f32(f32_to_bf16(s));
+            // q = rne(fl32(x'/s)) with x'/s = y/(8s), y = fl32(8x'), and no division per element:
+            // r = RN(1/(8s)), q0 = RN(y*r), e = y - q0*(8s) (exact by fma), q1 = RN(q0 + e*r) is
+            // the correctly rounded quotient (Markstein's correction step), and adding 1.5*2^23
+            // rounds q1 half-to-even into the low mantissa bits, whose low byte is the code.
+            const float s8 = s * 8.0f;
+            const float r8 = 1.0f / s8;
+            constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+            uint32_t w[kH / 4];
+#pragma unroll
+            for (int q = 0; q < kH / 4; ++q) {
+                float t[4];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const float y = static_cast<float>(acc[4 * q + p]);
+                    const float q0 = y * r8;
+                    const float q1 = fmaf(fmaf(-q0, s8, y), r8, q0);
+                    t[p] = q1 + kMagic;
+                }
+                const uint32_t lo = __builtin_amdgcn_perm(__float_as_uint(t[1]), __float_as_uint(t[0]), 0x0c0c0400u);
+                const uint32_t hi = __builtin_amdgcn_perm(__float_as_uint(t[3]), __float_as_uint(t[2]), 0x04000c0cu);
+                w[q] = lo | hi;
+            }
+            // fl32(8x')/(8s) equals x'/s while x' is normal; with amax >= 2^-103 a subnormal x' gives
+            // code 0 either way.  Tinier rows (and all-zero rows) take the exact path.
+            const bool fast = amax >= 0x1p-103f;
+            if (!fast) {
+                // exact: q = rne(fl32(x'/s)), x' = fl32(8x' / 8); transform again from LDS (still intact)
+#pragma unroll
+                for (int q = 0; q < kH / 4; ++q) w[q] = 0u;
+                if (s != 0.0f) {
+                    double a2[kH];
+                    load_block_fwht(buf, tid, a2);
+                    for (int b = 0; b < kH; ++b) {
+                        const float xr = static_cast<float>(a2[b] * 0.125);
+                        float r = rintf(xr / s);
+                        r = fminf(fmaxf(r, -127.0f), 127.0f);
+                        w[b >> 2] |= (static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xffu) << ((b & 3) * 8);
+                    }
+                }
+            }
+            if (valid) {
+                uint4* o = reinterpret_cast<uint4*>(static_cast<int8_t*>(out) + row * d + blk * kH);
+#pragma unroll
+                for (int q = 0; q < kH / 16; ++q) o[q] = make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+                if (blk == 0) {
+                    if (scale_bf16)
+                        static_cast<uint16_t*>(scale_out)[row] = static_cast<uint16_t>(f32_to_bf16(s));
+                    else
+                        static_cast<float*>(scale_out)[row] = s;
+                }
+            }
+        } else {
+            // x' = fl32(8x' / 8), exactly the oracle's rotated value for every input
+            float xr[kH];
+            double ss = 0.0;
+#pragma unroll
+            for (int b = 0; b < kH; ++b) {
+                xr[b] = static_cast<float>(acc[b] * 0.125);
+                const double f = static_cast<double>(xr[b]);
+                ss = fma(f, f, ss);
+            }
+            ss = row_sum(ss, log2nb, red);
+            const float s = static_cast<float>(sqrt(ss));
+            const float den = (eps == 0.0f) ? s : s + eps;
+            constexpr int kPerWord = 32 / kBits;
+            uint32_t w[kH / kPerWord];
+#pragma unroll
+            for (int q = 0; q < kH / kPerWord; ++q) w[q] = 0u;
+            if (den != 0.0f) {
+                // u = fl32(x'/den); code = #{k : t_k < u} = #{k : x' >= Y_k}, Y_k exact per row
+                if (kOut == kRowCode2) {
+                    float Y[3];
+#pragma unroll
+                    for (int k = 0; k < 3; ++k) Y[k] = exact_threshold(tb[k], den);
+#pragma unroll
+                    for (int b = 0; b < kH; ++b) {
+                        const uint32_t code = (xr[b] >= Y[0] ? 1u : 0u) + (xr[b] >= Y[1] ? 1u : 0u) + (xr[b] >= Y[2] ? 1u : 0u);
+                        w[b / kPerWord] |= code << ((b % kPerWord) * kBits);
+                    }
+                } else if (use_grid) {
+                    // my slot holds Y_kidx (slot 15: +inf); cells hold (#below << 8) | 4*slot
+                    const float myY = kidx < kNB ? exact_threshold(my_t, den) : __builtin_inff();
+                    const float ka = 4.0f * grid_k / den;      // 4 * cell units per unit of x'
+                    const int base4 = 4 * lane_base;
+#pragma unroll
+                    for (int b = 0; b < kH; ++b) {
+                        const int a = static_cast<int>(__builtin_amdgcn_fmed3f(fmaf(xr[b], ka, 128.0f), 0.0f, 255.0f));
+                        const uint32_t e = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(a, static_cast<int>(cell)));
+                        const float Yk = __int_as_float(__builtin_amdgcn_ds_bpermute(static_cast<int>(e) + base4, __float_as_int(myY)));
+                        const uint32_t code = (e >> 8) + (xr[b] >= Yk ? 1u : 0u);
+                        w[b / kPerWord] |= code << ((b % kPerWord) * kBits);
+                    }
+                } else {
+                    // a general codebook, or too few lanes per row for the slot table: divide and count
+#pragma unroll
+                    for (int b = 0; b < kH; ++b) {
+                        const float u = xr[b] / den;
+                        uint32_t code = 0;
+                        for (int k = 0; k < kNB; ++k) code += (bounds[k] < u) ? 1u : 0u;
+                        w[b / kPerWord] |= code << ((b % kPerWord) * kBits);
+                    }
+                }
+            } else {
+                // zero row with eps = 0: u = 0 for every element
+                uint32_t code = 0;
+                for (int k = 0; k < kNB; ++k) code += (bounds[k] < 0.0f) ? 1u : 0u;
+#pragma unroll
+                for (int b = 0; b < kH; ++b) w[b / kPerWord] |= code << ((b % kPerWord) * kBits);
+            }
+            if (valid) {
+                uint4* o = reinterpret_cast<uint4*>(static_cast<uint8_t*>(out) + (row * d + blk * kH) * kBits / 8);
+#pragma unroll
+                for (int q = 0; q < kH / kPerWord / 4; ++q) o[q] = make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+                if (blk == 0) {
+                    if (scale_bf16)
+                        static_cast<uint16_t*>(scale_out)[row] = static_cast<uint16_t>(f32_to_bf16(s));
+                    else
+                        static_cast<float*>(scale_out)[row] = s;
+                }
+            }
+        }
+        if (kBufs == 1) __syncthreads();  // every lane has read its block before the buffer is restaged
+    }
+}
+
+template <int kNC, int kOut>
+hipError_t launch_t(const RowArgs& a, int log2d, hipStream_t stream) {
+    auto kernel = rpbh_quant_bf16_kernel<kNC, kOut>;
+    const int log2nb = log2d - 6;
+    const int64_t rpg = kThreads >> log2nb;
+    const int64_t ngroups = (a.rows + rpg - 1) / rpg;
+    const size_t lds = kNC >= 4 ? static_cast<size_t>(kRowBuf) + 2 * static_cast<size_t>(a.d) + 64
+                                : 2 * static_cast<size_t>(kRowBuf) + 64;
+    int per_cu = 0;
+    const hipError_t e = kernel_blocks_per_cu(reinterpret_cast<const void*>(kernel), kThreads, lds, &per_cu);
+    if (e != hipSuccess) return e;
+    const int64_t cap = static_cast<int64_t>(per_cu) * device_cu_count();
+    // even share of groups per workgroup, then as few workgroups as that share allows
+    const int64_t per_wg = (ngroups + cap - 1) / cap;
+    const int grid = static_cast<int>((ngroups + per_wg - 1) / per_wg);
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), lds, stream, static_cast<const uint16_t*>(a.x), a.rows,
+                       a.d, log2d, log2nb, a.perm, a.signs, a.out, a.scale, a.scale_bf16 ? 1 : 0, a.bounds, a.eps);
+    return hipGetLastError();
+}
+
+template <int kOut>
+hipError_t launch_nc(const RowArgs& a, int log2d, hipStream_t stream) {
+    switch (a.d > 2048 ? a.d / 2048 : 1) {
+        case 1: return launch_t<1, kOut>(a, log2d, stream);
+        case 2: return launch_t<2, kOut>(a, log2d, stream);
+        case 4: return launch_t<4, kOut>(a, log2d, stream);
+        case 8: return launch_t<8, kOut>(a, log2d, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool rpbh_quant_bf16_supported(const RowArgs& a) {
+    return a.x_bf16 && a.perm != nullptr &&
+           (a.out_kind == kRowInt8 || a.out_kind == kRowCode4 || a.out_kind == kRowCode2) && a.d >= 64 &&
+           a.d <= kMaxD;
+}
+
+hipError_t launch_rpbh_quant_bf16(const RowArgs& a, hipStream_t stream) {
+    if (a.rows <= 0) return hipSuccess;
+    int log2d = 0;
+    while ((1 << log2d) < a.d) ++log2d;
+    switch (a.out_kind) {
+        case kRowInt8: return launch_nc<kRowInt8>(a, log2d, stream);
+        case kRowCode4: return launch_nc<kRowCode4>(a, log2d, stream);
+        case kRowCode2: return launch_nc<kRowCode2>(a, log2d, stream);
+        default: break;
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace rtq

@@ -393,23 +393,12 @@ int ilog2(int v) {
     return l;
 }
 
-int device_cus() {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 256;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 256;
-    return cus;
-}
-
 template <typename Kernel, typename... Args>
 hipError_t launch_persistent(Kernel kernel, size_t lds, int64_t ngroups, hipStream_t stream, Args... args) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (e != hipSuccess) return e;
     int per_cu = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, lds);
+    const hipError_t e = kernel_blocks_per_cu(reinterpret_cast<const void*>(kernel), kThreads, lds, &per_cu);
     if (e != hipSuccess) return e;
-    if (per_cu < 1) per_cu = 1;
-    const int64_t cap = static_cast<int64_t>(per_cu) * device_cus();
+    const int64_t cap = static_cast<int64_t>(per_cu) * device_cu_count();
     const int grid = static_cast<int>(ngroups < cap ? ngroups : cap);
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), lds, stream, args...);
     return hipGetLastError();
@@ -443,6 +432,7 @@ hipError_t launch_rows_kind(const RowArgs& a, hipStream_t stream) {
 
 hipError_t launch_rpbh_rows(const RowArgs& a, hipStream_t stream) {
     if (a.rows <= 0) return hipSuccess;
+    if (rpbh_quant_bf16_supported(a)) return launch_rpbh_quant_bf16(a, stream);
     const bool rot = a.perm != nullptr;
     if (a.x_bf16) return rot ? launch_rows_kind<true, true>(a, stream) : launch_rows_kind<true, false>(a, stream);
     return rot ? launch_rows_kind<false, true>(a, stream) : launch_rows_kind<false, false>(a, stream);

@@ -33,6 +33,16 @@ struct RowArgs {
 
 hipError_t launch_rpbh_rows(const RowArgs& a, hipStream_t stream);
 
+// Per-device launch facts, queried once per process and device (the queries can synchronise, so
+// they must stay off the per-launch path): compute units, and for a kernel with a given dynamic
+// LDS size the resident workgroups per CU (after raising its dynamic-LDS limit).
+int device_cu_count();
+hipError_t kernel_blocks_per_cu(const void* kernel, int threads, size_t lds, int* per_cu);
+
+// The throughput kernel for bf16 rows with the rotation and a quantising output (rpbh_quant.hip).
+bool rpbh_quant_bf16_supported(const RowArgs& a);
+hipError_t launch_rpbh_quant_bf16(const RowArgs& a, hipStream_t stream);
+
 // x = Pi^T y for each row (rotation inverse), fp32/bf16 in and out.
 hipError_t launch_rpbh_inverse(const void* y, bool y_bf16, void* x, bool x_bf16, int64_t rows, int d,
                                const int32_t* perm, const int8_t* signs, hipStream_t stream);
