@@ -25,6 +25,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "rtq_internal.h"
 
 namespace rtq {
@@ -42,6 +44,8 @@ constexpr int WM = 128, WN = 64;              // per wave
 constexpr int TM = WM / 32, TN = WN / 32;     // 4 x 2 MFMA tiles of 32 x 32
 constexpr int kTileBytes = BM * BK;           // 32 KB per operand per stage
 constexpr int kXcds = 8;
+constexpr int kBufferWord3 = 0x00020000;     // gfx9 buffer descriptor word 3 (raw, 32-bit dwords)
+constexpr int kOutOfRange = 0x7ffffff0;      // byte offset past any descriptor range: loads 0
 
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
     uint32_t u = __float_as_uint(f);
@@ -80,39 +84,52 @@ __global__ void __launch_bounds__(kThreads, 1)
 gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, const int8_t* __restrict__ W,
                const void* __restrict__ w_scale, int64_t T, int64_t N, int d, void* __restrict__ Y,
                int tiles_m, int tiles_n) {
-    extern __shared__ __attribute__((aligned(16))) int8_t lds[];   // [buf][A|W][kTileBytes]
+    extern __shared__ __attribute__((aligned(16))) int8_t lds[];   // [buf][A|W][kTileBytes], scales
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave >> 2, wn = wave & 3;
-    int tile_m, tile_n;
-    tile_of(blockIdx.x, tiles_m, tiles_n, &tile_m, &tile_n);
-    if (tile_m >= tiles_m || tile_n >= tiles_n) return;   // padding block: before any barrier
-    const int64_t m0 = static_cast<int64_t>(tile_m) * BM;
-    const int64_t n0 = static_cast<int64_t>(tile_n) * BN;
 
+    // Persistent schedule: the tiles are split into 8 contiguous ranges, one per XCD; the blocks of
+    // an XCD (block b runs on XCD b % 8) take its range round-robin.
+    const int total = tiles_m * tiles_n;
+    const int xcd = blockIdx.x % kXcds;
+    const int stride = gridDim.x / kXcds;
+    const int per = (total + kXcds - 1) / kXcds;
+    const int lin_end = min((xcd + 1) * per, total);
+    int lin = xcd * per + static_cast<int>(blockIdx.x / kXcds);
+    if (lin >= lin_end) return;   // no tile for this block: before any barrier
+
+    int64_t m0 = 0, n0 = 0;
+    __amdgpu_buffer_rsrc_t rsa, rsw;
     // staging: chunk c = tid + 512*i covers tile row c / 8, 16-byte column c % 8; 4 chunks of A and
-    // 4 of W per thread per stage (consecutive threads read consecutive 16 bytes of a row)
+    // 4 of W per thread per stage (consecutive threads read consecutive 16 bytes of a row).  The
+    // loads are buffer loads against descriptors that end at the tile's last valid row, so rows past
+    // T or N (and K past d, sent to an offset beyond the range) read as zero without a branch.
+    auto set_tile = [&](int l) {
+        int tm, tn;
+        tile_of(l, tiles_m, tiles_n, &tm, &tn);
+        m0 = static_cast<int64_t>(tm) * BM;
+        n0 = static_cast<int64_t>(tn) * BN;
+        const int rows_a = static_cast<int>(min<int64_t>(BM, T - m0));
+        const int rows_w = static_cast<int>(min<int64_t>(BN, N - n0));
+        rsa = __builtin_amdgcn_make_buffer_rsrc((void*)(A + m0 * d), (short)0, rows_a * d, kBufferWord3);
+        rsw = __builtin_amdgcn_make_buffer_rsrc((void*)(W + n0 * d), (short)0, rows_w * d, kBufferWord3);
+    };
     constexpr int kLoads = BM * kChunks / kThreads;   // 4
     uint4 ra[kLoads], rb[kLoads];
-    const bool full = (m0 + BM <= T) && (n0 + BN <= N);
-    const bool kfull = (d % BK) == 0;
-
     auto load_stage = [&](int k0) {
 #pragma unroll
         for (int i = 0; i < kLoads; ++i) {
             const int c = tid + i * kThreads;
             const int row = c >> 3, ch = c & 7;
             const int k = k0 + ch * 16;
-            const int64_t ga = m0 + row, gb = n0 + row;
-            if (full && kfull) {
-                ra[i] = *reinterpret_cast<const uint4*>(A + ga * d + k);
-                rb[i] = *reinterpret_cast<const uint4*>(W + gb * d + k);
-            } else {
-                ra[i] = (ga < T && k < d) ? *reinterpret_cast<const uint4*>(A + ga * d + k) : make_uint4(0u, 0u, 0u, 0u);
-                rb[i] = (gb < N && k < d) ? *reinterpret_cast<const uint4*>(W + gb * d + k) : make_uint4(0u, 0u, 0u, 0u);
-            }
+            const int off = k < d ? row * d + k : kOutOfRange;
+            const v4i va = __builtin_amdgcn_raw_buffer_load_b128(rsa, off, 0, 0);
+            const v4i vw = __builtin_amdgcn_raw_buffer_load_b128(rsw, off, 0, 0);
+            ra[i] = make_uint4(va.x, va.y, va.z, va.w);
+            rb[i] = make_uint4(vw.x, vw.y, vw.z, vw.w);
         }
     };
     auto store_stage = [&](int buf) {
@@ -126,17 +143,34 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
             *reinterpret_cast<uint4*>(lb + swz(row, ch)) = rb[i];
         }
     };
+    // The tile's token scales (threads 0-255) and output-row scales (threads 256-511), staged in LDS
+    // behind the operand stages for the epilogue.
+    float* s_as = reinterpret_cast<float*>(lds + 2 * 2 * kTileBytes);
+    float* s_ws = s_as + BM;
+    auto load_scale = [&]() -> float {
+        if (kYKind == 2) return 0.0f;
+        if (tid < BM) return m0 + tid < T ? a_scale[m0 + tid] : 0.0f;
+        const int64_t n = n0 + (tid - BM);
+        if (n >= N) return 0.0f;
+        if (kWScaleBF16) return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(w_scale)[n]) << 16);
+        return static_cast<const float*>(w_scale)[n];
+    };
+
+    const int nk = (d + BK - 1) / BK;
+    set_tile(lin);
+    load_stage(0);
+    float sc = load_scale();
+
+    for (;;) {
+    store_stage(0);
+    if (kYKind != 2) s_as[tid] = sc;
+    __syncthreads();
 
     v16i acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = v16i{};
-
-    const int nk = (d + BK - 1) / BK;
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
 
     const int frow = lane & 31;   // row (A) / column (W) inside a 32x32 tile
     const int fk = lane >> 5;     // which 16-byte half of the 32-byte MFMA K step
@@ -159,44 +193,96 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
             for (int i = 0; i < TM; ++i)
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[j], fa[i], acc[i][j], 0, 0, 0);
         }
         if (kt + 1 < nk) store_stage(buf ^ 1);
         __syncthreads();
     }
 
-    // ---- epilogue: for a 32x32 tile, lane holds D[8*(r/4) + 4*(lane/32) + r%4][lane % 32]
-    const int ocol = lane & 31;
-    const int orow = (lane >> 5) * 4;
+    // The next tile's first stage and scales are fetched now, so their latency (and the stores below)
+    // overlap the epilogue; LDS is rewritten only after the epilogue's last barrier.
+    const int64_t cm0 = m0, cn0 = n0;
+    const int next = lin + stride;
+    const bool more = next < lin_end;
+    if (more) {
+        set_tile(next);
+        load_stage(0);
+        sc = load_scale();
+    }
+
+    // ---- epilogue.  The MFMA computed the transposed tile (W fragment as the first operand), so a
+    // lane holds D[n][t] at n = 8*(r/4) + 4*(lane/32) + r%4, t = lane % 32: four consecutive output
+    // columns of one token row per group r/4.  Each wave scales its 128 x 64 block 32 token rows at a
+    // time into its own LDS region (row pitch padded by 16 bytes against bank conflicts), then writes
+    // it out row-contiguously: every 16-byte store lands in a 128- or 256-byte run of one Y row.
+    constexpr int kOutBytes = kYKind == 1 ? 2 : 4;
+    constexpr int kRowBytes = WN * kOutBytes;            // one wave's row segment
+    constexpr int kPitch = kRowBytes + 16;
+    constexpr int kPerChunk = 16 / kOutBytes;            // outputs per 16-byte store
+    constexpr int kChunksPerRow = kRowBytes / 16;
+    constexpr int kRowsPerPass = 64 / kChunksPerRow;
+    int8_t* ep = lds + wave * (32 * kPitch);
+    const bool vec_ok = (N % kPerChunk) == 0;
+    const int tl = lane & 31;
+    const int nq = (lane >> 5) * 4;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        const int64_t n = n0 + wn * WN + j * 32 + ocol;
-        if (n >= N) continue;
-        float ws = 1.0f;
-        if (kYKind != 2) {
-            if (kWScaleBF16)
-                ws = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(w_scale)[n]) << 16);
-            else
-                ws = static_cast<const float*>(w_scale)[n];
-        }
+    for (int i = 0; i < TM; ++i) {
+        const float as = s_as[wm * WM + i * 32 + tl];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
+        for (int j = 0; j < TN; ++j) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t t = m0 + wm * WM + i * 32 + 8 * (r >> 2) + orow + (r & 3);
-                if (t >= T) continue;
-                const int32_t a = acc[i][j][r];
+            for (int g = 0; g < 4; ++g) {
+                const int col = j * 32 + 8 * g + nq;
+                const int32_t a0 = acc[i][j][4 * g], a1 = acc[i][j][4 * g + 1];
+                const int32_t a2 = acc[i][j][4 * g + 2], a3 = acc[i][j][4 * g + 3];
+                int8_t* dst = ep + tl * kPitch + col * kOutBytes;
                 if (kYKind == 2) {
-                    static_cast<int32_t*>(Y)[t * N + n] = a;
+                    *reinterpret_cast<int4*>(dst) = make_int4(a0, a1, a2, a3);
                 } else {
-                    const float y = static_cast<float>(a) * a_scale[t] * ws;
+                    const float4 ws = *reinterpret_cast<const float4*>(s_ws + wn * WN + col);
+                    const float y0 = static_cast<float>(a0) * as * ws.x;
+                    const float y1 = static_cast<float>(a1) * as * ws.y;
+                    const float y2 = static_cast<float>(a2) * as * ws.z;
+                    const float y3 = static_cast<float>(a3) * as * ws.w;
                     if (kYKind == 0)
-                        static_cast<float*>(Y)[t * N + n] = y;
+                        *reinterpret_cast<float4*>(dst) = make_float4(y0, y1, y2, y3);
                     else
-                        static_cast<uint16_t*>(Y)[t * N + n] = static_cast<uint16_t>(f32_to_bf16(y));
+                        *reinterpret_cast<uint2*>(dst) = make_uint2(f32_to_bf16(y0) | (f32_to_bf16(y1) << 16),
+                                                                    f32_to_bf16(y2) | (f32_to_bf16(y3) << 16));
                 }
             }
         }
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < 32 / kRowsPerPass; ++p) {
+            const int row = p * kRowsPerPass + lane / kChunksPerRow;
+            const int ch = lane % kChunksPerRow;
+            const int64_t t = cm0 + wm * WM + i * 32 + row;
+            const int64_t n = cn0 + wn * WN + ch * kPerChunk;
+            if (t < T && n < N) {
+                const uint4 v = *reinterpret_cast<const uint4*>(ep + row * kPitch + ch * 16);
+                int8_t* yp = static_cast<int8_t*>(Y) + (t * N + n) * kOutBytes;
+                if (vec_ok && n + kPerChunk <= N) {
+                    // streaming store: Y is written once, and letting it allocate in the caches
+                    // evicts the operand panels that later tiles re-read
+                    __builtin_nontemporal_store(*reinterpret_cast<const v4i*>(&v), reinterpret_cast<v4i*>(yp));
+                } else {
+                    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int e = 0; e < kPerChunk; ++e) {
+                        if (n + e >= N) break;
+                        if (kOutBytes == 4)
+                            reinterpret_cast<uint32_t*>(yp)[e] = w[e];
+                        else
+                            reinterpret_cast<uint16_t*>(yp)[e] = static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1)));
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+    if (!more) break;
+    lin = next;
     }
 }
 
@@ -205,7 +291,7 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
 hipError_t launch_gemm_i8(const GemmI8Args& g, hipStream_t stream) {
     if (g.T <= 0 || g.N <= 0) return hipSuccess;
     if (g.d % 64 != 0) return hipErrorInvalidValue;
-    constexpr size_t kLds = 2 * 2 * kTileBytes;   // 128 KB: two stages of A and W
+    constexpr size_t kLds = 2 * 2 * kTileBytes + (BM + BN) * sizeof(float);   // two stages of A and W + scales
     static const hipError_t attr_err = [] {
         hipError_t e = hipSuccess;
         for (const void* k : {reinterpret_cast<const void*>(gemm_i8_kernel<0, true>),
@@ -223,8 +309,12 @@ hipError_t launch_gemm_i8(const GemmI8Args& g, hipStream_t stream) {
     const int64_t tiles_m = (g.T + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
     const int64_t total = tiles_m * tiles_n;
     if (total > (int64_t(1) << 30)) return hipErrorInvalidValue;
-    // round the grid up to a multiple of the XCD count so every XCD gets the same share
-    const int64_t grid = (total + kXcds - 1) / kXcds * kXcds;
+    // persistent grid: one block per compute unit (the LDS allows one), a multiple of the XCD count,
+    // and no more blocks than tiles (rounded up to that multiple)
+    const int cus = device_cu_count();
+    if (cus <= 0) return hipErrorInvalidDevice;
+    const int64_t slots = std::max<int64_t>(kXcds, cus / kXcds * kXcds);
+    const int64_t grid = std::min<int64_t>(slots, (total + kXcds - 1) / kXcds * kXcds);
 #define RTQ_LAUNCH(YK, WB)                                                                                   \
     hipLaunchKernelGGL((gemm_i8_kernel<YK, WB>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), kLds, stream,  \
                        g.a, g.a_scale, g.w, g.w_scale, g.T, g.N, g.d, g.y, static_cast<int>(tiles_m),          \
