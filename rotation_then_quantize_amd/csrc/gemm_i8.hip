@@ -9,19 +9,29 @@
 // lane, 16 consecutive K bytes of one row (lanes 0-31 the first 16 bytes of a 32-byte K step,
 // lanes 32-63 the second), so a 16-byte chunk of a row is one lane's operand for either side.
 //
-// Tiling.  A workgroup of 8 waves (2 per SIMD) owns a 256 x 256 output tile; wave w computes rows
-// 128*(w/4) .. +128 and columns 64*(w%4) .. +64 with v_mfma_i32_32x32x32_i8 (4 x 2 MFMA tiles,
-// 128 int32 accumulators per lane in AGPRs).  Two waves share each SIMD, so one wave's MFMAs
-// cover the other's LDS reads.  K advances in LDS stages of 128 bytes (4 MFMA steps), double
-// buffered: the next stage's global loads are in flight while the current stage is multiplied.
-// Per MFMA step a wave reads 4 A and 2 W fragments (6 KB of LDS) for 8 MFMAs.
-// LDS rows are 128 bytes; 16-byte chunk c of row r sits at chunk c ^ f(r) with
-// f(r) = ((r >> 1) & 7) ^ ((r & 1) << 2), which keeps fragment reads and staging writes free of
-// bank conflicts whether the LDS has 32 or 64 four-byte banks.
+// Tiling.  A workgroup owns a 256 x 256 output tile, split over 2 x kWavesN waves; each wave
+// computes a 128 x (256 / kWavesN) block as 32 x 32 MFMA tiles.  kWavesN = 2: four waves (one per
+// SIMD), 128 x 128 per wave, 8 KB of LDS fragment reads per 16 MFMAs.  kWavesN = 4: eight waves
+// (two per SIMD), 128 x 64 per wave, 6 KB per 8 MFMAs.
 //
-// Order.  Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2), so the
-// block index is remapped: the workgroups resident on one XCD cover a compact band of output
-// tiles that share A rows and W rows in that XCD's L2.
+// Pipeline.  K advances in stages of 64 bytes through a ring of 4 LDS stages (32 KB each: the A
+// and W tile rows for that K range).  Stages are filled by buffer loads that write LDS directly
+// (no staging registers), two stages ahead of the one being multiplied.  Inside a stage, the
+// fragments of the next K step are read while the MFMAs of the current one run (two fragment
+// register sets, reads interleaved one per MFMA).  The waits on the LDS-writing loads are explicit
+// (the compiler does not track them).
+//
+// LDS layout.  A stage block holds 256 rows x 64 bytes per operand; 16-byte chunk c of row r sits
+// at slot c ^ ((r >> 2) & 3).  A fragment read (16 lanes = 16 consecutive rows, one chunk, per LDS
+// cycle) then touches 16 distinct 16-byte bank groups, and every load instruction writes a
+// contiguous 1 KB (16 rows), with the permutation applied to which global chunk each lane fetches.
+//
+// Schedule.  One workgroup per CU runs persistently over tiles.  The tiles are split into 8
+// contiguous ranges, one per XCD (block b runs on XCD b % 8, and each XCD has its own L2); the
+// blocks of an XCD walk their range in bands of 8 N-tiles so concurrently running blocks share
+// A and W rows in that L2.  The next tile's first two stages are fetched while the current
+// tile's epilogue runs.  Y is written with streaming stores of whole cache lines: it is written
+// once, and letting it allocate in the caches evicts the operand rows that later tiles re-read.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -29,23 +39,29 @@
 
 #include "rtq_internal.h"
 
+// The LDS-writing loads set M0 in inline assembly; M0 is otherwise unused by this kernel.
+#pragma clang diagnostic ignored "-Winline-asm"
+
 namespace rtq {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-constexpr int kThreads = 512;
 constexpr int BM = 256;
 constexpr int BN = 256;
-constexpr int BK = 128;                       // bytes of K per LDS stage
-constexpr int kChunks = BK / 16;              // 16-byte chunks per tile row per stage (8)
-constexpr int WM = 128, WN = 64;              // per wave
-constexpr int TM = WM / 32, TN = WN / 32;     // 4 x 2 MFMA tiles of 32 x 32
-constexpr int kTileBytes = BM * BK;           // 32 KB per operand per stage
+constexpr int BK = 64;                          // K bytes per LDS stage (two MFMA K steps)
+constexpr int kStages = 4;                      // LDS ring depth
+constexpr int kOpBytes = BM * BK;               // 16 KB: one operand's rows for one stage
+constexpr int kStageBytes = 2 * kOpBytes;       // A then W
+constexpr int kRingBytes = kStages * kStageBytes;
+constexpr int kLds = kRingBytes + (BM + BN) * static_cast<int>(sizeof(float));   // ring + scales
+constexpr int kWavesM = 2;
+constexpr int WM = BM / kWavesM;                // 128 rows per wave
 constexpr int kXcds = 8;
-constexpr int kBufferWord3 = 0x00020000;     // gfx9 buffer descriptor word 3 (raw, 32-bit dwords)
-constexpr int kOutOfRange = 0x7ffffff0;      // byte offset past any descriptor range: loads 0
+constexpr int kBufferWord3 = 0x00020000;        // gfx9 buffer descriptor word 3 (raw, 32-bit dwords)
+constexpr int kStoreNT = 2;                     // buffer store cache policy: nontemporal (streaming)
+constexpr int kDefaultWavesN = 4;               // the configuration the launcher uses
 
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
     uint32_t u = __float_as_uint(f);
@@ -53,25 +69,41 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-__device__ __forceinline__ int swz(int row, int chunk) {
-    const int f = ((row >> 1) & 7) ^ ((row & 1) << 2);
-    return row * BK + ((chunk ^ f) << 4);
+// Raw buffer descriptor over [base, base + bytes): loads at offsets >= bytes return zero.
+__device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    v4i r;
+    r.x = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b)));
+    r.y = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b >> 32) & 0xffffu));
+    r.z = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+    r.w = kBufferWord3;
+    return r;
 }
 
-// Block index -> (tile_m, tile_n).  Blocks i and i + 8 land on the same XCD; each XCD walks its own
-// contiguous range of tiles, ordered in bands of 8 N-tiles so concurrent blocks share panels.
-__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int* tm, int* tn) {
-    const int total = tiles_m * tiles_n;
-    const int xcd = bid % kXcds;
-    const int local = bid / kXcds;
-    const int per = (total + kXcds - 1) / kXcds;
-    const int lin = xcd * per + local;
-    if (lin >= total) {  // padding blocks of the last round: no tile
-        *tm = tiles_m;
-        *tn = 0;
-        return;
-    }
-    constexpr int kBand = 8;      // N-tiles per band
+// 16 bytes per lane from buffer offset voff to LDS address lds_addr + 16 * lane.
+__device__ __forceinline__ void load_to_lds(v4i rsrc, uint32_t voff, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(static_cast<int>(lds_addr))), "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
+}
+
+#define RTQ_BARRIER() asm volatile("s_barrier" ::: "memory")
+// orders a wave's own LDS accesses (executed in order per wave) against compiler reordering
+#define RTQ_LDS_FENCE() asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory")
+
+// Wait until at most n vector-memory operations of this wave are outstanding.
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(n == 0 || n == 4 || n == 8, "add the immediate");
+    if constexpr (n == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if constexpr (n == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    if constexpr (n == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+}
+
+// Tile index within the XCD-ordered sequence -> (tile_m, tile_n), in bands of 8 N-tiles.
+__device__ __forceinline__ void tile_of(int lin, int tiles_m, int tiles_n, int* tm, int* tn) {
+    constexpr int kBand = 8;
     const int band = lin / (kBand * tiles_m);
     const int in_band = lin % (kBand * tiles_m);
     const int band_w = min(kBand, tiles_n - band * kBand);
@@ -79,20 +111,26 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int* 
     *tn = band * kBand + in_band % band_w;
 }
 
-template <int kYKind, bool kWScaleBF16>
-__global__ void __launch_bounds__(kThreads, 1)
+template <int kWavesN, int kYKind, bool kWScaleBF16, bool kVec>
+__global__ void __launch_bounds__(64 * kWavesM * kWavesN, 1)
 gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, const int8_t* __restrict__ W,
                const void* __restrict__ w_scale, int64_t T, int64_t N, int d, void* __restrict__ Y,
                int tiles_m, int tiles_n) {
-    extern __shared__ __attribute__((aligned(16))) int8_t lds[];   // [buf][A|W][kTileBytes], scales
+    constexpr int kWaves = kWavesM * kWavesN;
+    constexpr int kThreads = 64 * kWaves;
+    constexpr int WN = BN / kWavesN;                           // columns per wave
+    constexpr int TM = WM / 32, TN = WN / 32;                  // MFMA tiles per wave
+    constexpr int kLoadsPerOp = BM * BK / (kThreads * 16);     // 16-byte loads per thread per operand
+    constexpr int kLoadsPerStage = 2 * kLoadsPerOp;
+    constexpr int kScalesPerThread = (BM + BN) / kThreads;
+
+    extern __shared__ __attribute__((aligned(16))) int8_t lds[];   // ring of stages, then scales
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave >> 2, wn = wave & 3;
+    const int wm = wave / kWavesN, wn = wave % kWavesN;
 
-    // Persistent schedule: the tiles are split into 8 contiguous ranges, one per XCD; the blocks of
-    // an XCD (block b runs on XCD b % 8) take its range round-robin.
     const int total = tiles_m * tiles_n;
     const int xcd = blockIdx.x % kXcds;
     const int stride = gridDim.x / kXcds;
@@ -101,12 +139,31 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
     int lin = xcd * per + static_cast<int>(blockIdx.x / kXcds);
     if (lin >= lin_end) return;   // no tile for this block: before any barrier
 
+    const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+    float* s_as = reinterpret_cast<float*>(lds + kRingBytes);
+    float* s_ws = s_as + BM;
+    const int nk = d / BK;
+
+    // Load geometry: instruction q of wave w fills rows 16 * (q * kWaves + w) .. +16 of an operand
+    // block; lane L takes row 16 * (q * kWaves + w) + L / 4 and LDS slot L % 4, which holds the
+    // row's chunk (L % 4) ^ ((row >> 2) & 3) = (L % 4) ^ ((L >> 4) & 3).
+    uint32_t load_off[kLoadsPerOp];
+#pragma unroll
+    for (int q = 0; q < kLoadsPerOp; ++q) {
+        const int row = 16 * (q * kWaves + wave) + (lane >> 2);
+        const int chunk = (lane & 3) ^ ((lane >> 4) & 3);
+        load_off[q] = static_cast<uint32_t>(row * d + chunk * 16);
+    }
+    const uint32_t wave_lds = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave * 1024));
+
+    // Fragment geometry: lane reads row (lane % 32) of a 32-row block, chunk 2 * ks + lane / 32.
+    const int fr = lane & 31, fh = lane >> 5;
+    const int fsw = (fr >> 2) & 3;
+    const uint32_t frag_off0 = static_cast<uint32_t>(fr * BK + (((0 + fh) ^ fsw) << 4));
+    const uint32_t frag_off1 = static_cast<uint32_t>(fr * BK + (((2 + fh) ^ fsw) << 4));
+
     int64_t m0 = 0, n0 = 0;
-    __amdgpu_buffer_rsrc_t rsa, rsw;
-    // staging: chunk c = tid + 512*i covers tile row c / 8, 16-byte column c % 8; 4 chunks of A and
-    // 4 of W per thread per stage (consecutive threads read consecutive 16 bytes of a row).  The
-    // loads are buffer loads against descriptors that end at the tile's last valid row, so rows past
-    // T or N (and K past d, sent to an offset beyond the range) read as zero without a branch.
+    v4i rsa, rsw;
     auto set_tile = [&](int l) {
         int tm, tn;
         tile_of(l, tiles_m, tiles_n, &tm, &tn);
@@ -114,198 +171,252 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
         n0 = static_cast<int64_t>(tn) * BN;
         const int rows_a = static_cast<int>(min<int64_t>(BM, T - m0));
         const int rows_w = static_cast<int>(min<int64_t>(BN, N - n0));
-        rsa = __builtin_amdgcn_make_buffer_rsrc((void*)(A + m0 * d), (short)0, rows_a * d, kBufferWord3);
-        rsw = __builtin_amdgcn_make_buffer_rsrc((void*)(W + n0 * d), (short)0, rows_w * d, kBufferWord3);
+        rsa = make_rsrc(A + m0 * d, static_cast<uint32_t>(rows_a * d));
+        rsw = make_rsrc(W + n0 * d, static_cast<uint32_t>(rows_w * d));
     };
-    constexpr int kLoads = BM * kChunks / kThreads;   // 4
-    uint4 ra[kLoads], rb[kLoads];
-    auto load_stage = [&](int k0) {
+    auto issue_stage = [&](int st) {
+        const uint32_t sb = lds_base + static_cast<uint32_t>((st & (kStages - 1)) * kStageBytes) + wave_lds;
+        const uint32_t k0 = static_cast<uint32_t>(st * BK);
 #pragma unroll
-        for (int i = 0; i < kLoads; ++i) {
-            const int c = tid + i * kThreads;
-            const int row = c >> 3, ch = c & 7;
-            const int k = k0 + ch * 16;
-            const int off = k < d ? row * d + k : kOutOfRange;
-            const v4i va = __builtin_amdgcn_raw_buffer_load_b128(rsa, off, 0, 0);
-            const v4i vw = __builtin_amdgcn_raw_buffer_load_b128(rsw, off, 0, 0);
-            ra[i] = make_uint4(va.x, va.y, va.z, va.w);
-            rb[i] = make_uint4(vw.x, vw.y, vw.z, vw.w);
+        for (int q = 0; q < kLoadsPerOp; ++q) {
+            load_to_lds(rsa, load_off[q] + k0, sb + q * kWaves * 1024);
+            load_to_lds(rsw, load_off[q] + k0, sb + kOpBytes + q * kWaves * 1024);
         }
     };
-    auto store_stage = [&](int buf) {
-        int8_t* la = lds + buf * 2 * kTileBytes;
-        int8_t* lb = la + kTileBytes;
+    // The tile's token scales (entries 0..255) and output-row scales (256..511), one or two per
+    // thread, staged in LDS behind the ring for the epilogue.
+    float sc[kScalesPerThread];
+    auto load_scales = [&]() {
+        if (kYKind == 2) return;
 #pragma unroll
-        for (int i = 0; i < kLoads; ++i) {
-            const int c = tid + i * kThreads;
-            const int row = c >> 3, ch = c & 7;
-            *reinterpret_cast<uint4*>(la + swz(row, ch)) = ra[i];
-            *reinterpret_cast<uint4*>(lb + swz(row, ch)) = rb[i];
+        for (int r = 0; r < kScalesPerThread; ++r) {
+            const int k = tid + r * kThreads;
+            sc[r] = 0.0f;
+            if (k < BM) {
+                if (m0 + k < T) sc[r] = a_scale[m0 + k];
+            } else if (n0 + (k - BM) < N) {
+                const int64_t n = n0 + (k - BM);
+                if (kWScaleBF16)
+                    sc[r] = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(w_scale)[n]) << 16);
+                else
+                    sc[r] = static_cast<const float*>(w_scale)[n];
+            }
         }
     };
-    // The tile's token scales (threads 0-255) and output-row scales (threads 256-511), staged in LDS
-    // behind the operand stages for the epilogue.
-    float* s_as = reinterpret_cast<float*>(lds + 2 * 2 * kTileBytes);
-    float* s_ws = s_as + BM;
-    auto load_scale = [&]() -> float {
-        if (kYKind == 2) return 0.0f;
-        if (tid < BM) return m0 + tid < T ? a_scale[m0 + tid] : 0.0f;
-        const int64_t n = n0 + (tid - BM);
-        if (n >= N) return 0.0f;
-        if (kWScaleBF16) return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(w_scale)[n]) << 16);
-        return static_cast<const float*>(w_scale)[n];
+
+    v4i fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+    auto read_frags = [&](v4i* fa, v4i* fb, int st, uint32_t foff) {
+        const int8_t* la = lds + (st & (kStages - 1)) * kStageBytes + foff;
+        const int8_t* lb = la + kOpBytes;
+        // in the order the MFMAs below first use them: W0, A0, W1, A1, ...
+#pragma unroll
+        for (int k = 0; k < (TM > TN ? TM : TN); ++k) {
+            if (k < TN) fb[k] = *reinterpret_cast<const v4i*>(lb + (wn * WN + k * 32) * BK);
+            if (k < TM) fa[k] = *reinterpret_cast<const v4i*>(la + (wm * WM + k * 32) * BK);
+        }
     };
-
-    const int nk = (d + BK - 1) / BK;
-    set_tile(lin);
-    load_stage(0);
-    float sc = load_scale();
-
-    for (;;) {
-    store_stage(0);
-    if (kYKind != 2) s_as[tid] = sc;
-    __syncthreads();
-
     v16i acc[TM][TN];
+    auto mfmas = [&](const v4i* fa, const v4i* fb) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = v16i{};
-
-    const int frow = lane & 31;   // row (A) / column (W) inside a 32x32 tile
-    const int fk = lane >> 5;     // which 16-byte half of the 32-byte MFMA K step
-
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        const int8_t* la = lds + buf * 2 * kTileBytes;
-        const int8_t* lb = la + kTileBytes;
-        if (kt + 1 < nk) load_stage((kt + 1) * BK);
-#pragma unroll
-        for (int ks = 0; ks < BK / 32; ++ks) {
-            v4i fa[TM], fb[TN];
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-                fa[i] = *reinterpret_cast<const v4i*>(la + swz(wm * WM + i * 32 + frow, 2 * ks + fk));
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-                fb[j] = *reinterpret_cast<const v4i*>(lb + swz(wn * WN + j * 32 + frow, 2 * ks + fk));
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[j], fa[i], acc[i][j], 0, 0, 0);
+    };
+
+    // Stages 0 and 1 of a tile are fetched before the previous tile's epilogue (which stages its
+    // output through ring slots 2 and 3), stage 2 after it.
+    set_tile(lin);
+    issue_stage(0);
+    if (nk > 1) issue_stage(1);
+    load_scales();
+
+    for (;;) {
+        if (nk > 2) issue_stage(2);
+        if (kYKind != 2) {
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[j], fa[i], acc[i][j], 0, 0, 0);
+            for (int r = 0; r < kScalesPerThread; ++r) s_as[tid + r * kThreads] = sc[r];   // s_ws follows s_as
         }
-        if (kt + 1 < nk) store_stage(buf ^ 1);
-        __syncthreads();
-    }
+        // stages 0 and 1 have landed (and everything issued before them, e.g. earlier stores)
+        if (nk > 2)
+            wait_vmcnt<kLoadsPerStage>();
+        else
+            wait_vmcnt<0>();
+        RTQ_BARRIER();   // ... in every wave; the scales are visible
 
-    // The next tile's first stage and scales are fetched now, so their latency (and the stores below)
-    // overlap the epilogue; LDS is rewritten only after the epilogue's last barrier.
-    const int64_t cm0 = m0, cn0 = n0;
-    const int next = lin + stride;
-    const bool more = next < lin_end;
-    if (more) {
-        set_tile(next);
-        load_stage(0);
-        sc = load_scale();
-    }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) acc[i][j] = v16i{};
+        read_frags(fa0, fb0, 0, frag_off0);
 
-    // ---- epilogue.  The MFMA computed the transposed tile (W fragment as the first operand), so a
-    // lane holds D[n][t] at n = 8*(r/4) + 4*(lane/32) + r%4, t = lane % 32: four consecutive output
-    // columns of one token row per group r/4.  Each wave scales its 128 x 64 block 32 token rows at a
-    // time into its own LDS region (row pitch padded by 16 bytes against bank conflicts), then writes
-    // it out row-contiguously: every 16-byte store lands in a 128- or 256-byte run of one Y row.
-    constexpr int kOutBytes = kYKind == 1 ? 2 : 4;
-    constexpr int kRowBytes = WN * kOutBytes;            // one wave's row segment
-    constexpr int kPitch = kRowBytes + 16;
-    constexpr int kPerChunk = 16 / kOutBytes;            // outputs per 16-byte store
-    constexpr int kChunksPerRow = kRowBytes / 16;
-    constexpr int kRowsPerPass = 64 / kChunksPerRow;
-    int8_t* ep = lds + wave * (32 * kPitch);
-    const bool vec_ok = (N % kPerChunk) == 0;
-    const int tl = lane & 31;
-    const int nq = (lane >> 5) * 4;
+        for (int s = 0; s < nk; ++s) {
+            // stage s + 1 must have landed (stage s + 2 may still be in flight)
+            if (s + 2 < nk)
+                wait_vmcnt<kLoadsPerStage>();
+            else
+                wait_vmcnt<0>();
+            RTQ_BARRIER();   // every wave's part of stage s + 1 is in LDS; stage s - 1 is consumed
+            if (s + 3 < nk) issue_stage(s + 3);   // into stage s - 1's slot
+            read_frags(fa1, fb1, s, frag_off1);
+            mfmas(fa0, fb0);
+            // (on the last stage this reads an unused slot: unconditional, so the compiler's LDS wait
+            // before the next MFMAs does not also cover these reads)
+            read_frags(fa0, fb0, s + 1, frag_off0);
+            mfmas(fa1, fb1);
+            // Issue order: each fragment read sits between two MFMAs of the other register set, so
+            // the reads of one K step are in flight while the previous step's MFMAs run.
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const float as = s_as[wm * WM + i * 32 + tl];
+            for (int h = 0; h < 2; ++h) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int col = j * 32 + 8 * g + nq;
-                const int32_t a0 = acc[i][j][4 * g], a1 = acc[i][j][4 * g + 1];
-                const int32_t a2 = acc[i][j][4 * g + 2], a3 = acc[i][j][4 * g + 3];
-                int8_t* dst = ep + tl * kPitch + col * kOutBytes;
-                if (kYKind == 2) {
-                    *reinterpret_cast<int4*>(dst) = make_int4(a0, a1, a2, a3);
-                } else {
-                    const float4 ws = *reinterpret_cast<const float4*>(s_ws + wn * WN + col);
-                    const float y0 = static_cast<float>(a0) * as * ws.x;
-                    const float y1 = static_cast<float>(a1) * as * ws.y;
-                    const float y2 = static_cast<float>(a2) * as * ws.z;
-                    const float y3 = static_cast<float>(a3) * as * ws.w;
-                    if (kYKind == 0)
-                        *reinterpret_cast<float4*>(dst) = make_float4(y0, y1, y2, y3);
-                    else
-                        *reinterpret_cast<uint2*>(dst) = make_uint2(f32_to_bf16(y0) | (f32_to_bf16(y1) << 16),
-                                                                    f32_to_bf16(y2) | (f32_to_bf16(y3) << 16));
+                for (int k = 0; k < TM + TN; ++k) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
                 }
+                __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - (TM + TN), 0);
             }
         }
-        __syncthreads();
+        RTQ_BARRIER();   // every wave is done reading the ring
+
+        const int64_t cm0 = m0, cn0 = n0;
+        const int next = lin + stride;
+        const bool more = next < lin_end;
+        if (more) {
+            set_tile(next);
+            issue_stage(0);
+            if (nk > 1) issue_stage(1);
+            load_scales();
+        }
+
+        // ---- epilogue.  The MFMA computed the transposed tile (W fragment first), so a lane holds
+        // D[n][t] at n = 8*(r/4) + 4*(lane/32) + r%4, t = lane % 32: four consecutive output columns
+        // of one token row per group r/4.  Each wave copies its raw int32 block, 16 token rows at a
+        // time, into a private LDS region (ring slots 2 and 3; rows padded by 16 bytes against bank
+        // conflicts), then reads it back row-contiguously, scales and converts, and stores: the
+        // lanes of one row write a whole run of the wave's columns (128-512 bytes), so the
+        // streaming stores are full cache lines.  Stores go through a descriptor that ends at the
+        // tile's last valid row; columns past N are sent past its range.  kVec (N % 8 == 0): an
+        // output chunk of 16 bytes is wholly inside or outside [0, N).
+        {
+            constexpr int kOutBytes = kYKind == 1 ? 2 : 4;
+            constexpr int kPassRows = 16;
+            constexpr int kPitch = WN * 4 + 16;                    // raw int32 row + pad
+            constexpr int kPerChunk = 16 / kOutBytes;              // outputs per 16-byte store
+            constexpr int kChunksPerRow = WN / kPerChunk;
+            constexpr int kChunksPerLane = kPassRows * kChunksPerRow / 64;
+            constexpr uint32_t kOob = 0x80000000u;
+            static_assert(kWaves * kPassRows * kPitch <= 2 * kStageBytes, "staging must fit ring slots 2-3");
+            int8_t* stg = lds + 2 * kStageBytes + wave * (kPassRows * kPitch);
+            const int rows_y = static_cast<int>(min<int64_t>(BM, T - cm0));
+            const __amdgpu_buffer_rsrc_t rsy = __builtin_amdgcn_make_buffer_rsrc(
+                static_cast<int8_t*>(Y) + cm0 * N * kOutBytes, (short)0, static_cast<int>(rows_y * N * kOutBytes),
+                kBufferWord3);
 #pragma unroll
-        for (int p = 0; p < 32 / kRowsPerPass; ++p) {
-            const int row = p * kRowsPerPass + lane / kChunksPerRow;
-            const int ch = lane % kChunksPerRow;
-            const int64_t t = cm0 + wm * WM + i * 32 + row;
-            const int64_t n = cn0 + wn * WN + ch * kPerChunk;
-            if (t < T && n < N) {
-                const uint4 v = *reinterpret_cast<const uint4*>(ep + row * kPitch + ch * 16);
-                int8_t* yp = static_cast<int8_t*>(Y) + (t * N + n) * kOutBytes;
-                if (vec_ok && n + kPerChunk <= N) {
-                    // streaming store: Y is written once, and letting it allocate in the caches
-                    // evicts the operand panels that later tiles re-read
-                    __builtin_nontemporal_store(*reinterpret_cast<const v4i*>(&v), reinterpret_cast<v4i*>(yp));
-                } else {
-                    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            for (int i = 0; i < TM; ++i) {
 #pragma unroll
-                    for (int e = 0; e < kPerChunk; ++e) {
-                        if (n + e >= N) break;
-                        if (kOutBytes == 4)
-                            reinterpret_cast<uint32_t*>(yp)[e] = w[e];
-                        else
-                            reinterpret_cast<uint16_t*>(yp)[e] = static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1)));
+                for (int half = 0; half < 2; ++half) {
+                    if ((fr >> 4) == half) {
+                        int8_t* wrow = stg + (fr & 15) * kPitch;
+#pragma unroll
+                        for (int j = 0; j < TN; ++j)
+#pragma unroll
+                            for (int g = 0; g < 4; ++g)
+                                *reinterpret_cast<v4i*>(wrow + (j * 32 + 8 * g + 4 * fh) * 4) =
+                                    v4i{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                        acc[i][j][4 * g + 3]};
                     }
+                    RTQ_LDS_FENCE();   // the wave's rows are in LDS before they are read back
+#pragma unroll 1
+                    for (int p = 0; p < kChunksPerLane; ++p) {
+                        const int q = p * 64 + lane;
+                        const int r = q / kChunksPerRow, c = q % kChunksPerRow;
+                        const int trow = wm * WM + i * 32 + half * kPassRows + r;   // row within the tile
+                        const int col = wn * WN + c * kPerChunk;                    // column within the tile
+                        const int8_t* src = stg + r * kPitch + c * kPerChunk * 4;
+                        v4i out;
+                        if (kYKind == 2) {
+                            out = *reinterpret_cast<const v4i*>(src);
+                        } else {
+                            const float as = s_as[trow];
+                            float y[kPerChunk];
+#pragma unroll
+                            for (int h4 = 0; h4 < kPerChunk / 4; ++h4) {
+                                const v4i a = *reinterpret_cast<const v4i*>(src + 16 * h4);
+                                const float4 ws = *reinterpret_cast<const float4*>(s_ws + col + 4 * h4);
+                                y[4 * h4 + 0] = static_cast<float>(a.x) * as * ws.x;
+                                y[4 * h4 + 1] = static_cast<float>(a.y) * as * ws.y;
+                                y[4 * h4 + 2] = static_cast<float>(a.z) * as * ws.z;
+                                y[4 * h4 + 3] = static_cast<float>(a.w) * as * ws.w;
+                            }
+                            if (kYKind == 0) {
+                                out = v4i{static_cast<int>(__float_as_uint(y[0])), static_cast<int>(__float_as_uint(y[1])),
+                                          static_cast<int>(__float_as_uint(y[2])), static_cast<int>(__float_as_uint(y[3]))};
+                            } else {
+                                uint32_t w[4];
+#pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    w[e] = f32_to_bf16(y[2 * e]) | (f32_to_bf16(y[2 * e + 1]) << 16);
+                                out = v4i{static_cast<int>(w[0]), static_cast<int>(w[1]), static_cast<int>(w[2]),
+                                          static_cast<int>(w[3])};
+                            }
+                        }
+                        const int64_t n = cn0 + col;
+                        const uint32_t off = (static_cast<uint32_t>(trow) * static_cast<uint32_t>(N) +
+                                              static_cast<uint32_t>(n)) * kOutBytes;
+                        if (kVec) {
+                            __builtin_amdgcn_raw_buffer_store_b128(out, rsy, static_cast<int>(n < N ? off : kOob), 0,
+                                                                   kStoreNT);
+                        } else {
+                            const uint32_t w[4] = {static_cast<uint32_t>(out.x), static_cast<uint32_t>(out.y),
+                                                   static_cast<uint32_t>(out.z), static_cast<uint32_t>(out.w)};
+#pragma unroll
+                            for (int e = 0; e < kPerChunk; ++e) {
+                                const int o = static_cast<int>(n + e < N ? off + e * kOutBytes : kOob);
+                                if (kOutBytes == 4)
+                                    __builtin_amdgcn_raw_buffer_store_b32(w[e], rsy, o, 0, kStoreNT);
+                                else
+                                    __builtin_amdgcn_raw_buffer_store_b16(
+                                        static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1))), rsy, o, 0, kStoreNT);
+                            }
+                        }
+                    }
+                    RTQ_LDS_FENCE();   // read back before the next pass overwrites the region
                 }
             }
         }
-        __syncthreads();
-    }
-    if (!more) break;
-    lin = next;
+        RTQ_BARRIER();   // every wave is done with the staging slots and the scales
+        if (!more) break;
+        lin = next;
     }
 }
 
-}  // namespace
-
-hipError_t launch_gemm_i8(const GemmI8Args& g, hipStream_t stream) {
-    if (g.T <= 0 || g.N <= 0) return hipSuccess;
-    if (g.d % 64 != 0) return hipErrorInvalidValue;
-    constexpr size_t kLds = 2 * 2 * kTileBytes + (BM + BN) * sizeof(float);   // two stages of A and W + scales
+template <int kWavesN>
+hipError_t launch_config(const GemmI8Args& g, hipStream_t stream) {
+    using KernelFn = void (*)(const int8_t*, const float*, const int8_t*, const void*, int64_t, int64_t, int,
+                              void*, int, int);
+    // [w_scale bf16][N % 8 == 0][y kind]
+    static const KernelFn kernels[2][2][3] = {
+        {{gemm_i8_kernel<kWavesN, 0, false, false>, gemm_i8_kernel<kWavesN, 1, false, false>,
+          gemm_i8_kernel<kWavesN, 2, false, false>},
+         {gemm_i8_kernel<kWavesN, 0, false, true>, gemm_i8_kernel<kWavesN, 1, false, true>,
+          gemm_i8_kernel<kWavesN, 2, false, true>}},
+        {{gemm_i8_kernel<kWavesN, 0, true, false>, gemm_i8_kernel<kWavesN, 1, true, false>,
+          gemm_i8_kernel<kWavesN, 2, true, false>},
+         {gemm_i8_kernel<kWavesN, 0, true, true>, gemm_i8_kernel<kWavesN, 1, true, true>,
+          gemm_i8_kernel<kWavesN, 2, true, true>}}};
     static const hipError_t attr_err = [] {
         hipError_t e = hipSuccess;
-        for (const void* k : {reinterpret_cast<const void*>(gemm_i8_kernel<0, true>),
-                              reinterpret_cast<const void*>(gemm_i8_kernel<1, true>),
-                              reinterpret_cast<const void*>(gemm_i8_kernel<2, true>),
-                              reinterpret_cast<const void*>(gemm_i8_kernel<0, false>),
-                              reinterpret_cast<const void*>(gemm_i8_kernel<1, false>),
-                              reinterpret_cast<const void*>(gemm_i8_kernel<2, false>)}) {
-            const hipError_t r = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLds));
-            if (r != hipSuccess) e = r;
-        }
+        for (auto& a : kernels)
+            for (auto& b : a)
+                for (KernelFn k : b) {
+                    const hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                                             hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+                    if (r != hipSuccess) e = r;
+                }
         return e;
     }();
     if (attr_err != hipSuccess) return attr_err;
+    if (g.y_kind < 0 || g.y_kind > 2) return hipErrorInvalidValue;
     const int64_t tiles_m = (g.T + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
     const int64_t total = tiles_m * tiles_n;
     if (total > (int64_t(1) << 30)) return hipErrorInvalidValue;
@@ -315,21 +426,20 @@ hipError_t launch_gemm_i8(const GemmI8Args& g, hipStream_t stream) {
     if (cus <= 0) return hipErrorInvalidDevice;
     const int64_t slots = std::max<int64_t>(kXcds, cus / kXcds * kXcds);
     const int64_t grid = std::min<int64_t>(slots, (total + kXcds - 1) / kXcds * kXcds);
-#define RTQ_LAUNCH(YK, WB)                                                                                   \
-    hipLaunchKernelGGL((gemm_i8_kernel<YK, WB>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), kLds, stream,  \
-                       g.a, g.a_scale, g.w, g.w_scale, g.T, g.N, g.d, g.y, static_cast<int>(tiles_m),          \
-                       static_cast<int>(tiles_n))
-    if (g.w_scale_bf16) {
-        if (g.y_kind == 0) RTQ_LAUNCH(0, true);
-        else if (g.y_kind == 1) RTQ_LAUNCH(1, true);
-        else RTQ_LAUNCH(2, true);
-    } else {
-        if (g.y_kind == 0) RTQ_LAUNCH(0, false);
-        else if (g.y_kind == 1) RTQ_LAUNCH(1, false);
-        else RTQ_LAUNCH(2, false);
-    }
-#undef RTQ_LAUNCH
+    const KernelFn k = kernels[g.w_scale_bf16 ? 1 : 0][(g.N % 8) == 0 ? 1 : 0][g.y_kind];
+    hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(64 * kWavesM * kWavesN), kLds, stream, g.a,
+                       g.a_scale, g.w, g.w_scale, g.T, g.N, g.d, g.y, static_cast<int>(tiles_m),
+                       static_cast<int>(tiles_n));
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_i8(const GemmI8Args& g, hipStream_t stream) {
+    if (g.T <= 0 || g.N <= 0) return hipSuccess;
+    if (g.d % BK != 0 || g.d > 16384) return hipErrorInvalidValue;
+    if (g.N > (int64_t(1) << 22)) return hipErrorInvalidValue;   // 32-bit store offsets within a row block
+    return launch_config<kDefaultWavesN>(g, stream);
 }
 
 }  // namespace rtq
