@@ -49,6 +49,46 @@ def _copies(t, min_bytes, torch):
     return [t.clone() for _ in range(n)]
 
 
+def _prewarm(launch, torch, seconds=0.5):
+    """Untimed: run `launch` until `seconds` of wall time have passed, so the GPU is at its steady
+    clock and power state before the warm-up and timed steps (a cold GPU runs the first few hundred
+    milliseconds of MFMA work measurably slower)."""
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            launch(i)
+            i += 1
+        torch.cuda.synchronize()
+    return i
+
+
+def _source_sha256(*names):
+    import hashlib
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "rotation_then_quantize_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {"gemm_i8_kernel": ("gemm_i8.hip",), "rpbh_quant_bf16_kernel": ("rpbh_quant.hip",)}
+
+
+def _traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE runs (scaled by the
+    plain-copy calibration recorded with them), or None when the kernel source changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)["kernels"][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha256") != _source_sha256(*KERNEL_SOURCES[kernel]):
+        return None
+    return rec["fetch_bytes"] + rec["write_bytes"]
+
+
 def _time_pairs(steps, launch_a, launch_b, torch):
     """Run `steps` iterations of (a, b) with events around each launch on the current stream."""
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
@@ -89,6 +129,7 @@ def bench_w8a8(args, torch, rtq, workloads):
     def gemm(i):
         rtq.qgemm(codes, scale, wq, ws, y, d)
 
+    prewarm = _prewarm(lambda i: (quant(i), gemm(i)), torch)
     for i in range(args.warmup):
         quant(i)
         gemm(i)
@@ -110,7 +151,7 @@ def bench_w8a8(args, torch, rtq, workloads):
         "T": T, "d": d, "N": N, "wall_s": wall, "step_ms": wall * 1e3 / args.steps,
         "quant_ms": float(tq.mean()), "gemm_ms": float(tg.mean()),
         "quant_ms_median": float(np.median(tq)), "gemm_ms_median": float(np.median(tg)),
-        "flops": flops, "quant_bytes": q_bytes, "fused_step_ms": fused_ms,
+        "flops": flops, "quant_bytes": q_bytes, "fused_step_ms": fused_ms, "prewarm_steps": prewarm,
     }
 
 
@@ -171,6 +212,7 @@ def bench_codebook(args, torch, rtq, workloads, variant):
     def gemm(i):
         rtq.qgemm(codes, norm, wc, wn, y, d, rtq.RTQ_CODEBOOK, cb_a, cb_w)
 
+    _prewarm(lambda i: (quant(i), gemm(i)), torch, 0.25)
     for i in range(args.warmup):
         quant(i)
         gemm(i)
@@ -218,6 +260,62 @@ def cpu_baseline(workloads):
             "sample_seconds": t2 - t0}
 
 
+COPY_BYTES = 256 << 20
+
+
+def _counter_per_dispatch(run_dir, counter):
+    """{kernel name: [value per dispatch]} for one counter from a rocprofv3 CSV output directory."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    per = {}
+    for fn in files:
+        with open(fn) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] != counter:
+                    continue
+                key = (row["Kernel_Name"], row["Dispatch_Id"])
+                per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+    out = {}
+    for (name, _), v in sorted(per.items(), key=lambda kv: int(kv[0][1])):
+        out.setdefault(name, []).append(v)
+    return out
+
+
+def write_traffic(fetch_dir, write_dir):
+    """HBM bytes per launch of the hot kernels = FETCH_SIZE / WRITE_SIZE (KiB per dispatch, median over
+    dispatches) x the factor that maps the same counter to the known bytes of the plain copy."""
+    fetch = _counter_per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = _counter_per_dispatch(write_dir, "WRITE_SIZE")
+
+    def pick(table, key):
+        vals = [v for name, vs in table.items() if key in name for v in vs]
+        if not vals:
+            raise SystemExit(f"no dispatch of a kernel named *{key}* in the counter data")
+        return float(np.median(vals)) * 1024.0
+
+    f_copy, w_copy = pick(fetch, "bitwise_not"), pick(write, "bitwise_not")
+    cal = {"kernel": "bitwise_not over int8 (elementwise)", "bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
+           "fetch_counter_bytes": f_copy, "write_counter_bytes": w_copy,
+           "fetch_factor": COPY_BYTES / f_copy, "write_factor": COPY_BYTES / w_copy}
+    kernels = {}
+    for kernel in KERNEL_SOURCES:
+        fb, wb = pick(fetch, kernel), pick(write, kernel)
+        kernels[kernel] = {"source_sha256": _source_sha256(*KERNEL_SOURCES[kernel]),
+                           "fetch_counter_bytes": fb, "write_counter_bytes": wb,
+                           "fetch_bytes": round(fb * cal["fetch_factor"]), "write_bytes": round(wb * cal["write_factor"])}
+    rec = {"note": "HBM bytes per launch of the W8A8 step's kernels (4608 x 4096 -> 16384, bf16 in/out), from "
+                   "rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE runs of 'bench.py --calibrate-copy --only w8a8', "
+                   "each scaled by the factor that maps the same counter to the known bytes of a plain copy",
+           "calibration": cal, "kernels": kernels}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -226,7 +324,16 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     ap.add_argument("--only", choices=["w8a8", "all"], default="all",
                     help="w8a8: time only the headline step (profiling runs)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain streaming kernel of known size (bitwise_not over 256 MiB of int8, "
+                         "5 times) so a rocprofv3 FETCH_SIZE/WRITE_SIZE run can be scaled to bytes")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: read the counter CSVs of a FETCH_SIZE run and a WRITE_SIZE run of "
+                         "'bench.py --calibrate-copy --only w8a8' and write profiles/traffic.json")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU: the rotated linear is measured at "
                                    "its single-GPU shape; multi-GPU sharding is not part of this build",
@@ -240,6 +347,13 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     rtq.load_library()
 
+    if args.calibrate_copy:
+        src = torch.ones(COPY_BYTES, dtype=torch.int8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.bitwise_not(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     r = bench_w8a8(args, torch, rtq, workloads)
     extra = {}
     if args.only == "all":
@@ -271,12 +385,13 @@ def main():
                    "d_out": r["N"], "io": "bf16", "weights": "int8 per-row, bf16 scales",
                    "activations": "int8 per-token, fp32 scales", "rotation": "RPBH h=64"},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
-                     "frac": round(gemm_tops / PEAK_INT8_TOPS, 4), "traffic": None,
-                     "kernel": "gemm_i8_kernel", "work_per_launch": r["flops"], "avg_ms": round(r["gemm_ms"], 5)},
+                     "frac": round(gemm_tops / PEAK_INT8_TOPS, 4), "traffic": _traffic("gemm_i8_kernel"),
+                     "kernel": "gemm_i8_kernel", "work_per_launch": r["flops"], "avg_ms": round(r["gemm_ms"], 5),
+                     "median_ms": round(r["gemm_ms_median"], 5)},
         "rpbh_roofline": {"bound": "hbm", "achieved": round(q_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                          "frac": round(q_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
-                          "kernel": "rpbh_rows_kernel (int8)", "bytes_per_launch": r["quant_bytes"],
-                          "avg_ms": round(r["quant_ms"], 5)},
+                          "frac": round(q_gbps / PEAK_HBM_GBPS, 4), "traffic": _traffic("rpbh_quant_bf16_kernel"),
+                          "kernel": "rpbh_quant_bf16_kernel (int8)", "bytes_per_launch": r["quant_bytes"],
+                          "avg_ms": round(r["quant_ms"], 5), "median_ms": round(r["quant_ms_median"], 5)},
         "fused_entry_ms_per_step": round(r["fused_step_ms"], 4),
         "cpu_baseline": None if cpu is None else {k: (round(v, 6) if isinstance(v, float) else v)
                                                  for k, v in cpu.items()},
