@@ -26,6 +26,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "rtq_internal.h"
 
 namespace rtq {
@@ -300,30 +302,34 @@ rpbh_quant_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int 
         use_grid = __syncthreads_and(use_grid ? 1 : 0) != 0;
     }
 
-    const int64_t ngroups = (rows + rpg - 1) / rpg;
-    const int64_t row_elems = static_cast<int64_t>(rows) * d;
+    // This workgroup's rows: an even share [r_begin, r_end) of all rows, taken rpg rows per group
+    // (the last group of the share may be partial), so every workgroup does the same work.
+    const int64_t share = (rows + gridDim.x - 1) / gridDim.x;
+    const int64_t r_begin = min<int64_t>(rows, static_cast<int64_t>(blockIdx.x) * share);
+    const int64_t r_end = min<int64_t>(rows, r_begin + share);
+    const int64_t end_elems = r_end * d;
 
     // 8 chunks of 16 bytes per thread per group: chunk i covers group elements 8*tid + 2048*i.
     uint4 pre[8];
-    auto load_group = [&](int64_t g) {
-        const int64_t e0 = g * kGroup + 8 * tid;
-        if ((g + 1) * kGroup <= row_elems) {
+    auto load_group = [&](int64_t r0) {
+        const int64_t e0 = r0 * d + 8 * tid;
+        if (r0 * d + kGroup <= end_elems) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) pre[i] = *reinterpret_cast<const uint4*>(x + e0 + 2048 * i);
         } else {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int64_t e = e0 + 2048 * i;
-                pre[i] = e < row_elems ? *reinterpret_cast<const uint4*>(x + e) : make_uint4(0u, 0u, 0u, 0u);
+                pre[i] = e < end_elems ? *reinterpret_cast<const uint4*>(x + e) : make_uint4(0u, 0u, 0u, 0u);
             }
         }
     };
 
-    int64_t g = blockIdx.x;
-    if (g < ngroups) load_group(g);
+    int64_t r0 = r_begin;
+    if (r0 < r_end) load_group(r0);
     __syncthreads();  // inverse-permutation scratch consumed by every thread
 
-    for (int it = 0; g < ngroups; g += gridDim.x, ++it) {
+    for (int it = 0; r0 < r_end; r0 += rpg, ++it) {
         unsigned char* buf = smem + (kBufs == 2 ? (it & 1) * kRowBuf : 0);
         // ---- stage: signs, then scatter each element to its rotated block slot
 #pragma unroll
@@ -346,14 +352,18 @@ rpbh_quant_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int 
                 *reinterpret_cast<uint16_t*>(base + a) = h;
             }
         }
-        if (g + gridDim.x < ngroups) load_group(g + gridDim.x);
+        if (r0 + rpg < r_end) load_group(r0 + rpg);
         __syncthreads();
 
+        // A wave whose rows all lie past this workgroup's share (the partial last group) has nothing
+        // to compute; with rows spanning several waves (d > 4096) every wave joins the reductions.
+        const bool wave_busy = log2nb > 6 || r0 + ((64 * (tid >> 6)) >> log2nb) < r_end;
+        if (wave_busy) {
         double acc[kH];
         load_block_fwht(buf, tid, acc);
 
-        const int64_t row = g * rpg + rg;
-        const bool valid = row < rows;
+        const int64_t row = r0 + rg;
+        const bool valid = row < r_end;
 
         if (kOut == kRowInt8) {
             // amax = max |x'| = fl32(max |8x'| / 8) exactly (rounding is monotone), reduced over the row
@@ -484,6 +494,7 @@ rpbh_quant_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int 
                 }
             }
         }
+        }
         if (kBufs == 1) __syncthreads();  // every lane has read its block before the buffer is restaged
     }
 }
@@ -500,7 +511,8 @@ hipError_t launch_t(const RowArgs& a, int log2d, hipStream_t stream) {
     const hipError_t e = kernel_blocks_per_cu(reinterpret_cast<const void*>(kernel), kThreads, lds, &per_cu);
     if (e != hipSuccess) return e;
     const int64_t cap = static_cast<int64_t>(per_cu) * device_cu_count();
-    // even share of groups per workgroup, then as few workgroups as that share allows
+    // the fewest workgroups that keep every group count per workgroup at the minimum possible in
+    // one resident wave (measured faster than filling every slot with partial last groups)
     const int64_t per_wg = (ngroups + cap - 1) / cap;
     const int grid = static_cast<int>((ngroups + per_wg - 1) / per_wg);
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), lds, stream, static_cast<const uint16_t*>(a.x), a.rows,
