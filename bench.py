@@ -185,7 +185,12 @@ def bench_offline(args, torch, rtq, workloads):
     return {"bytes": total, "ms": ms, "GB/s": total / (ms * 1e-3) / 1e9}
 
 
-def bench_codebook(args, torch, rtq, workloads, variant):
+def bench_codebook(args, torch, rtq, workloads, variant, mode=None):
+    """One online codebook layer (quantise + product).  mode RTQ_CODEBOOK_I8 (default): codes on
+    the INT8 matrix cores (int8 codebook values, 1 byte per activation element); RTQ_CODEBOOK:
+    fp16 LUT product."""
+    mode = rtq.RTQ_CODEBOOK_I8 if mode is None else mode
+    i8 = mode == rtq.RTQ_CODEBOOK_I8
     if variant == "w4a4":
         d, N, bits_w = workloads.DIT_HIDDEN, workloads.DIT_HIDDEN, 4
         wh = workloads.w4a4_weight_bf16()
@@ -202,15 +207,15 @@ def bench_codebook(args, torch, rtq, workloads, variant):
     rtq.quantize_rows(w, wc, wn, R, rtq.RTQ_CODEBOOK, cb_w, 0.0)
     del w
     xs = _copies(_bf16_dev(xh, torch), 512 << 20, torch)
-    codes = torch.empty((T, d // 2), dtype=torch.uint8, device="cuda")
+    codes = torch.empty((T, d if i8 else d // 2), dtype=torch.int8 if i8 else torch.uint8, device="cuda")
     norm = torch.empty(T, dtype=torch.float32, device="cuda")
     y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
 
     def quant(i):
-        rtq.quantize_rows(xs[i % len(xs)], codes, norm, R, rtq.RTQ_CODEBOOK, cb_a, 1e-8)
+        rtq.quantize_rows(xs[i % len(xs)], codes, norm, R, mode, cb_a, 1e-8)
 
     def gemm(i):
-        rtq.qgemm(codes, norm, wc, wn, y, d, rtq.RTQ_CODEBOOK, cb_a, cb_w)
+        rtq.qgemm(codes, norm, wc, wn, y, d, mode, cb_a, cb_w)
 
     _prewarm(lambda i: (quant(i), gemm(i)), torch, 0.25)
     for i in range(args.warmup):
@@ -219,11 +224,13 @@ def bench_codebook(args, torch, rtq, workloads, variant):
     steps = max(5, args.steps // 2)
     wall, tq, tg = _time_pairs(steps, quant, gemm, torch)
     flops = 2.0 * T * d * N
-    q_bytes = T * (2 * d + d // 2 + 4)
-    return {"T": T, "d": d, "N": N, "step_ms": wall * 1e3 / steps, "quant_ms": float(tq.mean()),
+    q_bytes = T * (2 * d + (d if i8 else d // 2) + 4)
+    gemm_tflops = flops / (tg.mean() * 1e-3) / 1e12
+    peak = PEAK_INT8_TOPS if i8 else PEAK_F16_TFLOPS
+    return {"mode": "codebook on INT8 MFMA (int8 codebook values)" if i8 else "codebook, fp16 LUT on fp16 MFMA",
+            "T": T, "d": d, "N": N, "step_ms": wall * 1e3 / steps, "quant_ms": float(tq.mean()),
             "gemm_ms": float(tg.mean()), "TFLOP/s": flops / (wall / steps) / 1e12,
-            "gemm_TFLOP/s": flops / (tg.mean() * 1e-3) / 1e12, "gemm_frac_f16_peak":
-            flops / (tg.mean() * 1e-3) / 1e12 / PEAK_F16_TFLOPS,
+            "gemm_TFLOP/s": gemm_tflops, "gemm_peak": peak, "gemm_frac_peak": gemm_tflops / peak,
             "rpbh_GB/s": q_bytes / (tq.mean() * 1e-3) / 1e9}
 
 
@@ -321,7 +328,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
-    ap.add_argument("--only", choices=["w8a8", "all"], default="all",
+    ap.add_argument("--only", choices=["w8a8", "codebook", "all"], default="all",
                     help="w8a8: time only the headline step (profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain streaming kernel of known size (bitwise_not over 256 MiB of int8, "
@@ -353,12 +360,21 @@ def main():
             torch.bitwise_not(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
+    if args.only == "codebook":   # the codebook layers only (profiling runs)
+        out = {k: bench_codebook(args, torch, rtq, workloads, v) for k, v in
+               [("w4a4_dit_attn_out_4608x4096x4096", "w4a4"), ("w2a4_dit_mlp_down_4608x16384x4096", "w2a4")]}
+        print(json.dumps(out))
+        return
     r = bench_w8a8(args, torch, rtq, workloads)
     extra = {}
     if args.only == "all":
         extra["offline_weight_rotate_quantize"] = bench_offline(args, torch, rtq, workloads)
         extra["w4a4_dit_attn_out_4608x4096x4096"] = bench_codebook(args, torch, rtq, workloads, "w4a4")
         extra["w2a4_dit_mlp_down_4608x16384x4096"] = bench_codebook(args, torch, rtq, workloads, "w2a4")
+        extra["w4a4_dit_attn_out_4608x4096x4096_fp16_lut"] = bench_codebook(args, torch, rtq, workloads, "w4a4",
+                                                                            rtq.RTQ_CODEBOOK)
+        extra["w2a4_dit_mlp_down_4608x16384x4096_fp16_lut"] = bench_codebook(args, torch, rtq, workloads, "w2a4",
+                                                                             rtq.RTQ_CODEBOOK)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(workloads)

@@ -54,7 +54,15 @@ typedef enum {
 
 typedef enum {
     RTQ_INT8 = 0,     /* symmetric INT8, scale = max|v|/127, codes in [-127, 127]       */
-    RTQ_CODEBOOK = 1  /* L2 norm + Lloyd-Max direction codes of `bits` bits, packed     */
+    RTQ_CODEBOOK = 1, /* L2 norm + Lloyd-Max direction codes of `bits` bits, packed     */
+    RTQ_CODEBOOK_I8 = 2 /* the same Lloyd-Max codes, multiplied on the INT8 matrix cores:
+                         * each codebook enters the product as v_k = rint(c_k * S),
+                         * S = 127 / max_k |c_k| (largest centroid -> +-127), and y is
+                         * rescaled by 1/(S_a S_w).  Activations are then stored as their
+                         * int8 values v[code] (1 byte per element, not packed); weights
+                         * stay packed codes.  Relative Frobenius error of y against the
+                         * exact-centroid product: ~0.9% (W4A4) / ~0.5% (W2A4) on the DiT
+                         * synthetic shapes, inside the 2e-2 bound for bf16 outputs.    */
 } rtq_qmode;
 
 /* RPBH descriptor (OrbitQuant article, section 2.3).  perm (int32[d]) and signs (int8[d], +-1)
@@ -112,6 +120,8 @@ rtq_status rtq_rpbh_rotate(const void* x, rtq_dtype xt, void* y, rtq_dtype yt, i
  *              scale_t: BF16 for weights (eps = 0), F32 for activations (eps > 0, e.g. 1e-8).
  *              codes: uint8[rows][d * bits / 8], element j at byte j*bits/8, bit (j mod 8/bits)*bits
  *              (least significant first).  cb->bits must be 2 or 4.
+ *   CODEBOOK_I8: the CODEBOOK codes, written as their int8 codebook values v[code] (see
+ *              RTQ_CODEBOOK_I8): codes int8[rows][d].  cb needs centroids and boundaries.
  *   scale  [rows] of scale_t.
  * rows == 0 is a no-op. */
 rtq_status rtq_quantize_rows(const void* x, rtq_dtype xt, int64_t rows, int32_t d, const rtq_rpbh* R,
@@ -128,6 +138,11 @@ rtq_status rtq_quantize_rows(const void* x, rtq_dtype xt, int64_t rows, int32_t 
  *   CODEBOOK:  y = w_scale[n] * a_scale[t] * sum_j cb_w->centroids[qw] * cb_a->centroids[qa],
  *              accumulated in fp32 from fp16 copies of the centroids; yt F32 or BF16.
  *              cb_a->bits must be 4; cb_w->bits 2 or 4.
+ *   CODEBOOK_I8: a_codes int8[T][d] holds the activations' int8 codebook values (rtq_quantize_rows
+ *              in this mode), w_codes packed codes [N][d*bits_w/8]; acc = sum_j a[t][j] v_w[qw]
+ *              exactly in int32, y = acc * a_scale[t] * w_scale[n] / (S_a S_w) in fp32; yt F32 or
+ *              BF16.  cb_a (centroids, bits 2 or 4) gives S_a; cb_w (centroids, bits 2 or 4) the
+ *              weight values.  N <= 2^22, d a multiple of 64.
  * T == 0 is a no-op. */
 rtq_status rtq_qgemm(const void* a_codes, const float* a_scale, int64_t T, const void* w_codes,
                      const void* w_scale, rtq_dtype w_scale_t, int64_t N, int32_t d, rtq_qmode mode,
@@ -143,7 +158,8 @@ rtq_status rtq_rotated_qlinear(const void* x, rtq_dtype xt, int64_t T, const rtq
                                const rtq_codebook* cb_a, const rtq_codebook* cb_w, void* y, rtq_dtype yt,
                                void* workspace, size_t ws_bytes, void* stream);
 
-/* Bytes of workspace rtq_rotated_qlinear needs (codes + fp32 scales, each 256-byte aligned).
+/* Bytes of workspace rtq_rotated_qlinear needs (codes + fp32 scales, each 256-byte aligned; the
+ * codes take T*d bytes for RTQ_INT8 and RTQ_CODEBOOK_I8, T*d*bits_a/8 for RTQ_CODEBOOK).
  * bits_a is ignored for RTQ_INT8.  Returns 0 for invalid arguments. */
 size_t rtq_rotated_qlinear_workspace(int64_t T, int32_t d, rtq_qmode mode, int32_t bits_a);
 

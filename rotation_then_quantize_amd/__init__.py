@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_PKG, "librtq.so")
 
 RTQ_OK, RTQ_ERR_INVALID_ARG, RTQ_ERR_UNSUPPORTED, RTQ_ERR_MISALIGNED, RTQ_ERR_HIP = 0, -1, -2, -3, -4
 RTQ_F32, RTQ_BF16, RTQ_I32 = 0, 1, 2
-RTQ_INT8, RTQ_CODEBOOK = 0, 1
+RTQ_INT8, RTQ_CODEBOOK, RTQ_CODEBOOK_I8 = 0, 1, 2
 
 EXPORTS = ("rtq_rpbh_make", "rtq_lloyd_max", "rtq_rpbh_rotate", "rtq_quantize_rows", "rtq_qgemm",
            "rtq_rotated_qlinear", "rtq_rotated_qlinear_workspace", "rtq_last_error")
@@ -215,7 +215,7 @@ def rotated_qlinear(x, R: Rpbh, w_codes, w_scale, y, mode: int = RTQ_INT8, cb_a:
     """The online layer: rotate + quantise x, then the quantised product, on one stream."""
     torch = _torch()
     T = x.shape[0]
-    bits_a = cb_a.bits if (mode == RTQ_CODEBOOK and cb_a is not None) else 8
+    bits_a = cb_a.bits if (mode in (RTQ_CODEBOOK, RTQ_CODEBOOK_I8) and cb_a is not None) else 8
     need = rotated_qlinear_workspace(T, R.d, mode, bits_a)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)

@@ -37,6 +37,7 @@
 
 #include <algorithm>
 
+#include "codebook_int8.h"
 #include "rtq_internal.h"
 
 // The LDS-writing loads set M0 in inline assembly; M0 is otherwise unused by this kernel.
@@ -95,10 +96,51 @@ __device__ __forceinline__ void load_to_lds(v4i rsrc, uint32_t voff, uint32_t ld
 // Wait until at most n vector-memory operations of this wave are outstanding.
 template <int n>
 __device__ __forceinline__ void wait_vmcnt() {
-    static_assert(n == 0 || n == 4 || n == 8, "add the immediate");
+    static_assert(n == 0 || n == 2 || n == 3 || n == 4 || n == 8, "add the immediate");
     if constexpr (n == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if constexpr (n == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    if constexpr (n == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
     if constexpr (n == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     if constexpr (n == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+}
+
+// 4 bytes per lane from buffer offset voff to LDS address lds_addr + 4 * lane.
+__device__ __forceinline__ void load_to_lds4(v4i rsrc, uint32_t voff, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(static_cast<int>(lds_addr))), "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
+}
+
+// 32 packed 4-bit codes (LSB first) -> 32 int8 values in order (8 words)
+__device__ __forceinline__ void decode4(const uint32_t (&lut)[4], const uint32_t (&in)[4], uint32_t (&out)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t ev = lut16_x4(lut, in[i] & 0x0F0F0F0Fu);           // codes 0, 2, 4, 6 of the word
+        const uint32_t od = lut16_x4(lut, (in[i] >> 4) & 0x0F0F0F0Fu);    // codes 1, 3, 5, 7
+        out[2 * i] = __builtin_amdgcn_perm(od, ev, 0x05010400u);
+        out[2 * i + 1] = __builtin_amdgcn_perm(od, ev, 0x07030602u);
+    }
+}
+
+// 32 packed 2-bit codes (LSB first) -> 32 int8 values in order (8 words); lut[0] holds the 4 values
+__device__ __forceinline__ void decode2(const uint32_t (&lut)[4], const uint32_t (&in)[2], uint32_t (&out)[8]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        // vj = values of codes j, 4+j, 8+j, 12+j of the word
+        const uint32_t v0 = __builtin_amdgcn_perm(lut[0], lut[0], in[i] & 0x03030303u);
+        const uint32_t v1 = __builtin_amdgcn_perm(lut[0], lut[0], (in[i] >> 2) & 0x03030303u);
+        const uint32_t v2 = __builtin_amdgcn_perm(lut[0], lut[0], (in[i] >> 4) & 0x03030303u);
+        const uint32_t v3 = __builtin_amdgcn_perm(lut[0], lut[0], (in[i] >> 6) & 0x03030303u);
+        const uint32_t t01l = __builtin_amdgcn_perm(v1, v0, 0x05010400u);
+        const uint32_t t01h = __builtin_amdgcn_perm(v1, v0, 0x07030602u);
+        const uint32_t t23l = __builtin_amdgcn_perm(v3, v2, 0x05010400u);
+        const uint32_t t23h = __builtin_amdgcn_perm(v3, v2, 0x07030602u);
+        out[4 * i] = __builtin_amdgcn_perm(t23l, t01l, 0x05040100u);
+        out[4 * i + 1] = __builtin_amdgcn_perm(t23l, t01l, 0x07060302u);
+        out[4 * i + 2] = __builtin_amdgcn_perm(t23h, t01h, 0x05040100u);
+        out[4 * i + 3] = __builtin_amdgcn_perm(t23h, t01h, 0x07060302u);
+    }
 }
 
 // Tile index within the XCD-ordered sequence -> (tile_m, tile_n), in bands of 8 N-tiles.
@@ -111,17 +153,30 @@ __device__ __forceinline__ void tile_of(int lin, int tiles_m, int tiles_n, int* 
     *tn = band * kBand + in_band % band_w;
 }
 
-template <int kWavesN, int kYKind, bool kWScaleBF16, bool kVec>
+// LDS bytes of one stage of packed weight codes, and the ring of kRawSlots of them behind the
+// scales (codebook weights only).
+constexpr int raw_stage_bytes(int w_bits) { return w_bits < 8 ? BN * BK * w_bits / 8 : 0; }
+constexpr int kRawSlots = 3;
+constexpr int lds_bytes(int w_bits) { return kLds + kRawSlots * raw_stage_bytes(w_bits); }
+
+template <int kWavesN, int kYKind, bool kWScaleBF16, bool kVec, int kWBits>
 __global__ void __launch_bounds__(64 * kWavesM * kWavesN, 1)
 gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, const int8_t* __restrict__ W,
                const void* __restrict__ w_scale, int64_t T, int64_t N, int d, void* __restrict__ Y,
-               int tiles_m, int tiles_n) {
+               int tiles_m, int tiles_n, const float* __restrict__ cent_a, int a_bits,
+               const float* __restrict__ cent_w) {
     constexpr int kWaves = kWavesM * kWavesN;
+    // kWBits < 8: W holds packed codebook codes; they are loaded into a ring of raw LDS slots two
+    // stages ahead and decoded to int8 codebook values into the stage ring one stage ahead.
+    constexpr bool kCoded = kWBits < 8;
+    constexpr int kRawStage = raw_stage_bytes(kWBits);
+    constexpr int kCodeLoads = kWBits == 4 ? 1 : 2;     // LDS-writing loads per thread per code stage
+    static_assert(!kCoded || kYKind != 2, "raw accumulators only for int8 weights");
     constexpr int kThreads = 64 * kWaves;
     constexpr int WN = BN / kWavesN;                           // columns per wave
     constexpr int TM = WM / 32, TN = WN / 32;                  // MFMA tiles per wave
     constexpr int kLoadsPerOp = BM * BK / (kThreads * 16);     // 16-byte loads per thread per operand
-    constexpr int kLoadsPerStage = 2 * kLoadsPerOp;
+    constexpr int kLoadsPerStage = (kCoded ? 1 : 2) * kLoadsPerOp;   // A (and W when int8)
     constexpr int kScalesPerThread = (BM + BN) / kThreads;
 
     extern __shared__ __attribute__((aligned(16))) int8_t lds[];   // ring of stages, then scales
@@ -172,7 +227,8 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
         const int rows_a = static_cast<int>(min<int64_t>(BM, T - m0));
         const int rows_w = static_cast<int>(min<int64_t>(BN, N - n0));
         rsa = make_rsrc(A + m0 * d, static_cast<uint32_t>(rows_a * d));
-        rsw = make_rsrc(W + n0 * d, static_cast<uint32_t>(rows_w * d));
+        const int wrow = d * kWBits / 8;                      // bytes per weight row
+        rsw = make_rsrc(W + n0 * wrow, static_cast<uint32_t>(rows_w * wrow));
     };
     auto issue_stage = [&](int st) {
         const uint32_t sb = lds_base + static_cast<uint32_t>((st & (kStages - 1)) * kStageBytes) + wave_lds;
@@ -180,12 +236,55 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
 #pragma unroll
         for (int q = 0; q < kLoadsPerOp; ++q) {
             load_to_lds(rsa, load_off[q] + k0, sb + q * kWaves * 1024);
-            load_to_lds(rsw, load_off[q] + k0, sb + kOpBytes + q * kWaves * 1024);
+            if (!kCoded) load_to_lds(rsw, load_off[q] + k0, sb + kOpBytes + q * kWaves * 1024);
         }
+    };
+    // Packed weight codes of stage st -> raw slot st % kRawSlots, laid out [row][BK * bits / 8].
+    // 4-bit: one 16-byte load per thread (thread t: row t / 2, half t % 2 of the row's 32 bytes);
+    // 2-bit: two 4-byte loads per thread (load q, thread t: bytes q * 2048 + 4t of the slot).
+    const uint32_t raw_base = lds_base + static_cast<uint32_t>(kLds);
+    auto issue_codes = [&](int st) {
+        const uint32_t slot = raw_base + static_cast<uint32_t>((st % kRawSlots) * kRawStage);
+        const int wrow = d * kWBits / 8;
+        if constexpr (kWBits == 4) {
+            const uint32_t off = static_cast<uint32_t>((tid >> 1) * wrow + st * 32 + (tid & 1) * 16);
+            load_to_lds(rsw, off, slot + wave_lds);
+        } else if constexpr (kWBits == 2) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int b = q * 2048 + 4 * tid;                 // byte within the slot
+                const uint32_t off = static_cast<uint32_t>((b >> 4) * wrow + st * 16 + (b & 15));
+                load_to_lds4(rsw, off, slot + q * 2048 + static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave * 256)));
+            }
+        }
+    };
+    // Raw slot of stage st -> int8 values in the W half of stage st's ring slot.  Thread t decodes
+    // row t / 2, K bytes 32 * (t % 2) .. +32 (two 16-byte chunks of the swizzled row).
+    uint32_t lut[4] = {0u, 0u, 0u, 0u};
+    auto decode_stage = [&](int st) {
+        const int8_t* raw = lds + kLds + (st % kRawSlots) * kRawStage;
+        uint32_t v[8];
+        if constexpr (kWBits == 4) {
+            const v4i x = *reinterpret_cast<const v4i*>(raw + 16 * tid);
+            const uint32_t in[4] = {static_cast<uint32_t>(x.x), static_cast<uint32_t>(x.y),
+                                    static_cast<uint32_t>(x.z), static_cast<uint32_t>(x.w)};
+            decode4(lut, in, v);
+        } else if constexpr (kWBits == 2) {
+            const uint2 x = *reinterpret_cast<const uint2*>(raw + 8 * tid);
+            const uint32_t in[2] = {x.x, x.y};
+            decode2(lut, in, v);
+        }
+        const int row = tid >> 1, c0 = 2 * (tid & 1), sw = (row >> 2) & 3;
+        int8_t* wb = lds + (st & (kStages - 1)) * kStageBytes + kOpBytes + row * BK;
+        *reinterpret_cast<v4i*>(wb + (((c0) ^ sw) << 4)) =
+            v4i{static_cast<int>(v[0]), static_cast<int>(v[1]), static_cast<int>(v[2]), static_cast<int>(v[3])};
+        *reinterpret_cast<v4i*>(wb + (((c0 + 1) ^ sw) << 4)) =
+            v4i{static_cast<int>(v[4]), static_cast<int>(v[5]), static_cast<int>(v[6]), static_cast<int>(v[7])};
     };
     // The tile's token scales (entries 0..255) and output-row scales (256..511), one or two per
     // thread, staged in LDS behind the ring for the epilogue.
     float sc[kScalesPerThread];
+    float alpha = 1.0f;   // codebook operands: 1 / (S_a S_w), folded into the token scales
     auto load_scales = [&]() {
         if (kYKind == 2) return;
 #pragma unroll
@@ -193,7 +292,7 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
             const int k = tid + r * kThreads;
             sc[r] = 0.0f;
             if (k < BM) {
-                if (m0 + k < T) sc[r] = a_scale[m0 + k];
+                if (m0 + k < T) sc[r] = kCoded ? a_scale[m0 + k] * alpha : a_scale[m0 + k];
             } else if (n0 + (k - BM) < N) {
                 const int64_t n = n0 + (k - BM);
                 if (kWScaleBF16)
@@ -224,11 +323,26 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
                 acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[j], fa[i], acc[i][j], 0, 0, 0);
     };
 
-    // Stages 0 and 1 of a tile are fetched before the previous tile's epilogue (which stages its
-    // output through ring slots 2 and 3), stage 2 after it.
+    if constexpr (kCoded) {
+        const float sw = codebook_int8_scale(cent_w, 1 << kWBits);
+        codebook_int8_table(cent_w, 1 << kWBits, sw, lut);
+        alpha = 1.0f / (codebook_int8_scale(cent_a, 1 << a_bits) * sw);
+    }
+
+    // Stages 0 and 1 of a tile (and weight codes 0..2) are fetched before the previous tile's
+    // epilogue (which stages its output through ring slots 2 and 3), stage 2 after it.  Order of
+    // the loads matters for the waits: in the loop, iteration s issues stage s + 3 then codes s + 4.
+    auto prefetch_early = [&]() {
+        issue_stage(0);
+        if (kCoded) {
+            issue_codes(0);
+            if (nk > 1) issue_codes(1);
+        }
+        if (nk > 1) issue_stage(1);
+        if (kCoded && nk > 2) issue_codes(2);
+    };
     set_tile(lin);
-    issue_stage(0);
-    if (nk > 1) issue_stage(1);
+    prefetch_early();
     load_scales();
 
     for (;;) {
@@ -237,12 +351,19 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
 #pragma unroll
             for (int r = 0; r < kScalesPerThread; ++r) s_as[tid + r * kThreads] = sc[r];   // s_ws follows s_as
         }
-        // stages 0 and 1 have landed (and everything issued before them, e.g. earlier stores)
+        // stages 0 and 1 (and codes 0..2) have landed, with everything issued before them
+        // (e.g. the previous tile's stores); only stage 2 may be in flight
         if (nk > 2)
             wait_vmcnt<kLoadsPerStage>();
         else
             wait_vmcnt<0>();
-        RTQ_BARRIER();   // ... in every wave; the scales are visible
+        if constexpr (kCoded) {
+            RTQ_BARRIER();   // every wave's code loads have landed (2-bit rows are loaded by other waves)
+            decode_stage(0);
+            if (nk > 1) decode_stage(1);
+        }
+        RTQ_BARRIER();   // ... in every wave; the scales and decoded stages are visible
+        if (kCoded && nk > 3) issue_codes(3);   // raw slot 0: decoded above, in every wave
 
 #pragma unroll
         for (int i = 0; i < TM; ++i)
@@ -251,13 +372,27 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
         read_frags(fa0, fb0, 0, frag_off0);
 
         for (int s = 0; s < nk; ++s) {
-            // stage s + 1 must have landed (stage s + 2 may still be in flight)
-            if (s + 2 < nk)
-                wait_vmcnt<kLoadsPerStage>();
-            else
-                wait_vmcnt<0>();
+            // stage s + 1 (and codes s + 2) must have landed; what iteration s - 1 issued (stage
+            // s + 2, codes s + 3) may still be in flight
+            if constexpr (kCoded) {
+                if (s + 3 < nk)
+                    wait_vmcnt<kLoadsPerStage + kCodeLoads>();
+                else if (s + 2 < nk)
+                    wait_vmcnt<kLoadsPerStage>();
+                else
+                    wait_vmcnt<0>();
+            } else {
+                if (s + 2 < nk)
+                    wait_vmcnt<kLoadsPerStage>();
+                else
+                    wait_vmcnt<0>();
+            }
             RTQ_BARRIER();   // every wave's part of stage s + 1 is in LDS; stage s - 1 is consumed
             if (s + 3 < nk) issue_stage(s + 3);   // into stage s - 1's slot
+            if (kCoded) {
+                if (s + 4 < nk) issue_codes(s + 4);   // raw slot of codes s + 1, decoded last iteration
+                if (s + 2 < nk) decode_stage(s + 2);  // visible after the next barrier
+            }
             read_frags(fa1, fb1, s, frag_off1);
             mfmas(fa0, fb0);
             // (on the last stage this reads an unused slot: unconditional, so the compiler's LDS wait
@@ -283,8 +418,7 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
         const bool more = next < lin_end;
         if (more) {
             set_tile(next);
-            issue_stage(0);
-            if (nk > 1) issue_stage(1);
+            prefetch_early();
             load_scales();
         }
 
@@ -390,33 +524,36 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
     }
 }
 
-template <int kWavesN>
+template <int kWavesN, int kWBits>
 hipError_t launch_config(const GemmI8Args& g, hipStream_t stream) {
     using KernelFn = void (*)(const int8_t*, const float*, const int8_t*, const void*, int64_t, int64_t, int,
-                              void*, int, int);
+                              void*, int, int, const float*, int, const float*);
+    constexpr int kYKinds = kWBits == 8 ? 3 : 2;   // raw int32 output only for int8 weights
+    constexpr int kLdsBytes = lds_bytes(kWBits);
     // [w_scale bf16][N % 8 == 0][y kind]
     static const KernelFn kernels[2][2][3] = {
-        {{gemm_i8_kernel<kWavesN, 0, false, false>, gemm_i8_kernel<kWavesN, 1, false, false>,
-          gemm_i8_kernel<kWavesN, 2, false, false>},
-         {gemm_i8_kernel<kWavesN, 0, false, true>, gemm_i8_kernel<kWavesN, 1, false, true>,
-          gemm_i8_kernel<kWavesN, 2, false, true>}},
-        {{gemm_i8_kernel<kWavesN, 0, true, false>, gemm_i8_kernel<kWavesN, 1, true, false>,
-          gemm_i8_kernel<kWavesN, 2, true, false>},
-         {gemm_i8_kernel<kWavesN, 0, true, true>, gemm_i8_kernel<kWavesN, 1, true, true>,
-          gemm_i8_kernel<kWavesN, 2, true, true>}}};
+        {{gemm_i8_kernel<kWavesN, 0, false, false, kWBits>, gemm_i8_kernel<kWavesN, 1, false, false, kWBits>,
+          kYKinds > 2 ? gemm_i8_kernel<kWavesN, kYKinds - 1, false, false, kWBits> : nullptr},
+         {gemm_i8_kernel<kWavesN, 0, false, true, kWBits>, gemm_i8_kernel<kWavesN, 1, false, true, kWBits>,
+          kYKinds > 2 ? gemm_i8_kernel<kWavesN, kYKinds - 1, false, true, kWBits> : nullptr}},
+        {{gemm_i8_kernel<kWavesN, 0, true, false, kWBits>, gemm_i8_kernel<kWavesN, 1, true, false, kWBits>,
+          kYKinds > 2 ? gemm_i8_kernel<kWavesN, kYKinds - 1, true, false, kWBits> : nullptr},
+         {gemm_i8_kernel<kWavesN, 0, true, true, kWBits>, gemm_i8_kernel<kWavesN, 1, true, true, kWBits>,
+          kYKinds > 2 ? gemm_i8_kernel<kWavesN, kYKinds - 1, true, true, kWBits> : nullptr}}};
     static const hipError_t attr_err = [] {
         hipError_t e = hipSuccess;
         for (auto& a : kernels)
             for (auto& b : a)
                 for (KernelFn k : b) {
+                    if (k == nullptr) continue;
                     const hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                                                             hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+                                                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
                     if (r != hipSuccess) e = r;
                 }
         return e;
     }();
     if (attr_err != hipSuccess) return attr_err;
-    if (g.y_kind < 0 || g.y_kind > 2) return hipErrorInvalidValue;
+    if (g.y_kind < 0 || g.y_kind >= kYKinds) return hipErrorInvalidValue;
     const int64_t tiles_m = (g.T + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
     const int64_t total = tiles_m * tiles_n;
     if (total > (int64_t(1) << 30)) return hipErrorInvalidValue;
@@ -427,9 +564,9 @@ hipError_t launch_config(const GemmI8Args& g, hipStream_t stream) {
     const int64_t slots = std::max<int64_t>(kXcds, cus / kXcds * kXcds);
     const int64_t grid = std::min<int64_t>(slots, (total + kXcds - 1) / kXcds * kXcds);
     const KernelFn k = kernels[g.w_scale_bf16 ? 1 : 0][(g.N % 8) == 0 ? 1 : 0][g.y_kind];
-    hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(64 * kWavesM * kWavesN), kLds, stream, g.a,
+    hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(64 * kWavesM * kWavesN), kLdsBytes, stream, g.a,
                        g.a_scale, g.w, g.w_scale, g.T, g.N, g.d, g.y, static_cast<int>(tiles_m),
-                       static_cast<int>(tiles_n));
+                       static_cast<int>(tiles_n), g.cent_a, g.a_bits, g.cent_w);
     return hipGetLastError();
 }
 
@@ -439,7 +576,16 @@ hipError_t launch_gemm_i8(const GemmI8Args& g, hipStream_t stream) {
     if (g.T <= 0 || g.N <= 0) return hipSuccess;
     if (g.d % BK != 0 || g.d > 16384) return hipErrorInvalidValue;
     if (g.N > (int64_t(1) << 22)) return hipErrorInvalidValue;   // 32-bit store offsets within a row block
-    return launch_config<kDefaultWavesN>(g, stream);
+    switch (g.w_bits) {
+        case 8: return launch_config<kDefaultWavesN, 8>(g, stream);
+        case 4:
+            if (g.cent_a == nullptr || g.cent_w == nullptr || g.a_bits < 1 || g.a_bits > 4) return hipErrorInvalidValue;
+            return launch_config<kDefaultWavesN, 4>(g, stream);
+        case 2:
+            if (g.cent_a == nullptr || g.cent_w == nullptr || g.a_bits < 1 || g.a_bits > 4) return hipErrorInvalidValue;
+            return launch_config<kDefaultWavesN, 2>(g, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace rtq

@@ -28,6 +28,7 @@
 
 #include <algorithm>
 
+#include "codebook_int8.h"
 #include "rtq_internal.h"
 
 namespace rtq {
@@ -191,7 +192,12 @@ template <int kNC, int kOut>
 __global__ void __launch_bounds__(kThreads, 2)
 rpbh_quant_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int log2d, int log2nb,
                        const int32_t* __restrict__ perm, const int8_t* __restrict__ signs, void* __restrict__ out,
-                       void* __restrict__ scale_out, int scale_bf16, const float* __restrict__ bounds, float eps) {
+                       void* __restrict__ scale_out, int scale_bf16, const float* __restrict__ bounds, float eps,
+                       const float* __restrict__ cent) {
+    // codebook outputs: kRowCode* pack the codes, kRowLut* write each code's int8 codebook value
+    constexpr bool k4 = kOut == kRowCode4 || kOut == kRowLut4;
+    constexpr bool k2 = kOut == kRowCode2 || kOut == kRowLut2;
+    constexpr bool kLut = kOut == kRowLut4 || kOut == kRowLut2;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     // LDS: [row buffer(s) | prologue scratch overlaid][sign masks, d x u16 (kNC >= 4)][reduction]
     // d <= 4096: two row buffers, so staging group g+1 never waits for readers of group g
@@ -265,7 +271,7 @@ rpbh_quant_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int 
     }
 
     // ---- codebook set-up: this lane's boundary, and (4-bit) the lane's cell of the grid
-    constexpr int kBits = kOut == kRowCode4 ? 4 : (kOut == kRowCode2 ? 2 : 8);
+    constexpr int kBits = k4 ? 4 : (k2 ? 2 : 8);
     constexpr int kNB = (1 << kBits) - 1;
     const int row_lanes = (1 << log2nb) < 64 ? (1 << log2nb) : 64;   // lanes of my row in my wave
     const int lane_base = lane & ~(row_lanes - 1);
@@ -275,11 +281,13 @@ rpbh_quant_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int 
     uint32_t cell = 0;
     float grid_k = 0.0f;
     bool use_grid = false;
-    if (kOut == kRowCode2) {
+    uint32_t lut[4] = {0u, 0u, 0u, 0u};
+    if (kLut) codebook_int8_table(cent, 1 << kBits, codebook_int8_scale(cent, 1 << kBits), lut);
+    if (k2) {
 #pragma unroll
         for (int k = 0; k < 3; ++k) tb[k] = bounds[k];
     }
-    if (kOut == kRowCode4) {
+    if (k4) {
         if (kidx < kNB) my_t = bounds[kidx];
         // grid over [-tmax, tmax] with 40 cells of width tmax/20; 64 cells in all (end cells clamp)
         const float tmax = fmaxf(fabsf(bounds[0]), fabsf(bounds[kNB - 1]));
@@ -437,20 +445,22 @@ rpbh_quant_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int 
             ss = row_sum(ss, log2nb, red);
             const float s = static_cast<float>(sqrt(ss));
             const float den = (eps == 0.0f) ? s : s + eps;
-            constexpr int kPerWord = 32 / kBits;
+            // codes per 32-bit word: packed, or one per byte before the int8 table lookup
+            constexpr int kSlot = kLut ? 8 : kBits;
+            constexpr int kPerWord = 32 / kSlot;
             uint32_t w[kH / kPerWord];
 #pragma unroll
             for (int q = 0; q < kH / kPerWord; ++q) w[q] = 0u;
             if (den != 0.0f) {
                 // u = fl32(x'/den); code = #{k : t_k < u} = #{k : x' >= Y_k}, Y_k exact per row
-                if (kOut == kRowCode2) {
+                if (k2) {
                     float Y[3];
 #pragma unroll
                     for (int k = 0; k < 3; ++k) Y[k] = exact_threshold(tb[k], den);
 #pragma unroll
                     for (int b = 0; b < kH; ++b) {
                         const uint32_t code = (xr[b] >= Y[0] ? 1u : 0u) + (xr[b] >= Y[1] ? 1u : 0u) + (xr[b] >= Y[2] ? 1u : 0u);
-                        w[b / kPerWord] |= code << ((b % kPerWord) * kBits);
+                        w[b / kPerWord] |= code << ((b % kPerWord) * kSlot);
                     }
                 } else if (use_grid) {
                     // my slot holds Y_kidx (slot 15: +inf); cells hold (#below << 8) | 4*slot
@@ -463,7 +473,7 @@ rpbh_quant_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int 
                         const uint32_t e = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(a, static_cast<int>(cell)));
                         const float Yk = __int_as_float(__builtin_amdgcn_ds_bpermute(static_cast<int>(e) + base4, __float_as_int(myY)));
                         const uint32_t code = (e >> 8) + (xr[b] >= Yk ? 1u : 0u);
-                        w[b / kPerWord] |= code << ((b % kPerWord) * kBits);
+                        w[b / kPerWord] |= code << ((b % kPerWord) * kSlot);
                     }
                 } else {
                     // a general codebook, or too few lanes per row for the slot table: divide and count
@@ -472,7 +482,7 @@ rpbh_quant_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int 
                         const float u = xr[b] / den;
                         uint32_t code = 0;
                         for (int k = 0; k < kNB; ++k) code += (bounds[k] < u) ? 1u : 0u;
-                        w[b / kPerWord] |= code << ((b % kPerWord) * kBits);
+                        w[b / kPerWord] |= code << ((b % kPerWord) * kSlot);
                     }
                 }
             } else {
@@ -480,10 +490,14 @@ rpbh_quant_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int 
                 uint32_t code = 0;
                 for (int k = 0; k < kNB; ++k) code += (bounds[k] < 0.0f) ? 1u : 0u;
 #pragma unroll
-                for (int b = 0; b < kH; ++b) w[b / kPerWord] |= code << ((b % kPerWord) * kBits);
+                for (int b = 0; b < kH; ++b) w[b / kPerWord] |= code << ((b % kPerWord) * kSlot);
+            }
+            if (kLut) {
+#pragma unroll
+                for (int q = 0; q < kH / kPerWord; ++q) w[q] = k4 ? lut16_x4(lut, w[q]) : lut4_x4(lut, w[q]);
             }
             if (valid) {
-                uint4* o = reinterpret_cast<uint4*>(static_cast<uint8_t*>(out) + (row * d + blk * kH) * kBits / 8);
+                uint4* o = reinterpret_cast<uint4*>(static_cast<uint8_t*>(out) + (row * d + blk * kH) * kSlot / 8);
 #pragma unroll
                 for (int q = 0; q < kH / kPerWord / 4; ++q) o[q] = make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
                 if (blk == 0) {
@@ -516,7 +530,8 @@ hipError_t launch_t(const RowArgs& a, int log2d, hipStream_t stream) {
     const int64_t per_wg = (ngroups + cap - 1) / cap;
     const int grid = static_cast<int>((ngroups + per_wg - 1) / per_wg);
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), lds, stream, static_cast<const uint16_t*>(a.x), a.rows,
-                       a.d, log2d, log2nb, a.perm, a.signs, a.out, a.scale, a.scale_bf16 ? 1 : 0, a.bounds, a.eps);
+                       a.d, log2d, log2nb, a.perm, a.signs, a.out, a.scale, a.scale_bf16 ? 1 : 0, a.bounds, a.eps,
+                       a.centroids);
     return hipGetLastError();
 }
 
@@ -535,7 +550,8 @@ hipError_t launch_nc(const RowArgs& a, int log2d, hipStream_t stream) {
 
 bool rpbh_quant_bf16_supported(const RowArgs& a) {
     return a.x_bf16 && a.perm != nullptr &&
-           (a.out_kind == kRowInt8 || a.out_kind == kRowCode4 || a.out_kind == kRowCode2) && a.d >= 64 &&
+           (a.out_kind == kRowInt8 || a.out_kind == kRowCode4 || a.out_kind == kRowCode2 ||
+            a.out_kind == kRowLut4 || a.out_kind == kRowLut2) && a.d >= 64 &&
            a.d <= kMaxD;
 }
 
@@ -547,6 +563,8 @@ hipError_t launch_rpbh_quant_bf16(const RowArgs& a, hipStream_t stream) {
         case kRowInt8: return launch_nc<kRowInt8>(a, log2d, stream);
         case kRowCode4: return launch_nc<kRowCode4>(a, log2d, stream);
         case kRowCode2: return launch_nc<kRowCode2>(a, log2d, stream);
+        case kRowLut4: return launch_nc<kRowLut4>(a, log2d, stream);
+        case kRowLut2: return launch_nc<kRowLut2>(a, log2d, stream);
         default: break;
     }
     return hipErrorInvalidValue;

@@ -28,6 +28,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "codebook_int8.h"
 #include "rtq_internal.h"
 
 namespace rtq {
@@ -93,8 +94,12 @@ template <bool kBF16In, bool kRotate, int kOut>
 __global__ void __launch_bounds__(kThreads)
 rpbh_rows_kernel(const void* __restrict__ xin, int64_t rows, int d, int log2d, int log2nb,
                  const int32_t* __restrict__ perm, const int8_t* __restrict__ signs, void* __restrict__ out,
-                 void* __restrict__ scale_out, int scale_bf16, const float* __restrict__ bounds, float eps) {
+                 void* __restrict__ scale_out, int scale_bf16, const float* __restrict__ bounds, float eps,
+                 const float* __restrict__ cent) {
     constexpr int ES = kBF16In ? 2 : 4;
+    // codebook outputs: kRowCode* pack the codes, kRowLut* write each code's int8 codebook value
+    constexpr bool k4 = kOut == kRowCode4 || kOut == kRowLut4;
+    constexpr bool kLut = kOut == kRowLut4 || kOut == kRowLut2;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     unsigned char* rowbuf = smem;                          // kGroup elements
     unsigned char* maskbuf = smem + kGroup * ES;           // d sign masks (source order)
@@ -139,9 +144,11 @@ rpbh_rows_kernel(const void* __restrict__ xin, int64_t rows, int d, int log2d, i
         for (int b = 0; b < kH; ++b) addr[b] = ((static_cast<uint32_t>(rg) << log2d) + blk * kH + b) * ES;
     }
     float tb[15];
-    constexpr int kNB = kOut == kRowCode4 ? 15 : (kOut == kRowCode2 ? 3 : 0);
+    constexpr int kNB = k4 ? 15 : ((kOut == kRowCode2 || kOut == kRowLut2) ? 3 : 0);
 #pragma unroll
     for (int k = 0; k < kNB; ++k) tb[k] = bounds[k];
+    uint32_t lut[4] = {0u, 0u, 0u, 0u};
+    if (kLut) codebook_int8_table(cent, kNB + 1, codebook_int8_scale(cent, kNB + 1), lut);
     __syncthreads();
 
     const int64_t ngroups = (rows + rpg - 1) / rpg;
@@ -275,8 +282,9 @@ rpbh_rows_kernel(const void* __restrict__ xin, int64_t rows, int d, int log2d, i
             const float den = (eps == 0.0f) ? s : s + eps;
             const bool fast = s >= 0x1p-100f;
             const float den8 = den * 8.0f;
-            constexpr int kBits = kOut == kRowCode4 ? 4 : 2;
-            constexpr int kPerWord = 32 / kBits;
+            constexpr int kBits = k4 ? 4 : 2;
+            constexpr int kSlot = kLut ? 8 : kBits;      // bits per code in the output words
+            constexpr int kPerWord = 32 / kSlot;
             uint32_t w[kH / kPerWord];
 #pragma unroll
             for (int q = 0; q < kH / kPerWord; ++q) w[q] = 0u;
@@ -292,11 +300,19 @@ rpbh_rows_kernel(const void* __restrict__ xin, int64_t rows, int d, int log2d, i
                 uint32_t code = 0;
 #pragma unroll
                 for (int k = 0; k < kNB; ++k) code += (tb[k] < u) ? 1u : 0u;
-                w[b / kPerWord] |= code << ((b % kPerWord) * kBits);
+                w[b / kPerWord] |= code << ((b % kPerWord) * kSlot);
+            }
+            if (kLut) {
+#pragma unroll
+                for (int q = 0; q < kH / kPerWord; ++q) w[q] = k4 ? lut16_x4(lut, w[q]) : lut4_x4(lut, w[q]);
             }
             if (valid) {
-                uint32_t* o = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(out) + (row * d + blk * kH) * kBits / 8);
-                if (kBits == 4) {
+                uint32_t* o = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(out) + (row * d + blk * kH) * kSlot / 8);
+                if (kLut) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        reinterpret_cast<uint4*>(o)[q] = make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+                } else if (kBits == 4) {
                     reinterpret_cast<uint4*>(o)[0] = make_uint4(w[0], w[1], w[2], w[3]);
                     reinterpret_cast<uint4*>(o)[1] = make_uint4(w[4], w[5], w[6], w[7]);
                 } else {
@@ -413,7 +429,8 @@ hipError_t launch_rows_t(const RowArgs& a, hipStream_t stream) {
     const int64_t ngroups = (a.rows + rpg - 1) / rpg;
     const size_t lds = static_cast<size_t>(kGroup) * ES + static_cast<size_t>(a.d) * ES + kRedBytes;
     return launch_persistent(rpbh_rows_kernel<kBF16In, kRotate, kOut>, lds, ngroups, stream, a.x, a.rows, a.d,
-                             log2d, log2nb, a.perm, a.signs, a.out, a.scale, a.scale_bf16 ? 1 : 0, a.bounds, a.eps);
+                             log2d, log2nb, a.perm, a.signs, a.out, a.scale, a.scale_bf16 ? 1 : 0, a.bounds, a.eps,
+                             a.centroids);
 }
 
 template <bool kBF16In, bool kRotate>
@@ -424,6 +441,8 @@ hipError_t launch_rows_kind(const RowArgs& a, hipStream_t stream) {
         case kRowInt8: return launch_rows_t<kBF16In, kRotate, kRowInt8>(a, stream);
         case kRowCode4: return launch_rows_t<kBF16In, kRotate, kRowCode4>(a, stream);
         case kRowCode2: return launch_rows_t<kBF16In, kRotate, kRowCode2>(a, stream);
+        case kRowLut4: return launch_rows_t<kBF16In, kRotate, kRowLut4>(a, stream);
+        case kRowLut2: return launch_rows_t<kBF16In, kRotate, kRowLut2>(a, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -117,6 +117,12 @@ rtq_status plan_quantize(const void* x, rtq_dtype xt, int64_t rows, int32_t d, c
         if (!(eps >= 0.0f) || std::isinf(eps)) return fail(RTQ_ERR_INVALID_ARG, "eps must be finite and >= 0");
         a.out_kind = cb->bits == 4 ? rtq::kRowCode4 : rtq::kRowCode2;
         a.bounds = cb->boundaries;
+    } else if (mode == RTQ_CODEBOOK_I8) {
+        RTQ_TRY(check_codebook(cb, "cb", true, true));
+        if (!(eps >= 0.0f) || std::isinf(eps)) return fail(RTQ_ERR_INVALID_ARG, "eps must be finite and >= 0");
+        a.out_kind = cb->bits == 4 ? rtq::kRowLut4 : rtq::kRowLut2;
+        a.bounds = cb->boundaries;
+        a.centroids = cb->centroids;
     } else {
         return fail(RTQ_ERR_INVALID_ARG, "unknown mode %d", static_cast<int>(mode));
     }
@@ -163,6 +169,18 @@ rtq_status plan_gemm(const void* a_codes, const float* a_scale, int64_t T, const
         p.cb = rtq::GemmLutArgs{static_cast<const uint8_t*>(a_codes), a_scale, static_cast<const uint8_t*>(w_codes),
                                 w_scale, w_scale_t == RTQ_BF16, cb_a->centroids, cb_w->centroids, cb_a->bits,
                                 cb_w->bits, T, N, d, y, yt == RTQ_F32 ? 0 : 1};
+    } else if (mode == RTQ_CODEBOOK_I8) {
+        RTQ_TRY(check_codebook(cb_a, "cb_a", true, false));
+        RTQ_TRY(check_codebook(cb_w, "cb_w", true, false));
+        if (yt != RTQ_F32 && yt != RTQ_BF16) return fail(RTQ_ERR_UNSUPPORTED, "yt must be RTQ_F32 or RTQ_BF16");
+        if (N > (int64_t(1) << 22)) return fail(RTQ_ERR_UNSUPPORTED, "N too large (max %d)", 1 << 22);
+        p.lut = false;
+        p.i8 = rtq::GemmI8Args{static_cast<const int8_t*>(a_codes), a_scale, static_cast<const int8_t*>(w_codes),
+                               w_scale, w_scale_t == RTQ_BF16, T, N, d, y, yt == RTQ_F32 ? 0 : 1};
+        p.i8.w_bits = cb_w->bits;
+        p.i8.cent_a = cb_a->centroids;
+        p.i8.a_bits = cb_a->bits;
+        p.i8.cent_w = cb_w->centroids;
     } else {
         return fail(RTQ_ERR_INVALID_ARG, "unknown mode %d", static_cast<int>(mode));
     }
@@ -175,7 +193,7 @@ size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 size_t workspace_bytes(int64_t T, int32_t d, rtq_qmode mode, int32_t bits_a) {
     if (T < 0 || d <= 0) return 0;
     size_t code_bytes;
-    if (mode == RTQ_INT8)
+    if (mode == RTQ_INT8 || (mode == RTQ_CODEBOOK_I8 && (bits_a == 2 || bits_a == 4)))
         code_bytes = static_cast<size_t>(T) * static_cast<size_t>(d);
     else if (mode == RTQ_CODEBOOK && (bits_a == 2 || bits_a == 4))
         code_bytes = static_cast<size_t>(T) * static_cast<size_t>(d) * static_cast<size_t>(bits_a) / 8;
@@ -265,22 +283,24 @@ rtq_status rtq_rotated_qlinear(const void* x, rtq_dtype xt, int64_t T, const rtq
     const int32_t d = R->d;
     RTQ_TRY(check_d(d));
     if (yt == RTQ_I32) return fail(RTQ_ERR_UNSUPPORTED, "rtq_rotated_qlinear produces F32 or BF16 output");
-    if (mode == RTQ_CODEBOOK && cb_a == nullptr) return fail(RTQ_ERR_INVALID_ARG, "cb_a is NULL");
-    const int32_t bits_a = mode == RTQ_CODEBOOK ? cb_a->bits : 8;
+    const bool cbook = mode == RTQ_CODEBOOK || mode == RTQ_CODEBOOK_I8;
+    if (cbook && cb_a == nullptr) return fail(RTQ_ERR_INVALID_ARG, "cb_a is NULL");
+    const int32_t bits_a = cbook ? cb_a->bits : 8;
     const size_t need = workspace_bytes(T < 0 ? 0 : T, d, mode, bits_a);
     if (mode == RTQ_CODEBOOK && bits_a != 4)
         return fail(RTQ_ERR_UNSUPPORTED, "activation codes must be 4-bit (got %d)", bits_a);
+    if (need == 0 && T > 0) return fail(RTQ_ERR_INVALID_ARG, "unsupported mode or activation bits");
     if (workspace == nullptr) return fail(RTQ_ERR_INVALID_ARG, "workspace is NULL");
     if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return fail(RTQ_ERR_MISALIGNED, "workspace is not 16-byte aligned");
     if (ws_bytes < need) return fail(RTQ_ERR_INVALID_ARG, "workspace too small: %zu < %zu bytes", ws_bytes, need);
     unsigned char* ws = static_cast<unsigned char*>(workspace);
-    const size_t code_bytes = mode == RTQ_INT8 ? static_cast<size_t>(T < 0 ? 0 : T) * d
-                                               : static_cast<size_t>(T < 0 ? 0 : T) * d * bits_a / 8;
+    const size_t code_bytes = mode == RTQ_CODEBOOK ? static_cast<size_t>(T < 0 ? 0 : T) * d * bits_a / 8
+                                                   : static_cast<size_t>(T < 0 ? 0 : T) * d;
     void* a_codes = ws;
     float* a_scale = reinterpret_cast<float*>(ws + align256(code_bytes));
     rtq::RowArgs qa{};
-    RTQ_TRY(plan_quantize(x, xt, T, d, R, mode, mode == RTQ_CODEBOOK ? cb_a : nullptr,
-                          mode == RTQ_CODEBOOK ? 1e-8f : 0.0f, a_codes, a_scale, RTQ_F32, &qa));
+    RTQ_TRY(plan_quantize(x, xt, T, d, R, mode, cbook ? cb_a : nullptr, cbook ? 1e-8f : 0.0f, a_codes, a_scale,
+                          RTQ_F32, &qa));
     GemmPlan gp{};
     RTQ_TRY(plan_gemm(a_codes, a_scale, T, w_codes, w_scale, w_scale_t, N, d, mode, cb_a, cb_w, y, yt, &gp));
     if (T == 0) return ok();

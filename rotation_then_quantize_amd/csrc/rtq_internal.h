@@ -14,6 +14,8 @@ enum RowOut : int {
     kRowInt8 = 2,     // symmetric INT8 codes + per-row scale
     kRowCode4 = 3,    // 4-bit Lloyd-Max codes (packed) + row norm
     kRowCode2 = 4,    // 2-bit Lloyd-Max codes (packed) + row norm
+    kRowLut4 = 5,     // 4-bit Lloyd-Max codes written as their int8 codebook values (1 byte each) + norm
+    kRowLut2 = 6,     // 2-bit Lloyd-Max codes written as their int8 codebook values + norm
 };
 
 struct RowArgs {
@@ -29,6 +31,7 @@ struct RowArgs {
     bool scale_bf16;
     const float* bounds;    // codebook boundaries (device), 2^bits - 1 entries
     float eps;
+    const float* centroids = nullptr;   // codebook centroids (device), 2^bits entries (kRowLut*)
 };
 
 hipError_t launch_rpbh_rows(const RowArgs& a, hipStream_t stream);
@@ -48,15 +51,21 @@ hipError_t launch_rpbh_inverse(const void* y, bool y_bf16, void* x, bool x_bf16,
                                const int32_t* perm, const int8_t* signs, hipStream_t stream);
 
 struct GemmI8Args {
-    const int8_t* a;        // [T][d]
+    const int8_t* a;        // [T][d] int8 operand (INT8 codes, or int8 codebook values)
     const float* a_scale;   // [T]
-    const int8_t* w;        // [N][d]
+    const int8_t* w;        // [N][d] int8 codes (w_bits 8), or [N][d*w_bits/8] packed codebook codes
     const void* w_scale;    // [N] fp32 or bf16
     bool w_scale_bf16;
     int64_t T, N;
     int d;
     void* y;                // [T][N]
-    int y_kind;             // 0 fp32, 1 bf16, 2 raw int32
+    int y_kind;             // 0 fp32, 1 bf16, 2 raw int32 (w_bits 8 only)
+    // codebook operands on the INT8 matrix cores (w_bits 4 or 2): both codebooks are rounded to
+    // int8 as v_k = rint(c_k * S), S = 127 / max_k |c_k|; the product is rescaled by 1/(S_a S_w)
+    int w_bits = 8;
+    const float* cent_a = nullptr;   // activation codebook centroids (device), 2^a_bits
+    int a_bits = 0;
+    const float* cent_w = nullptr;   // weight codebook centroids (device), 2^w_bits
 };
 
 hipError_t launch_gemm_i8(const GemmI8Args& g, hipStream_t stream);

@@ -1,0 +1,201 @@
+"""GPU parity of the codebook path on the INT8 matrix cores (RTQ_CODEBOOK_I8).
+
+The mode keeps the Lloyd-Max codes of the method and changes only the numbers the product sees:
+each codebook enters as v_k = rint(c_k * S), S = 127 / max_k |c_k| (fp32 arithmetic, as the
+header states).  So the tests check two things separately:
+  * the integer part is exact: activation values are the table entries of the oracle's codes
+    (same boundary allowance as the packed codes), and the product equals the int64 product of
+    the tables, rescaled by a_scale * w_scale / (S_a S_w), to fp32/bf16 rounding;
+  * the whole layer stays within the benchmark spec's bound (2e-2 relative Frobenius, bf16 output) of
+    the oracle's exact-centroid product.
+The table is computed here from the oracle's centroids with numpy fp32 arithmetic (the rule in
+include/rtq.h), independently of the library."""
+import numpy as np
+import pytest
+
+import oracle
+import rotation_then_quantize_amd as rtq
+import workloads
+from _helpers import bf16_host, codebook_mismatches_allowed, dense_pi, rel_fro, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    rtq.load_library()
+
+
+def int8_table(centroids):
+    """(S, v) with S = fl32(127 / max|c|) and v_k = rint(fl32(c_k * S)) as int8."""
+    c = np.asarray(centroids, np.float32)
+    s = np.float32(127.0) / np.max(np.abs(c))
+    v = np.rint(c * s).astype(np.int8)
+    return s, v
+
+
+def codes_of(values, table):
+    """Invert the (injective) table: int8 values -> codes."""
+    lookup = {int(v): k for k, v in enumerate(table)}
+    assert len(lookup) == len(table)
+    flat = np.array([lookup.get(int(v), -1) for v in values.ravel()], np.int64)
+    assert (flat >= 0).all(), "value outside the codebook table"
+    return flat.reshape(values.shape)
+
+
+def test_int8_tables_are_injective_and_symmetric():
+    for d, bits in [(4096, 4), (16384, 4), (16384, 2), (256, 2), (1024, 4)]:
+        s, v = int8_table(oracle.lloyd_max(bits, d)["centroids"])
+        assert len(set(v.tolist())) == len(v)
+        assert np.array_equal(v, -v[::-1])
+        assert np.max(np.abs(v)) == 127
+
+
+@pytest.mark.parametrize("d,rows,bits", [(4096, 130, 4), (16384, 6, 4), (256, 65, 2), (1024, 40, 4)])
+def test_quantize_codebook_i8_values(d, rows, bits):
+    xf = workloads.small_case(900 + d + bits, rows, d, "t3")
+    xf[rows - 1] = 0.0
+    xh = workloads.f32_to_bf16_bits(xf)
+    xf = workloads.bf16_bits_to_f32(xh)
+    seed = 21 + d
+    cb = rtq.Codebook.for_dim(d, bits)
+    ref_cb = oracle.lloyd_max(bits, d)
+    _, table = int8_table(ref_cb["centroids"])
+    vals = torch.empty((rows, d), dtype=torch.int8, device="cuda")
+    scale = torch.empty(rows, dtype=torch.float32, device="cuda")
+    rtq.quantize_rows(to_dev(xh, "bf16"), vals, scale, rtq.Rpbh.from_seed(seed, d), rtq.RTQ_CODEBOOK_I8, cb, 1e-8)
+    torch.cuda.synchronize()
+    _, rot = oracle.rotate(xf, dense_pi(seed, d))
+    co, so, u = oracle.quantize_codebook(rot, ref_cb["boundaries"], False, 1e-8)
+    assert np.array_equal(scale.cpu().numpy(), so)
+    got = codes_of(vals.cpu().numpy(), table)
+    n_bad, n_out = codebook_mismatches_allowed(got, co, u, ref_cb["boundaries"], d)
+    assert n_out == 0, f"{n_bad} mismatches, {n_out} outside the boundary allowance"
+    assert np.all(got[rows - 1] == (1 << bits) // 2 - 1)
+
+
+def test_quantize_codebook_i8_fp32_input_without_rotation():
+    # the generic row kernel (fp32 input, rows already rotated)
+    d, rows, bits = 512, 33, 4
+    rng = np.random.default_rng(5)
+    xf = (rng.standard_normal((rows, d)) / np.sqrt(d)).astype(np.float32)
+    cb = rtq.Codebook.for_dim(d, bits)
+    ref_cb = oracle.lloyd_max(bits, d)
+    _, table = int8_table(ref_cb["centroids"])
+    vals = torch.empty((rows, d), dtype=torch.int8, device="cuda")
+    scale = torch.empty(rows, dtype=torch.float32, device="cuda")
+    rtq.quantize_rows(to_dev(xf), vals, scale, None, rtq.RTQ_CODEBOOK_I8, cb, 1e-8)
+    torch.cuda.synchronize()
+    co, so, u = oracle.quantize_codebook(xf, ref_cb["boundaries"], False, 1e-8)
+    assert np.array_equal(scale.cpu().numpy(), so)
+    got = codes_of(vals.cpu().numpy(), table)
+    assert codebook_mismatches_allowed(got, co, u, ref_cb["boundaries"], d)[1] == 0
+
+
+@pytest.mark.parametrize("bits_w", [4, 2])
+@pytest.mark.parametrize("yt,wst", [("f32", "f32"), ("bf16", "bf16"), ("bf16", "f32")])
+@pytest.mark.parametrize("T,N,d", [(130, 200, 256), (300, 521, 1024), (64, 384, 4096), (7, 9, 64), (257, 130, 128)])
+def test_codebook_i8_gemm(bits_w, yt, wst, T, N, d):
+    rng = np.random.default_rng(T + 7 * N + d + bits_w)
+    qa = rng.integers(0, 16, size=(T, d)).astype(np.uint8)
+    qw = rng.integers(0, 1 << bits_w, size=(N, d)).astype(np.uint8)
+    ocb_a, ocb_w = oracle.lloyd_max(4, d), oracle.lloyd_max(bits_w, d)
+    sa_i, ta = int8_table(ocb_a["centroids"])
+    sw_i, tw = int8_table(ocb_w["centroids"])
+    s_a = (rng.random(T) * 10 + 1).astype(np.float32)
+    if wst == "bf16":
+        r_wb = oracle.to_bf16_bits(rng.random(N) + 0.5)
+        r_w = oracle.bf16_bits_to_f32(r_wb)
+        w_scale = to_dev(r_wb, "bf16")
+    else:
+        r_w = (rng.random(N) + 0.5).astype(np.float32)
+        w_scale = to_dev(r_w)
+    y = torch.empty((T, N), dtype=torch.float32 if yt == "f32" else torch.bfloat16, device="cuda")
+    rtq.qgemm(to_dev(ta[qa]), to_dev(s_a), to_dev(oracle.pack(qw, bits_w)), w_scale, y, d, rtq.RTQ_CODEBOOK_I8,
+              rtq.Codebook.for_dim(d, 4), rtq.Codebook.for_dim(d, bits_w))
+    torch.cuda.synchronize()
+    got = y.cpu().numpy().astype(np.float64) if yt == "f32" else oracle.bf16_bits_to_f32(bf16_host(y))
+    # integer part: exact int64 product of the two tables
+    acc = ta[qa].astype(np.int64) @ tw[qw].astype(np.int64).T
+    y_int = acc * s_a.astype(np.float64)[:, None] * r_w.astype(np.float64)[None, :] / (float(sa_i) * float(sw_i))
+    assert rel_fro(got, y_int) <= (1e-5 if yt == "f32" else 4e-3)
+    # against the oracle's exact-centroid product: inside the bf16 bound
+    ref = oracle.gemm_codebook(qa, qw, ocb_a["centroids"], ocb_w["centroids"], s_a, r_w)
+    assert rel_fro(got, ref) <= 2e-2
+
+
+@pytest.mark.parametrize("bits_w,T,N,d", [(4, 200, 256, 4096), (2, 70, 130, 16384), (4, 33, 65, 256),
+                                          (2, 300, 520, 1024)])
+def test_codebook_i8_layer_small(bits_w, T, N, d):
+    xf = workloads.small_case(710 + d, T, d, "t3")
+    wf = workloads.small_case(711 + d, N, d, "w")
+    xh, wh = workloads.f32_to_bf16_bits(xf), workloads.f32_to_bf16_bits(wf)
+    xf, wf = workloads.bf16_bits_to_f32(xh), workloads.bf16_bits_to_f32(wh)
+    seed = 47
+    R = rtq.Rpbh.from_seed(seed, d)
+    cb_a, cb_w = rtq.Codebook.for_dim(d, 4), rtq.Codebook.for_dim(d, bits_w)
+    wcodes = torch.empty((N, d * bits_w // 8), dtype=torch.uint8, device="cuda")
+    wnorm = torch.empty(N, dtype=torch.bfloat16, device="cuda")
+    rtq.quantize_rows(to_dev(wh, "bf16"), wcodes, wnorm, R, rtq.RTQ_CODEBOOK, cb_w, 0.0)
+    y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    need = rtq.rotated_qlinear_workspace(T, d, rtq.RTQ_CODEBOOK_I8, 4)
+    assert need == ((T * d + 255) // 256) * 256 + ((4 * T + 255) // 256) * 256
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    rtq.rotated_qlinear(to_dev(xh, "bf16"), R, wcodes, wnorm, y, rtq.RTQ_CODEBOOK_I8, cb_a, cb_w, workspace=ws)
+    torch.cuda.synchronize()
+    pi = dense_pi(seed, d)
+    ocb_a, ocb_w = oracle.lloyd_max(4, d), oracle.lloyd_max(bits_w, d)
+    wo = oracle.weights_codebook(wf, pi, ocb_w, bits_w)
+    assert codebook_mismatches_allowed(oracle.unpack(wcodes.cpu().numpy(), d, bits_w), wo["codes"], wo["u"],
+                                       ocb_w["boundaries"], d)[1] == 0
+    out = oracle.qlinear_codebook(xf, pi, wo, ocb_a, ocb_w, 4)
+    # the workspace holds the activations' int8 codebook values and their norms
+    _, ta = int8_table(ocb_a["centroids"])
+    a_codes = codes_of(ws[:T * d].view(T, d).cpu().numpy().view(np.int8), ta)
+    assert codebook_mismatches_allowed(a_codes, out["act"]["codes"], out["act"]["u"], ocb_a["boundaries"], d)[1] == 0
+    off = ((T * d + 255) // 256) * 256
+    assert np.array_equal(ws[off:off + 4 * T].view(torch.float32).cpu().numpy(), out["act"]["norm"])
+    got = workloads.bf16_bits_to_f32(bf16_host(y))
+    assert rel_fro(got, out["y"]) <= 2e-2
+
+
+@pytest.mark.parametrize("variant", ["w4a4", "w2a4"])
+def test_codebook_i8_dit_shape_sampled(variant):
+    # the benchmark's codebook layers, launched on the full tensors as the benchmark does
+    if variant == "w4a4":
+        d, N, bits_w = workloads.DIT_HIDDEN, workloads.DIT_HIDDEN, 4
+        xh, wh = workloads.dit_activations_bf16(d), workloads.w4a4_weight_bf16()
+        nr, nc = 8, 24
+    else:
+        d, N, bits_w = workloads.DIT_MLP, workloads.DIT_HIDDEN, 2
+        xh, wh = workloads.dit_activations_bf16(d), workloads.w2a4_weight_bf16()
+        nr, nc = 3, 6
+    T = xh.shape[0]
+    seed = workloads.RPBH_SEED[d]
+    R = rtq.Rpbh.from_seed(seed, d)
+    cb_a, cb_w = rtq.Codebook.for_dim(d, 4), rtq.Codebook.for_dim(d, bits_w)
+    wcodes = torch.empty((N, d * bits_w // 8), dtype=torch.uint8, device="cuda")
+    wnorm = torch.empty(N, dtype=torch.bfloat16, device="cuda")
+    rtq.quantize_rows(to_dev(wh, "bf16"), wcodes, wnorm, R, rtq.RTQ_CODEBOOK, cb_w, 0.0)
+    y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    work = torch.empty(rtq.rotated_qlinear_workspace(T, d, rtq.RTQ_CODEBOOK_I8, 4), dtype=torch.uint8,
+                       device="cuda")
+    rtq.rotated_qlinear(to_dev(xh, "bf16"), R, wcodes, wnorm, y, rtq.RTQ_CODEBOOK_I8, cb_a, cb_w, workspace=work)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(97)
+    rows = np.concatenate([[T - 1], np.sort(rng.choice(np.arange(0, T - 1), nr - 1, replace=False))])
+    cols = np.concatenate([[N - 1], np.sort(rng.choice(np.arange(0, N - 1), nc - 1, replace=False))])
+    pi = dense_pi(seed, d)
+    ocb_a, ocb_w = oracle.lloyd_max(4, d), oracle.lloyd_max(bits_w, d)
+    wo = oracle.weights_codebook(workloads.bf16_bits_to_f32(wh[cols]), pi, ocb_w, bits_w)
+    ao = oracle.activations_codebook(workloads.bf16_bits_to_f32(xh[rows]), pi, ocb_a, 4)
+    _, ta = int8_table(ocb_a["centroids"])
+    a_codes = codes_of(work[:T * d].view(T, d).cpu().numpy().view(np.int8)[rows], ta)
+    assert codebook_mismatches_allowed(a_codes, ao["codes"], ao["u"], ocb_a["boundaries"], d)[1] == 0
+    ref = oracle.gemm_codebook(ao["codes"], wo["codes"], ocb_a["centroids"], ocb_w["centroids"], ao["norm"],
+                               wo["norm"])
+    got = workloads.bf16_bits_to_f32(bf16_host(y))[np.ix_(rows, cols)]
+    assert rel_fro(got, ref) <= 2e-2
