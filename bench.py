@@ -126,8 +126,10 @@ def bench_w8a8(args, torch, rtq, workloads):
     def quant(i):
         rtq.quantize_rows(xs[i % len(xs)], codes, scale, R, rtq.RTQ_INT8)
 
+    split_ws = torch.empty(rtq.qgemm_workspace(), dtype=torch.uint8, device="cuda")
+
     def gemm(i):
-        rtq.qgemm(codes, scale, wq, ws, y, d)
+        rtq.qgemm(codes, scale, wq, ws, y, d, workspace=split_ws)
 
     prewarm = _prewarm(lambda i: (quant(i), gemm(i)), torch)
     for i in range(args.warmup):
@@ -214,8 +216,10 @@ def bench_codebook(args, torch, rtq, workloads, variant, mode=None):
     def quant(i):
         rtq.quantize_rows(xs[i % len(xs)], codes, norm, R, mode, cb_a, 1e-8)
 
+    split_ws = torch.empty(rtq.qgemm_workspace(), dtype=torch.uint8, device="cuda")
+
     def gemm(i):
-        rtq.qgemm(codes, norm, wc, wn, y, d, mode, cb_a, cb_w)
+        rtq.qgemm(codes, norm, wc, wn, y, d, mode, cb_a, cb_w, workspace=split_ws)
 
     _prewarm(lambda i: (quant(i), gemm(i)), torch, 0.25)
     for i in range(args.warmup):

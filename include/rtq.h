@@ -148,18 +148,37 @@ rtq_status rtq_qgemm(const void* a_codes, const float* a_scale, int64_t T, const
                      const void* w_scale, rtq_dtype w_scale_t, int64_t N, int32_t d, rtq_qmode mode,
                      const rtq_codebook* cb_a, const rtq_codebook* cb_w, void* y, rtq_dtype yt, void* stream);
 
+/* rtq_qgemm with a workspace for the INT8-core modes (RTQ_INT8, RTQ_CODEBOOK_I8): the tiles of the
+ * last, partial round of 256 x 256 output tiles are split along d over the otherwise idle compute
+ * units; each piece stores an int32 partial tile in the workspace and the last piece of a tile to
+ * finish adds the others (exact int32 sums, so results equal rtq_qgemm's bit for bit).
+ *   workspace: device memory of at least rtq_qgemm_workspace() bytes, 16-byte aligned, any
+ *   contents (per-tile arrival counters carry a launch tag, so no clearing is needed).  Launches
+ *   that share a workspace must not run concurrently.  A smaller or NULL workspace, or the
+ *   RTQ_CODEBOOK mode, gives exactly rtq_qgemm. */
+rtq_status rtq_qgemm_ws(const void* a_codes, const float* a_scale, int64_t T, const void* w_codes,
+                        const void* w_scale, rtq_dtype w_scale_t, int64_t N, int32_t d, rtq_qmode mode,
+                        const rtq_codebook* cb_a, const rtq_codebook* cb_w, void* y, rtq_dtype yt,
+                        void* workspace, size_t ws_bytes, void* stream);
+
+/* Bytes of workspace rtq_qgemm_ws uses on the current device: one 256 KB int32 partial tile and
+ * one 8-byte counter per compute unit (64 MB on a 256-CU MI355X). */
+size_t rtq_qgemm_workspace(void);
+
 /* The online layer: rtq_quantize_rows(x, R, mode, cb_a, eps = 1e-8 (CODEBOOK) ...) into `workspace`
  * followed by rtq_qgemm on the same stream (OrbitQuant article, section 2.2, steps 1-5 and the
  * cancellation).  Weights come from rtq_quantize_rows with the SAME descriptor R.
  *   workspace: device memory of at least rtq_rotated_qlinear_workspace(T, R->d, mode, bits_a) bytes,
- *   16-byte aligned; its contents on return are the activation codes and scales. */
+ *   16-byte aligned; on return it starts with the activation codes and scales. */
 rtq_status rtq_rotated_qlinear(const void* x, rtq_dtype xt, int64_t T, const rtq_rpbh* R, const void* w_codes,
                                const void* w_scale, rtq_dtype w_scale_t, int64_t N, rtq_qmode mode,
                                const rtq_codebook* cb_a, const rtq_codebook* cb_w, void* y, rtq_dtype yt,
                                void* workspace, size_t ws_bytes, void* stream);
 
-/* Bytes of workspace rtq_rotated_qlinear needs (codes + fp32 scales, each 256-byte aligned; the
- * codes take T*d bytes for RTQ_INT8 and RTQ_CODEBOOK_I8, T*d*bits_a/8 for RTQ_CODEBOOK).
+/* Bytes of workspace rtq_rotated_qlinear uses: the codes and fp32 scales (each 256-byte aligned;
+ * the codes take T*d bytes for RTQ_INT8 and RTQ_CODEBOOK_I8, T*d*bits_a/8 for RTQ_CODEBOOK), then,
+ * for the INT8-core modes, rtq_qgemm_workspace() bytes for the product's K-split.  A workspace
+ * that holds only the codes and scales is accepted (the product then runs without the split).
  * bits_a is ignored for RTQ_INT8.  Returns 0 for invalid arguments. */
 size_t rtq_rotated_qlinear_workspace(int64_t T, int32_t d, rtq_qmode mode, int32_t bits_a);
 

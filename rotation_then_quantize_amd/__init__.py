@@ -23,7 +23,8 @@ RTQ_F32, RTQ_BF16, RTQ_I32 = 0, 1, 2
 RTQ_INT8, RTQ_CODEBOOK, RTQ_CODEBOOK_I8 = 0, 1, 2
 
 EXPORTS = ("rtq_rpbh_make", "rtq_lloyd_max", "rtq_rpbh_rotate", "rtq_quantize_rows", "rtq_qgemm",
-           "rtq_rotated_qlinear", "rtq_rotated_qlinear_workspace", "rtq_last_error")
+           "rtq_qgemm_ws", "rtq_qgemm_workspace", "rtq_rotated_qlinear", "rtq_rotated_qlinear_workspace",
+           "rtq_last_error")
 
 
 class RtqError(RuntimeError):
@@ -61,13 +62,16 @@ def load_library():
     lib.rtq_rpbh_rotate.argtypes = [vp, i32, vp, i32, i64, R, i32, vp]
     lib.rtq_quantize_rows.argtypes = [vp, i32, i64, i32, R, i32, C, f32, vp, vp, i32, vp]
     lib.rtq_qgemm.argtypes = [vp, vp, i64, vp, vp, i32, i64, i32, i32, C, C, vp, i32, vp]
+    lib.rtq_qgemm_ws.argtypes = [vp, vp, i64, vp, vp, i32, i64, i32, i32, C, C, vp, i32, vp, sz, vp]
+    lib.rtq_qgemm_workspace.argtypes = []
+    lib.rtq_qgemm_workspace.restype = sz
     lib.rtq_rotated_qlinear.argtypes = [vp, i32, i64, R, vp, vp, i32, i64, i32, C, C, vp, i32, vp, sz, vp]
     lib.rtq_rotated_qlinear_workspace.argtypes = [i64, i32, i32, i32]
     lib.rtq_rotated_qlinear_workspace.restype = sz
     lib.rtq_last_error.argtypes = []
     lib.rtq_last_error.restype = ctypes.c_char_p
     for name in ("rtq_rpbh_make", "rtq_lloyd_max", "rtq_rpbh_rotate", "rtq_quantize_rows", "rtq_qgemm",
-                 "rtq_rotated_qlinear"):
+                 "rtq_qgemm_ws", "rtq_rotated_qlinear"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -196,14 +200,26 @@ def quantize_rows(x, codes, scale, R: Rpbh | None = None, mode: int = RTQ_INT8, 
 
 
 def qgemm(a_codes, a_scale, w_codes, w_scale, y, d: int, mode: int = RTQ_INT8, cb_a: Codebook | None = None,
-          cb_w: Codebook | None = None, stream=None):
-    """y = dequantised product of activation and weight codes (rotation already cancelled)."""
+          cb_w: Codebook | None = None, stream=None, workspace=None):
+    """y = dequantised product of activation and weight codes (rotation already cancelled).
+    With a workspace (qgemm_workspace() bytes) this is rtq_qgemm_ws: the last partial round of
+    tiles is split along d over idle compute units."""
     T = a_codes.shape[0]
     N = w_codes.shape[0]
-    _check(load_library().rtq_qgemm(_ptr(a_codes), _ptr(a_scale), T, _ptr(w_codes), _ptr(w_scale),
-                                    _dtype_code(w_scale), N, d, mode, _cb(cb_a), _cb(cb_w), _ptr(y),
-                                    _dtype_code(y), _stream(stream)))
+    lib = load_library()
+    if workspace is None:
+        _check(lib.rtq_qgemm(_ptr(a_codes), _ptr(a_scale), T, _ptr(w_codes), _ptr(w_scale), _dtype_code(w_scale), N,
+                             d, mode, _cb(cb_a), _cb(cb_w), _ptr(y), _dtype_code(y), _stream(stream)))
+    else:
+        _check(lib.rtq_qgemm_ws(_ptr(a_codes), _ptr(a_scale), T, _ptr(w_codes), _ptr(w_scale), _dtype_code(w_scale),
+                                N, d, mode, _cb(cb_a), _cb(cb_w), _ptr(y), _dtype_code(y), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream)))
     return y
+
+
+def qgemm_workspace() -> int:
+    """Bytes of workspace qgemm(..., workspace=...) uses on the current device."""
+    return int(load_library().rtq_qgemm_workspace())
 
 
 def rotated_qlinear_workspace(T: int, d: int, mode: int = RTQ_INT8, bits_a: int = 8) -> int:

@@ -36,6 +36,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "codebook_int8.h"
 #include "rtq_internal.h"
@@ -56,12 +57,13 @@ constexpr int kStages = 4;                      // LDS ring depth
 constexpr int kOpBytes = BM * BK;               // 16 KB: one operand's rows for one stage
 constexpr int kStageBytes = 2 * kOpBytes;       // A then W
 constexpr int kRingBytes = kStages * kStageBytes;
-constexpr int kLds = kRingBytes + (BM + BN) * static_cast<int>(sizeof(float));   // ring + scales
+constexpr int kLds = kRingBytes + (BM + BN) * static_cast<int>(sizeof(float)) + 16;   // ring + scales + flag
 constexpr int kWavesM = 2;
 constexpr int WM = BM / kWavesM;                // 128 rows per wave
 constexpr int kXcds = 8;
 constexpr int kBufferWord3 = 0x00020000;        // gfx9 buffer descriptor word 3 (raw, 32-bit dwords)
 constexpr int kStoreNT = 2;                     // buffer store cache policy: nontemporal (streaming)
+constexpr int kLoadL2 = 1;                      // buffer load cache policy: sc0, served from the L2 (not L1)
 constexpr int kDefaultWavesN = 4;               // the configuration the launcher uses
 
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
@@ -90,6 +92,8 @@ __device__ __forceinline__ void load_to_lds(v4i rsrc, uint32_t voff, uint32_t ld
 }
 
 #define RTQ_BARRIER() asm volatile("s_barrier" ::: "memory")
+// every vector memory access of this wave has completed (stores acknowledged by the L2)
+#define RTQ_WAIT_ALL_VMEM() asm volatile("s_waitcnt vmcnt(0)" ::: "memory")
 // orders a wave's own LDS accesses (executed in order per wave) against compiler reordering
 #define RTQ_LDS_FENCE() asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory")
 
@@ -143,6 +147,33 @@ __device__ __forceinline__ void decode2(const uint32_t (&lut)[4], const uint32_t
     }
 }
 
+// K-split of the last, partial round of tiles.  Tiles [0, dp_tiles) run whole, data-parallel;
+// each of the remaining tiles is split into `split` K ranges run by `split` blocks.  Every block of
+// a split tile stores its int32 partial tile and arrives on the tile's counter; the last to arrive
+// adds the others' partials and runs the epilogue (no block ever waits for another).  Counters hold
+// (epoch << 32) | arrivals; a counter from an earlier launch (other epoch) counts as zero, so the
+// workspace needs no clearing.
+struct SplitArgs {
+    int dp_tiles;
+    int split;                      // 1: no split
+    v4i* partials;                  // [units][BM * BN / 4] int32 quads
+    unsigned long long* counters;   // [tail tiles]
+    unsigned int epoch;
+};
+
+// Arrive on a split tile's counter; returns how many blocks of this launch arrived before.
+__device__ unsigned int split_arrive(unsigned long long* c, unsigned int epoch) {
+    unsigned long long cur = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = 0; i < (1 << 20); ++i) {   // lock-free: each failed exchange means another block's succeeded
+        const bool same = static_cast<unsigned int>(cur >> 32) == epoch;
+        const unsigned long long next = same ? cur + 1ull : ((static_cast<unsigned long long>(epoch) << 32) | 1ull);
+        const unsigned long long seen = atomicCAS(c, cur, next);
+        if (seen == cur) return same ? static_cast<unsigned int>(cur) : 0u;
+        cur = seen;
+    }
+    return 0xffffffffu;
+}
+
 // Tile index within the XCD-ordered sequence -> (tile_m, tile_n), in bands of 8 N-tiles.
 __device__ __forceinline__ void tile_of(int lin, int tiles_m, int tiles_n, int* tm, int* tn) {
     constexpr int kBand = 8;
@@ -164,7 +195,7 @@ __global__ void __launch_bounds__(64 * kWavesM * kWavesN, 1)
 gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, const int8_t* __restrict__ W,
                const void* __restrict__ w_scale, int64_t T, int64_t N, int d, void* __restrict__ Y,
                int tiles_m, int tiles_n, const float* __restrict__ cent_a, int a_bits,
-               const float* __restrict__ cent_w) {
+               const float* __restrict__ cent_w, SplitArgs sp) {
     constexpr int kWaves = kWavesM * kWavesN;
     // kWBits < 8: W holds packed codebook codes; they are loaded into a ring of raw LDS slots two
     // stages ahead and decoded to int8 codebook values into the stage ring one stage ahead.
@@ -186,18 +217,28 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
     const int wave = tid >> 6;
     const int wm = wave / kWavesN, wn = wave % kWavesN;
 
+    // Whole tiles [0, dp): split into 8 contiguous ranges, one per XCD (block b runs on XCD b % 8),
+    // taken round-robin by that XCD's blocks.  Split tiles [dp, total): unit u = xcd * stride + local
+    // is K range u % split of tile dp + u / split, so the units of one tile sit on one XCD.
     const int total = tiles_m * tiles_n;
     const int xcd = blockIdx.x % kXcds;
     const int stride = gridDim.x / kXcds;
-    const int per = (total + kXcds - 1) / kXcds;
-    const int lin_end = min((xcd + 1) * per, total);
-    int lin = xcd * per + static_cast<int>(blockIdx.x / kXcds);
-    if (lin >= lin_end) return;   // no tile for this block: before any barrier
+    const int local = static_cast<int>(blockIdx.x / kXcds);
+    const int dp = sp.dp_tiles;
+    const int per = (dp + kXcds - 1) / kXcds;
+    const int lin_end = min((xcd + 1) * per, dp);
+    const int unit = xcd * stride + local;
+    const bool has_unit = sp.split > 1 && unit < (total - dp) * sp.split;
+    int lin = xcd * per + local;
+    bool in_tail = lin >= lin_end;
+    if (in_tail && !has_unit) return;   // no work for this block: before any barrier
 
     const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
     float* s_as = reinterpret_cast<float*>(lds + kRingBytes);
     float* s_ws = s_as + BM;
-    const int nk = d / BK;
+    int* s_flag = reinterpret_cast<int*>(s_ws + BN);
+    const int nk_all = d / BK;
+    int kbeg = 0, nk = nk_all;   // the current work item's K stages
 
     // Load geometry: instruction q of wave w fills rows 16 * (q * kWaves + w) .. +16 of an operand
     // block; lane L takes row 16 * (q * kWaves + w) + L / 4 and LDS slot L % 4, which holds the
@@ -219,9 +260,18 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
 
     int64_t m0 = 0, n0 = 0;
     v4i rsa, rsw;
-    auto set_tile = [&](int l) {
+    auto set_item = [&](bool tail, int l) {
+        int tile = l;
+        kbeg = 0;
+        nk = nk_all;
+        if (tail) {
+            tile = dp + unit / sp.split;
+            const int sg = unit % sp.split;
+            kbeg = sg * nk_all / sp.split;
+            nk = (sg + 1) * nk_all / sp.split - kbeg;
+        }
         int tm, tn;
-        tile_of(l, tiles_m, tiles_n, &tm, &tn);
+        tile_of(tile, tiles_m, tiles_n, &tm, &tn);
         m0 = static_cast<int64_t>(tm) * BM;
         n0 = static_cast<int64_t>(tn) * BN;
         const int rows_a = static_cast<int>(min<int64_t>(BM, T - m0));
@@ -232,7 +282,7 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
     };
     auto issue_stage = [&](int st) {
         const uint32_t sb = lds_base + static_cast<uint32_t>((st & (kStages - 1)) * kStageBytes) + wave_lds;
-        const uint32_t k0 = static_cast<uint32_t>(st * BK);
+        const uint32_t k0 = static_cast<uint32_t>((kbeg + st) * BK);
 #pragma unroll
         for (int q = 0; q < kLoadsPerOp; ++q) {
             load_to_lds(rsa, load_off[q] + k0, sb + q * kWaves * 1024);
@@ -247,13 +297,13 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
         const uint32_t slot = raw_base + static_cast<uint32_t>((st % kRawSlots) * kRawStage);
         const int wrow = d * kWBits / 8;
         if constexpr (kWBits == 4) {
-            const uint32_t off = static_cast<uint32_t>((tid >> 1) * wrow + st * 32 + (tid & 1) * 16);
+            const uint32_t off = static_cast<uint32_t>((tid >> 1) * wrow + (kbeg + st) * 32 + (tid & 1) * 16);
             load_to_lds(rsw, off, slot + wave_lds);
         } else if constexpr (kWBits == 2) {
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 const int b = q * 2048 + 4 * tid;                 // byte within the slot
-                const uint32_t off = static_cast<uint32_t>((b >> 4) * wrow + st * 16 + (b & 15));
+                const uint32_t off = static_cast<uint32_t>((b >> 4) * wrow + (kbeg + st) * 16 + (b & 15));
                 load_to_lds4(rsw, off, slot + q * 2048 + static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave * 256)));
             }
         }
@@ -341,7 +391,7 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
         if (nk > 1) issue_stage(1);
         if (kCoded && nk > 2) issue_codes(2);
     };
-    set_tile(lin);
+    set_item(in_tail, lin);
     prefetch_early();
     load_scales();
 
@@ -414,13 +464,64 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
         RTQ_BARRIER();   // every wave is done reading the ring
 
         const int64_t cm0 = m0, cn0 = n0;
-        const int next = lin + stride;
-        const bool more = next < lin_end;
+        const bool ctail = in_tail;
+        bool more = false;
+        if (!in_tail) {
+            if (lin + stride < lin_end) {
+                lin += stride;
+                more = true;
+            } else if (has_unit) {
+                in_tail = true;
+                more = true;
+            }
+        }
         if (more) {
-            set_tile(next);
+            set_item(in_tail, lin);
             prefetch_early();
             load_scales();
         }
+
+        // ---- split tile: publish this K range's partial (row-major int32 256 x 256); the last
+        // block of the tile to arrive runs the epilogue and adds the other partials there
+        bool epilogue = true;
+        int others = 0;                 // first unit of my tile, when summing partials
+        if (ctail) {
+            v4i* mine = sp.partials + static_cast<size_t>(unit) * (BM * BN / 4);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int row = wm * WM + i * 32 + fr, col = wn * WN + j * 32 + 8 * g + 4 * fh;
+                        mine[(row * BN + col) >> 2] =
+                            v4i{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                    }
+            // All blocks of a split tile run on one XCD (the launcher makes the split divide the
+            // blocks per XCD), so its L2 is the point of coherence: the stores have reached it once
+            // they are acknowledged, the counter's atomic executes there, and the last block reads
+            // the partials with loads that bypass its own L1.
+            RTQ_WAIT_ALL_VMEM();
+            __syncthreads();
+            if (tid == 0)
+                s_flag[0] = split_arrive(sp.counters + (unit / sp.split), sp.epoch) ==
+                            static_cast<unsigned int>(sp.split - 1);
+            __syncthreads();
+            epilogue = s_flag[0] != 0;
+            others = unit - unit % sp.split;
+        }
+        // int32 quad (4 consecutive columns) at (row, col) of the tile: mine plus the other K ranges'
+        const __amdgpu_buffer_rsrc_t rsp = __builtin_amdgcn_make_buffer_rsrc(
+            sp.partials + static_cast<size_t>(others) * (BM * BN / 4), (short)0, sp.split * BM * BN * 4, kBufferWord3);
+        auto add_others = [&](v4i v, int row, int col) -> v4i {
+            if (ctail) {
+                for (int o = 0; o < sp.split; ++o) {
+                    if (others + o == unit) continue;
+                    v += __builtin_amdgcn_raw_buffer_load_b128(rsp, (o * BM * BN + row * BN + col) * 4, 0, kLoadL2);
+                }
+            }
+            return v;
+        };
 
         // ---- epilogue.  The MFMA computed the transposed tile (W fragment first), so a lane holds
         // D[n][t] at n = 8*(r/4) + 4*(lane/32) + r%4, t = lane % 32: four consecutive output columns
@@ -431,7 +532,7 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
         // streaming stores are full cache lines.  Stores go through a descriptor that ends at the
         // tile's last valid row; columns past N are sent past its range.  kVec (N % 8 == 0): an
         // output chunk of 16 bytes is wholly inside or outside [0, N).
-        {
+        if (epilogue) {
             constexpr int kOutBytes = kYKind == 1 ? 2 : 4;
             constexpr int kPassRows = 16;
             constexpr int kPitch = WN * 4 + 16;                    // raw int32 row + pad
@@ -469,13 +570,13 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
                         const int8_t* src = stg + r * kPitch + c * kPerChunk * 4;
                         v4i out;
                         if (kYKind == 2) {
-                            out = *reinterpret_cast<const v4i*>(src);
+                            out = add_others(*reinterpret_cast<const v4i*>(src), trow, col);
                         } else {
                             const float as = s_as[trow];
                             float y[kPerChunk];
 #pragma unroll
                             for (int h4 = 0; h4 < kPerChunk / 4; ++h4) {
-                                const v4i a = *reinterpret_cast<const v4i*>(src + 16 * h4);
+                                const v4i a = add_others(*reinterpret_cast<const v4i*>(src + 16 * h4), trow, col + 4 * h4);
                                 const float4 ws = *reinterpret_cast<const float4*>(s_ws + col + 4 * h4);
                                 y[4 * h4 + 0] = static_cast<float>(a.x) * as * ws.x;
                                 y[4 * h4 + 1] = static_cast<float>(a.y) * as * ws.y;
@@ -520,14 +621,13 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
         }
         RTQ_BARRIER();   // every wave is done with the staging slots and the scales
         if (!more) break;
-        lin = next;
     }
 }
 
 template <int kWavesN, int kWBits>
 hipError_t launch_config(const GemmI8Args& g, hipStream_t stream) {
     using KernelFn = void (*)(const int8_t*, const float*, const int8_t*, const void*, int64_t, int64_t, int,
-                              void*, int, int, const float*, int, const float*);
+                              void*, int, int, const float*, int, const float*, SplitArgs);
     constexpr int kYKinds = kWBits == 8 ? 3 : 2;   // raw int32 output only for int8 weights
     constexpr int kLdsBytes = lds_bytes(kWBits);
     // [w_scale bf16][N % 8 == 0][y kind]
@@ -562,15 +662,42 @@ hipError_t launch_config(const GemmI8Args& g, hipStream_t stream) {
     const int cus = device_cu_count();
     if (cus <= 0) return hipErrorInvalidDevice;
     const int64_t slots = std::max<int64_t>(kXcds, cus / kXcds * kXcds);
-    const int64_t grid = std::min<int64_t>(slots, (total + kXcds - 1) / kXcds * kXcds);
+    int64_t grid = std::min<int64_t>(slots, (total + kXcds - 1) / kXcds * kXcds);
+    SplitArgs sp{static_cast<int>(total), 1, nullptr, nullptr, 0u};
+    // With a workspace, the tiles of the last partial round are split along K over the idle slots:
+    // `rem` tiles, each in min(slots / rem, K stages) ranges.
+    if (g.workspace != nullptr && g.ws_bytes >= gemm_i8_workspace_bytes()) {
+        const int64_t whole = total / slots * slots;
+        const int64_t rem = total - whole;
+        int64_t split = rem > 0 ? std::min<int64_t>(std::min<int64_t>(slots / rem, g.d / BK), slots / kXcds) : 0;
+        // a power of two: the blocks per XCD are a multiple of it, so a tile's pieces share an XCD
+        while (split & (split - 1)) split &= split - 1;
+        if ((slots / kXcds) % std::max<int64_t>(split, 1) != 0) split = 1;
+        if (split >= 2) {
+            static std::atomic<unsigned int> epoch{0};
+            unsigned int e = ++epoch;
+            if (e == 0) e = ++epoch;
+            unsigned char* ws = static_cast<unsigned char*>(g.workspace);
+            sp = SplitArgs{static_cast<int>(whole), static_cast<int>(split), reinterpret_cast<v4i*>(ws),
+                           reinterpret_cast<unsigned long long*>(ws + static_cast<size_t>(slots) * BM * BN * 4), e};
+            grid = slots;
+        }
+    }
     const KernelFn k = kernels[g.w_scale_bf16 ? 1 : 0][(g.N % 8) == 0 ? 1 : 0][g.y_kind];
     hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(64 * kWavesM * kWavesN), kLdsBytes, stream, g.a,
                        g.a_scale, g.w, g.w_scale, g.T, g.N, g.d, g.y, static_cast<int>(tiles_m),
-                       static_cast<int>(tiles_n), g.cent_a, g.a_bits, g.cent_w);
+                       static_cast<int>(tiles_n), g.cent_a, g.a_bits, g.cent_w, sp);
     return hipGetLastError();
 }
 
 }  // namespace
+
+size_t gemm_i8_workspace_bytes() {
+    const int cus = device_cu_count();
+    const int64_t slots = std::max<int64_t>(kXcds, cus / kXcds * kXcds);
+    // partial tiles (int32) and counters, one each per slot
+    return static_cast<size_t>(slots) * (static_cast<size_t>(BM) * BN * 4 + sizeof(unsigned long long));
+}
 
 hipError_t launch_gemm_i8(const GemmI8Args& g, hipStream_t stream) {
     if (g.T <= 0 || g.N <= 0) return hipSuccess;

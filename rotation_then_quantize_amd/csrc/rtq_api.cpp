@@ -190,7 +190,9 @@ rtq_status plan_gemm(const void* a_codes, const float* a_scale, int64_t T, const
 
 size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
-size_t workspace_bytes(int64_t T, int32_t d, rtq_qmode mode, int32_t bits_a) {
+// Bytes of rtq_rotated_qlinear's workspace: codes and scales (required), then the product's
+// K-split region (used when present; see rtq_qgemm_ws).
+size_t workspace_bytes(int64_t T, int32_t d, rtq_qmode mode, int32_t bits_a, bool with_split = true) {
     if (T < 0 || d <= 0) return 0;
     size_t code_bytes;
     if (mode == RTQ_INT8 || (mode == RTQ_CODEBOOK_I8 && (bits_a == 2 || bits_a == 4)))
@@ -199,7 +201,8 @@ size_t workspace_bytes(int64_t T, int32_t d, rtq_qmode mode, int32_t bits_a) {
         code_bytes = static_cast<size_t>(T) * static_cast<size_t>(d) * static_cast<size_t>(bits_a) / 8;
     else
         return 0;
-    return align256(code_bytes) + align256(static_cast<size_t>(T) * sizeof(float));
+    return align256(code_bytes) + align256(static_cast<size_t>(T) * sizeof(float)) +
+           (with_split && mode != RTQ_CODEBOOK ? align256(rtq::gemm_i8_workspace_bytes()) : 0);
 }
 
 }  // namespace
@@ -271,6 +274,24 @@ rtq_status rtq_qgemm(const void* a_codes, const float* a_scale, int64_t T, const
     return hip_status(rtq::launch_gemm_i8(p.i8, s), "gemm_i8 launch");
 }
 
+rtq_status rtq_qgemm_ws(const void* a_codes, const float* a_scale, int64_t T, const void* w_codes,
+                        const void* w_scale, rtq_dtype w_scale_t, int64_t N, int32_t d, rtq_qmode mode,
+                        const rtq_codebook* cb_a, const rtq_codebook* cb_w, void* y, rtq_dtype yt,
+                        void* workspace, size_t ws_bytes, void* stream) {
+    GemmPlan p{};
+    RTQ_TRY(plan_gemm(a_codes, a_scale, T, w_codes, w_scale, w_scale_t, N, d, mode, cb_a, cb_w, y, yt, &p));
+    if (workspace != nullptr && reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+        return fail(RTQ_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+    if (T == 0) return ok();
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (p.lut) return hip_status(rtq::launch_gemm_lut(p.cb, s), "gemm_lut launch");
+    p.i8.workspace = workspace;
+    p.i8.ws_bytes = workspace != nullptr ? ws_bytes : 0;
+    return hip_status(rtq::launch_gemm_i8(p.i8, s), "gemm_i8 launch");
+}
+
+size_t rtq_qgemm_workspace(void) { return rtq::gemm_i8_workspace_bytes(); }
+
 size_t rtq_rotated_qlinear_workspace(int64_t T, int32_t d, rtq_qmode mode, int32_t bits_a) {
     return workspace_bytes(T, d, mode, bits_a);
 }
@@ -286,10 +307,11 @@ rtq_status rtq_rotated_qlinear(const void* x, rtq_dtype xt, int64_t T, const rtq
     const bool cbook = mode == RTQ_CODEBOOK || mode == RTQ_CODEBOOK_I8;
     if (cbook && cb_a == nullptr) return fail(RTQ_ERR_INVALID_ARG, "cb_a is NULL");
     const int32_t bits_a = cbook ? cb_a->bits : 8;
-    const size_t need = workspace_bytes(T < 0 ? 0 : T, d, mode, bits_a);
+    const size_t need = workspace_bytes(T < 0 ? 0 : T, d, mode, bits_a, false);
     if (mode == RTQ_CODEBOOK && bits_a != 4)
         return fail(RTQ_ERR_UNSUPPORTED, "activation codes must be 4-bit (got %d)", bits_a);
     if (need == 0 && T > 0) return fail(RTQ_ERR_INVALID_ARG, "unsupported mode or activation bits");
+    // (need covers the codes and scales; a larger workspace also carries the product's K-split)
     if (workspace == nullptr) return fail(RTQ_ERR_INVALID_ARG, "workspace is NULL");
     if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return fail(RTQ_ERR_MISALIGNED, "workspace is not 16-byte aligned");
     if (ws_bytes < need) return fail(RTQ_ERR_INVALID_ARG, "workspace too small: %zu < %zu bytes", ws_bytes, need);
@@ -307,6 +329,9 @@ rtq_status rtq_rotated_qlinear(const void* x, rtq_dtype xt, int64_t T, const rtq
     hipStream_t s = static_cast<hipStream_t>(stream);
     RTQ_TRY(hip_status(rtq::launch_rpbh_rows(qa, s), "rpbh_rows launch"));
     if (gp.lut) return hip_status(rtq::launch_gemm_lut(gp.cb, s), "gemm_lut launch");
+    const size_t split_off = align256(code_bytes) + align256(static_cast<size_t>(T) * sizeof(float));
+    gp.i8.workspace = ws + split_off;
+    gp.i8.ws_bytes = ws_bytes - split_off;
     return hip_status(rtq::launch_gemm_i8(gp.i8, s), "gemm_i8 launch");
 }
 

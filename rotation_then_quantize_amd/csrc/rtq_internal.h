@@ -66,9 +66,16 @@ struct GemmI8Args {
     const float* cent_a = nullptr;   // activation codebook centroids (device), 2^a_bits
     int a_bits = 0;
     const float* cent_w = nullptr;   // weight codebook centroids (device), 2^w_bits
+    // optional workspace (gemm_i8_workspace_bytes()): lets the last, partial round of tiles be
+    // split along K over the otherwise idle CUs
+    void* workspace = nullptr;
+    size_t ws_bytes = 0;
 };
 
 hipError_t launch_gemm_i8(const GemmI8Args& g, hipStream_t stream);
+// Workspace bytes for the K-split of launch_gemm_i8 on the current device (partial int32 tiles
+// for up to one per CU, plus one counter per CU).
+size_t gemm_i8_workspace_bytes();
 
 struct GemmLutArgs {
     const uint8_t* a;         // [T][d*bits_a/8] packed codes

@@ -143,7 +143,11 @@ def test_qgemm_and_qlinear_validation():
     assert call({2: 0}) == rtq.RTQ_OK                                    # T = 0 is a no-op
     # workspace sizing and checks of the fused call
     ws = lib.rtq_rotated_qlinear_workspace
-    assert ws(4608, 4096, rtq.RTQ_INT8, 8) == 4608 * 4096 + 4608 * 4 + (256 - (4608 * 4) % 256) % 256
+    split = lib.rtq_qgemm_workspace()
+    assert split % 16 == 0 and split >= 8 * (256 * 256 * 4 + 8)
+    split256 = (split + 255) // 256 * 256
+    assert ws(4608, 4096, rtq.RTQ_INT8, 8) == 4608 * 4096 + 4608 * 4 + (256 - (4608 * 4) % 256) % 256 + split256
+    assert ws(4608, 4096, rtq.RTQ_CODEBOOK_I8, 4) == 4608 * 4096 + 18432 + split256
     assert ws(4608, 4096, rtq.RTQ_CODEBOOK, 4) == 4608 * 2048 + 18432
     assert ws(10, 4096, rtq.RTQ_CODEBOOK, 3) == 0
     R = _R(256, 64, A, A)

@@ -142,7 +142,8 @@ def test_codebook_i8_layer_small(bits_w, T, N, d):
     rtq.quantize_rows(to_dev(wh, "bf16"), wcodes, wnorm, R, rtq.RTQ_CODEBOOK, cb_w, 0.0)
     y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
     need = rtq.rotated_qlinear_workspace(T, d, rtq.RTQ_CODEBOOK_I8, 4)
-    assert need == ((T * d + 255) // 256) * 256 + ((4 * T + 255) // 256) * 256
+    split = (rtq.qgemm_workspace() + 255) // 256 * 256      # the product's K-split region
+    assert need == ((T * d + 255) // 256) * 256 + ((4 * T + 255) // 256) * 256 + split
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     rtq.rotated_qlinear(to_dev(xh, "bf16"), R, wcodes, wnorm, y, rtq.RTQ_CODEBOOK_I8, cb_a, cb_w, workspace=ws)
     torch.cuda.synchronize()

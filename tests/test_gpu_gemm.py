@@ -115,3 +115,46 @@ def test_int8_full_shape_sampled():
     ref = oracle.gemm_int8(a[rows], w[cols])
     got = acc.cpu().numpy()[np.ix_(rows, cols)].astype(np.int64)
     assert np.array_equal(got, ref)
+
+
+# ---------------------------------------------------------------- K-split of the last round
+
+@pytest.mark.parametrize("T,N,d", [(130, 200, 256), (257, 129, 128), (64, 384, 4096), (33, 70, 16384),
+                                   (2000, 9000, 512)])
+def test_int8_ksplit_accumulators_bit_exact(T, N, d):
+    # with a workspace the tiles of the last partial round are split along d; the pieces add
+    # exactly in int32.  Few tiles split into many pieces (up to 256 at d = 16384); 2000 x 9000 is
+    # 288 tiles on 256 CUs: one whole round, then 32 tiles split 8 ways.
+    a = _codes(11 + T, T, d)
+    w = _codes(12 + N, N, d)
+    ws = torch.full((rtq.qgemm_workspace(),), 0x5A, dtype=torch.uint8, device="cuda")   # arbitrary contents
+    acc = torch.empty((T, N), dtype=torch.int32, device="cuda")
+    ones_t, ones_n = to_dev(np.ones(T, np.float32)), to_dev(np.ones(N, np.float32))
+    da, dw = to_dev(a), to_dev(w)
+    rows = np.arange(T) if T * N <= 1 << 17 else np.sort(np.random.default_rng(3).choice(T, 40, replace=False))
+    ref = oracle.gemm_int8(a[rows], w)
+    for _ in range(3):   # the same workspace again: per-launch counter tags
+        acc.fill_(0)
+        rtq.qgemm(da, ones_t, dw, ones_n, acc, d, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(acc.cpu().numpy()[rows].astype(np.int64), ref)
+
+
+@pytest.mark.parametrize("yt", ["f32", "bf16"])
+def test_ksplit_outputs_equal_unsplit(yt):
+    # exact int32 sums, then the same epilogue: split and unsplit products agree bit for bit
+    T, N, d = 300, 700, 2048
+    a = _codes(21, T, d)
+    w = _codes(22, N, d)
+    rng = np.random.default_rng(23)
+    a_s = to_dev((rng.random(T) * 0.1 + 0.01).astype(np.float32))
+    w_s = to_dev(oracle.to_bf16_bits(rng.random(N) * 0.1 + 0.01), "bf16")
+    dt = torch.float32 if yt == "f32" else torch.bfloat16
+    y0 = torch.empty((T, N), dtype=dt, device="cuda")
+    y1 = torch.empty((T, N), dtype=dt, device="cuda")
+    rtq.qgemm(to_dev(a), a_s, to_dev(w), w_s, y0, d)
+    ws = torch.empty(rtq.qgemm_workspace(), dtype=torch.uint8, device="cuda")
+    rtq.qgemm(to_dev(a), a_s, to_dev(w), w_s, y1, d, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y0.view(torch.int16) if yt == "bf16" else y0.view(torch.int32),
+                       y1.view(torch.int16) if yt == "bf16" else y1.view(torch.int32))
