@@ -153,6 +153,8 @@ __device__ __forceinline__ void decode2(const uint32_t (&lut)[4], const uint32_t
 // adds the others' partials and runs the epilogue (no block ever waits for another).  Counters hold
 // (epoch << 32) | arrivals; a counter from an earlier launch (other epoch) counts as zero, so the
 // workspace needs no clearing.
+constexpr int kMaxSplit = 8;
+
 struct SplitArgs {
     int dp_tiles;
     int split;                      // 1: no split
@@ -513,12 +515,19 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
         // int32 quad (4 consecutive columns) at (row, col) of the tile: mine plus the other K ranges'
         const __amdgpu_buffer_rsrc_t rsp = __builtin_amdgcn_make_buffer_rsrc(
             sp.partials + static_cast<size_t>(others) * (BM * BN / 4), (short)0, sp.split * BM * BN * 4, kBufferWord3);
+        // All kMaxSplit loads are issued back to back (the unit's own range and ranges past `split`
+        // are addressed past the descriptor and read as zero), so their latencies overlap.
         auto add_others = [&](v4i v, int row, int col) -> v4i {
             if (ctail) {
-                for (int o = 0; o < sp.split; ++o) {
-                    if (others + o == unit) continue;
-                    v += __builtin_amdgcn_raw_buffer_load_b128(rsp, (o * BM * BN + row * BN + col) * 4, 0, kLoadL2);
+                v4i part[kMaxSplit];
+#pragma unroll
+                for (int o = 0; o < kMaxSplit; ++o) {
+                    const uint32_t off = others + o == unit ? 0x80000000u
+                                                            : static_cast<uint32_t>((o * BM * BN + row * BN + col) * 4);
+                    part[o] = __builtin_amdgcn_raw_buffer_load_b128(rsp, static_cast<int>(off), 0, kLoadL2);
                 }
+#pragma unroll
+                for (int o = 0; o < kMaxSplit; ++o) v += part[o];
             }
             return v;
         };
@@ -664,12 +673,18 @@ hipError_t launch_config(const GemmI8Args& g, hipStream_t stream) {
     const int64_t slots = std::max<int64_t>(kXcds, cus / kXcds * kXcds);
     int64_t grid = std::min<int64_t>(slots, (total + kXcds - 1) / kXcds * kXcds);
     SplitArgs sp{static_cast<int>(total), 1, nullptr, nullptr, 0u};
-    // With a workspace, the tiles of the last partial round are split along K over the idle slots:
-    // `rem` tiles, each in min(slots / rem, K stages) ranges.
+    // With a workspace, the tiles of a last round that would leave at least 3/4 of the slots idle
+    // are split along K over them: `rem` tiles, each in min(slots / rem, K stages / 16, kMaxSplit)
+    // ranges.  (Measured: a range shorter than 16 stages, or a last round that already fills half
+    // the slots, loses more to the partial tiles' traffic and the lower clock of a full chip than
+    // the split gains.)
     if (g.workspace != nullptr && g.ws_bytes >= gemm_i8_workspace_bytes()) {
         const int64_t whole = total / slots * slots;
         const int64_t rem = total - whole;
-        int64_t split = rem > 0 ? std::min<int64_t>(std::min<int64_t>(slots / rem, g.d / BK), slots / kXcds) : 0;
+        int64_t split = rem > 0 && 4 * rem <= slots
+                            ? std::min<int64_t>(std::min<int64_t>(slots / rem, g.d / (16 * BK)),
+                                                std::min<int64_t>(slots / kXcds, kMaxSplit))
+                            : 0;
         // a power of two: the blocks per XCD are a multiple of it, so a tile's pieces share an XCD
         while (split & (split - 1)) split &= split - 1;
         if ((slots / kXcds) % std::max<int64_t>(split, 1) != 0) split = 1;

@@ -120,11 +120,12 @@ def test_int8_full_shape_sampled():
 # ---------------------------------------------------------------- K-split of the last round
 
 @pytest.mark.parametrize("T,N,d", [(130, 200, 256), (257, 129, 128), (64, 384, 4096), (33, 70, 16384),
-                                   (2000, 9000, 512)])
+                                   (300, 700, 2048), (4608, 4096, 8192)])
 def test_int8_ksplit_accumulators_bit_exact(T, N, d):
-    # with a workspace the tiles of the last partial round are split along d; the pieces add
-    # exactly in int32.  Few tiles split into many pieces (up to 256 at d = 16384); 2000 x 9000 is
-    # 288 tiles on 256 CUs: one whole round, then 32 tiles split 8 ways.
+    # with a workspace the tiles of a last round that leaves most compute units idle are split
+    # along d; the pieces add exactly in int32.  On 256 CUs: d < 2048 never splits; one tile at
+    # d = 4096 / 16384 splits 4 / 8 ways; 300 x 700 x 2048 is 6 tiles split 2 ways; 4608 x 4096 is
+    # 288 tiles: one whole round, then 32 tiles split 8 ways.
     a = _codes(11 + T, T, d)
     w = _codes(12 + N, N, d)
     ws = torch.full((rtq.qgemm_workspace(),), 0x5A, dtype=torch.uint8, device="cuda")   # arbitrary contents
