@@ -4,16 +4,18 @@
 // 2.3; INT8 s = max|x'|/127, q = rne(x'/s), cloud.baidu.com/article/9432521 4; Lloyd-Max codes of
 // x'/(||x'|| + eps), OrbitQuant article 2.1-2.2), organised for HBM throughput:
 //
-//  * Scatter on staging.  A 256-thread workgroup moves a group of 16384 bf16 elements (16384/d
-//    whole rows) per iteration.  Thread t always loads the same chunk columns of a row, so the
-//    permutation is applied as it writes: each of its 8 elements per 16-byte chunk goes straight
-//    to the LDS slot of the rotated block it feeds (inverse permutation, precomputed once per
-//    workgroup into 8 * max(1, d/2048) address registers; the row offset is an immediate).  The
-//    Rademacher sign of that slot is XOR-ed into the bf16 sign bit on the way.
+//  * Scatter on staging.  Each lane loads 16-byte chunks of bf16 inputs and writes each element
+//    straight to the LDS slot of the rotated block it feeds (the inverse permutation, as LDS
+//    offsets), XOR-ing the Rademacher sign of that slot into the bf16 sign bit on the way.
+//  * d <= 4096 (rpbh_wave_bf16_kernel): a row never spans waves, so every wave works alone on
+//    units of 4096 consecutive elements (4096/d rows, 64 blocks, one per lane) in its own LDS
+//    buffer, with the offset and sign tables shared by the workgroup; no barrier after the
+//    prologue.  d > 4096 (rpbh_quant_bf16_kernel): a 256-thread workgroup moves groups of 16384
+//    elements, rows span waves, and the row reductions cross waves through LDS.
 //  * LDS blocks are 128 bytes of data + 16 bytes of padding, so lane l reads its own 64-element
 //    block contiguously (eight 16-byte reads) without bank conflicts.
-//  * Register prefetch: the next group's global loads are issued before the current group is
-//    transformed, so HBM traffic overlaps the butterflies and quantisation.
+//  * Register prefetch: the next unit's (group's) global loads are issued before the current one
+//    is transformed, so HBM traffic overlaps the butterflies and quantisation.
 //  * Division-free INT8: the correctly rounded quotient x'/s comes from the row's reciprocal and
 //    one fma correction step, then one add of 1.5*2^23 rounds it half-to-even into the low mantissa
 //    bits; branch-free, and bit-identical to rne(fl32(x'/s)).  Only rows whose max |x'| is below
@@ -97,8 +99,10 @@ __device__ __forceinline__ void fwht64(double (&v)[kH]) {
 }
 
 // My block from LDS (already permuted and signed), widened to fp64 and transformed: v = 8 * x'.
-__device__ __forceinline__ void load_block_fwht(const unsigned char* smem, int tid, double (&acc)[kH]) {
-    const uint4* bp = reinterpret_cast<const uint4*>(smem + tid * kBlockPitch);
+// A lane's 64-element block from LDS (already permuted and signed), widened to fp64 and
+// transformed: v = 8 * x'.
+__device__ __forceinline__ void load_block_fwht(const unsigned char* block, double (&acc)[kH]) {
+    const uint4* bp = reinterpret_cast<const uint4*>(block);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
         const uint4 v = bp[q];
@@ -111,7 +115,6 @@ __device__ __forceinline__ void load_block_fwht(const unsigned char* smem, int t
     }
     fwht64(acc);
 }
-
 // ---- reductions over the nb = 2^log2nb consecutive lanes that hold one row (DPP inside a
 //      16-lane row, lane reads across rows, LDS across waves).  Every thread of the workgroup
 //      must call these together (the cross-wave step has a barrier); the result reaches every
@@ -187,6 +190,222 @@ __device__ __forceinline__ double row_sum(double v, int log2nb, double* red) {
     return v;
 }
 
+// Per-lane codebook state for one launch: the lane's boundary slot, and (4-bit) the lane's cell of
+// the boundary grid; the int8 value table for kRowLut*.
+template <int kOut>
+struct CodeCtx {
+    static constexpr bool k4 = kOut == kRowCode4 || kOut == kRowLut4;
+    static constexpr bool k2 = kOut == kRowCode2 || kOut == kRowLut2;
+    static constexpr bool kLut = kOut == kRowLut4 || kOut == kRowLut2;
+    static constexpr int kBits = k4 ? 4 : (k2 ? 2 : 8);
+    static constexpr int kNB = (1 << kBits) - 1;
+    int lane_base = 0;
+    int kidx = 0;                 // my threshold slot
+    float my_t = __builtin_inff();
+    float tb[3] = {0.0f, 0.0f, 0.0f};
+    uint32_t cell = 0;
+    float grid_k = 0.0f;
+    bool use_grid = false;        // per lane here: the caller makes it uniform over the workgroup
+    uint32_t lut[4] = {0u, 0u, 0u, 0u};
+
+    __device__ __forceinline__ void setup(const float* __restrict__ bounds, const float* __restrict__ cent,
+                                          int log2nb, int lane) {
+        const int row_lanes = (1 << log2nb) < 64 ? (1 << log2nb) : 64;   // lanes of my row in my wave
+        lane_base = lane & ~(row_lanes - 1);
+        kidx = lane - lane_base;
+        if (kLut) codebook_int8_table(cent, 1 << kBits, codebook_int8_scale(cent, 1 << kBits), lut);
+        if (k2) {
+#pragma unroll
+            for (int k = 0; k < 3; ++k) tb[k] = bounds[k];
+        }
+        if (k4) {
+            if (kidx < kNB) my_t = bounds[kidx];
+            // grid over [-tmax, tmax] with 40 cells of width tmax/20; 64 cells in all (end cells clamp)
+            const float tmax = fmaxf(fabsf(bounds[0]), fabsf(bounds[kNB - 1]));
+            use_grid = row_lanes >= 16 && tmax > 0.0f;
+            if (use_grid) {
+                grid_k = 20.0f / tmax;                 // cell units per unit of u
+                const int j = lane;                    // cell index, 0..63
+                const float slack = 1.0f / 1024.0f;    // in cell units: covers every rounding error
+                const float lo = (j == 0) ? -__builtin_inff() : (static_cast<float>(j - 32) - slack) / grid_k;
+                const float hi = (j == 63) ? __builtin_inff() : (static_cast<float>(j - 31) + slack) / grid_k;
+                int below = 0, inside = 0, kin = kNB;  // slot kNB holds +inf: "no boundary in this cell"
+                for (int k = 0; k < kNB; ++k) {
+                    const float t = bounds[k];
+                    if (t < lo) ++below;
+                    else if (t < hi) { ++inside; kin = k; }
+                }
+                if (inside > 1) use_grid = false;
+                cell = (static_cast<uint32_t>(below) << 8) | (4u * static_cast<uint32_t>(kin));
+            }
+        }
+    }
+};
+
+// A lane's quantised block: its code words (INT8 and int8 codebook values: 16 words of 4 bytes;
+// packed 4-bit codes: 8 words; 2-bit: 4) and its row's scale or norm.
+struct BlockOut {
+    uint32_t w[kH / 4];
+    float s;
+};
+
+// Bytes per output element (8 codes per 64 bits for 4-bit codes etc., in bits).
+template <int kOut>
+constexpr int out_bits() {
+    return kOut == kRowCode4 ? 4 : (kOut == kRowCode2 ? 2 : 8);
+}
+
+// Quantise a lane's rotated block (acc = 8 x' in fp64: the lane's 64 outputs of its row) with the
+// row's scale or norm, reduced over the row's lanes.  Every lane of the workgroup calls this
+// together when rows span several waves (log2nb > 6).
+template <int kOut>
+__device__ __forceinline__ void quantize_block(double (&acc)[kH], const unsigned char* block, int log2nb,
+                                               double* red, const CodeCtx<kOut>& cc,
+                                               const float* __restrict__ bounds, float eps, int scale_bf16,
+                                               BlockOut& res) {
+    constexpr bool k4 = CodeCtx<kOut>::k4;
+    constexpr bool k2 = CodeCtx<kOut>::k2;
+    constexpr bool kLut = CodeCtx<kOut>::kLut;
+    constexpr int kBits = CodeCtx<kOut>::kBits;
+    constexpr int kNB = CodeCtx<kOut>::kNB;
+    uint32_t* w = res.w;
+    if (kOut == kRowInt8) {
+        // amax = max |x'| = fl32(max |8x'| / 8) exactly (rounding is monotone), reduced over the row;
+        // the block maximum as a tree (no serial chain of 64 dependent maxima)
+        double m4[kH / 4];
+#pragma unroll
+        for (int k = 0; k < kH / 4; ++k)
+            m4[k] = fmax(fmax(fabs(acc[4 * k]), fabs(acc[4 * k + 1])), fmax(fabs(acc[4 * k + 2]), fabs(acc[4 * k + 3])));
+#pragma unroll
+        for (int k = 0; k < kH / 16; ++k)
+            m4[k] = fmax(fmax(m4[4 * k], m4[4 * k + 1]), fmax(m4[4 * k + 2], m4[4 * k + 3]));
+        const double m = fmax(fmax(m4[0], m4[1]), fmax(m4[2], m4[3]));
+        const float amax = row_max(static_cast<float>(m * 0.125), log2nb, reinterpret_cast<float*>(red));
+        float s = amax / 127.0f;
+        if (scale_bf16) s = bf16_to_f32(f32_to_bf16(s));
+        // q = rne(fl32(x'/s)) with x'/s = y/(8s), y = fl32(8x'), and no division per element:
+        // r = RN(1/(8s)), q0 = RN(y*r), e = y - q0*(8s) (exact by fma), q1 = RN(q0 + e*r) is
+        // the correctly rounded quotient (Markstein's correction step), and adding 1.5*2^23
+        // rounds q1 half-to-even into the low mantissa bits, whose low byte is the code.
+        const float s8 = s * 8.0f;
+        const float r8 = 1.0f / s8;
+        constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+#pragma unroll
+        for (int q = 0; q < kH / 4; ++q) {
+            float t[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const float y = static_cast<float>(acc[4 * q + p]);
+                const float q0 = y * r8;
+                const float q1 = fmaf(fmaf(-q0, s8, y), r8, q0);
+                t[p] = q1 + kMagic;
+            }
+            const uint32_t lo = __builtin_amdgcn_perm(__float_as_uint(t[1]), __float_as_uint(t[0]), 0x0c0c0400u);
+            const uint32_t hi = __builtin_amdgcn_perm(__float_as_uint(t[3]), __float_as_uint(t[2]), 0x04000c0cu);
+            w[q] = lo | hi;
+        }
+        // fl32(8x')/(8s) equals x'/s while x' is normal; with amax >= 2^-103 a subnormal x' gives
+        // code 0 either way.  Tinier rows (and all-zero rows) take the exact path.
+        const bool fast = amax >= 0x1p-103f;
+        if (!fast) {
+            // exact: q = rne(fl32(x'/s)), x' = fl32(8x' / 8); transform again from LDS (still intact)
+#pragma unroll
+            for (int q = 0; q < kH / 4; ++q) w[q] = 0u;
+            if (s != 0.0f) {
+                double a2[kH];
+                load_block_fwht(block, a2);
+                for (int b = 0; b < kH; ++b) {
+                    const float xr = static_cast<float>(a2[b] * 0.125);
+                    float r = rintf(xr / s);
+                    r = fminf(fmaxf(r, -127.0f), 127.0f);
+                    w[b >> 2] |= (static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xffu) << ((b & 3) * 8);
+                }
+            }
+        }
+        res.s = s;
+    } else {
+        // x' = fl32(8x' / 8), exactly the oracle's rotated value for every input
+        float xr[kH];
+        double ss4[4] = {0.0, 0.0, 0.0, 0.0};   // four interleaved partial sums: short dependency chains
+#pragma unroll
+        for (int b = 0; b < kH; ++b) {
+            xr[b] = static_cast<float>(acc[b] * 0.125);
+            const double f = static_cast<double>(xr[b]);
+            ss4[b & 3] = fma(f, f, ss4[b & 3]);
+        }
+        double ss = row_sum((ss4[0] + ss4[1]) + (ss4[2] + ss4[3]), log2nb, red);
+        const float s = static_cast<float>(sqrt(ss));
+        const float den = (eps == 0.0f) ? s : s + eps;
+        // codes per 32-bit word: packed, or one per byte before the int8 table lookup
+        constexpr int kSlot = kLut ? 8 : kBits;
+        constexpr int kPerWord = 32 / kSlot;
+#pragma unroll
+        for (int q = 0; q < kH / kPerWord; ++q) w[q] = 0u;
+        if (den != 0.0f) {
+            // u = fl32(x'/den); code = #{k : t_k < u} = #{k : x' >= Y_k}, Y_k exact per row
+            if (k2) {
+                float Y[3];
+#pragma unroll
+                for (int k = 0; k < 3; ++k) Y[k] = exact_threshold(cc.tb[k], den);
+#pragma unroll
+                for (int b = 0; b < kH; ++b) {
+                    const uint32_t code = (xr[b] >= Y[0] ? 1u : 0u) + (xr[b] >= Y[1] ? 1u : 0u) + (xr[b] >= Y[2] ? 1u : 0u);
+                    w[b / kPerWord] |= code << ((b % kPerWord) * kSlot);
+                }
+            } else if (cc.use_grid) {
+                // my slot holds Y_kidx (slot 15: +inf); cells hold (#below << 8) | 4*slot
+                const float myY = cc.kidx < kNB ? exact_threshold(cc.my_t, den) : __builtin_inff();
+                const float ka = 4.0f * cc.grid_k / den;      // 4 * cc.cell units per unit of x'
+                const int base4 = 4 * cc.lane_base;
+#pragma unroll
+                for (int b = 0; b < kH; ++b) {
+                    const int a = static_cast<int>(__builtin_amdgcn_fmed3f(fmaf(xr[b], ka, 128.0f), 0.0f, 255.0f));
+                    const uint32_t e = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(a, static_cast<int>(cc.cell)));
+                    const float Yk = __int_as_float(__builtin_amdgcn_ds_bpermute(static_cast<int>(e) + base4, __float_as_int(myY)));
+                    const uint32_t code = (e >> 8) + (xr[b] >= Yk ? 1u : 0u);
+                    w[b / kPerWord] |= code << ((b % kPerWord) * kSlot);
+                }
+            } else {
+                // a general codebook, or too few lanes per row for the slot table: divide and count
+#pragma unroll
+                for (int b = 0; b < kH; ++b) {
+                    const float u = xr[b] / den;
+                    uint32_t code = 0;
+                    for (int k = 0; k < kNB; ++k) code += (bounds[k] < u) ? 1u : 0u;
+                    w[b / kPerWord] |= code << ((b % kPerWord) * kSlot);
+                }
+            }
+        } else {
+            // zero row with eps = 0: u = 0 for every element
+            uint32_t code = 0;
+            for (int k = 0; k < kNB; ++k) code += (bounds[k] < 0.0f) ? 1u : 0u;
+#pragma unroll
+            for (int b = 0; b < kH; ++b) w[b / kPerWord] |= code << ((b % kPerWord) * kSlot);
+        }
+        if (kLut) {
+#pragma unroll
+            for (int q = 0; q < kH / kPerWord; ++q) w[q] = k4 ? lut16_x4(cc.lut, w[q]) : lut4_x4(cc.lut, w[q]);
+        }
+        res.s = s;
+    }
+}
+
+// Store a lane's quantised block (block `blk` of row `row`) and, from the row's first block, its scale.
+template <int kOut>
+__device__ __forceinline__ void store_block(const BlockOut& res, void* __restrict__ out, void* __restrict__ scale_out,
+                                            int scale_bf16, int64_t row, int blk, int d) {
+    constexpr int kWords = kH * out_bits<kOut>() / 32;
+    uint4* o = reinterpret_cast<uint4*>(static_cast<uint8_t*>(out) + (row * d + blk * kH) * out_bits<kOut>() / 8);
+#pragma unroll
+    for (int q = 0; q < kWords / 4; ++q) o[q] = make_uint4(res.w[4 * q], res.w[4 * q + 1], res.w[4 * q + 2], res.w[4 * q + 3]);
+    if (blk == 0) {
+        if (scale_bf16)
+            static_cast<uint16_t*>(scale_out)[row] = static_cast<uint16_t>(f32_to_bf16(res.s));
+        else
+            static_cast<float*>(scale_out)[row] = res.s;
+    }
+}
+
 // kNC: distinct 16-byte chunk columns a thread stages per group = max(1, d / 2048).
 template <int kNC, int kOut>
 __global__ void __launch_bounds__(kThreads, 2)
@@ -194,10 +413,6 @@ rpbh_quant_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int 
                        const int32_t* __restrict__ perm, const int8_t* __restrict__ signs, void* __restrict__ out,
                        void* __restrict__ scale_out, int scale_bf16, const float* __restrict__ bounds, float eps,
                        const float* __restrict__ cent) {
-    // codebook outputs: kRowCode* pack the codes, kRowLut* write each code's int8 codebook value
-    constexpr bool k4 = kOut == kRowCode4 || kOut == kRowLut4;
-    constexpr bool k2 = kOut == kRowCode2 || kOut == kRowLut2;
-    constexpr bool kLut = kOut == kRowLut4 || kOut == kRowLut2;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     // LDS: [row buffer(s) | prologue scratch overlaid][sign masks, d x u16 (kNC >= 4)][reduction]
     // d <= 4096: two row buffers, so staging group g+1 never waits for readers of group g
@@ -270,45 +485,10 @@ rpbh_quant_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int 
         }
     }
 
-    // ---- codebook set-up: this lane's boundary, and (4-bit) the lane's cell of the grid
-    constexpr int kBits = k4 ? 4 : (k2 ? 2 : 8);
-    constexpr int kNB = (1 << kBits) - 1;
-    const int row_lanes = (1 << log2nb) < 64 ? (1 << log2nb) : 64;   // lanes of my row in my wave
-    const int lane_base = lane & ~(row_lanes - 1);
-    const int kidx = lane - lane_base;                                 // my threshold slot
-    float my_t = __builtin_inff();
-    float tb[kBits == 2 ? 3 : 1];
-    uint32_t cell = 0;
-    float grid_k = 0.0f;
-    bool use_grid = false;
-    uint32_t lut[4] = {0u, 0u, 0u, 0u};
-    if (kLut) codebook_int8_table(cent, 1 << kBits, codebook_int8_scale(cent, 1 << kBits), lut);
-    if (k2) {
-#pragma unroll
-        for (int k = 0; k < 3; ++k) tb[k] = bounds[k];
-    }
-    if (k4) {
-        if (kidx < kNB) my_t = bounds[kidx];
-        // grid over [-tmax, tmax] with 40 cells of width tmax/20; 64 cells in all (end cells clamp)
-        const float tmax = fmaxf(fabsf(bounds[0]), fabsf(bounds[kNB - 1]));
-        use_grid = row_lanes >= 16 && tmax > 0.0f;
-        if (use_grid) {
-            grid_k = 20.0f / tmax;                 // cell units per unit of u
-            const int j = lane;                    // cell index, 0..63
-            const float slack = 1.0f / 1024.0f;    // in cell units: covers every rounding error
-            const float lo = (j == 0) ? -__builtin_inff() : (static_cast<float>(j - 32) - slack) / grid_k;
-            const float hi = (j == 63) ? __builtin_inff() : (static_cast<float>(j - 31) + slack) / grid_k;
-            int below = 0, inside = 0, kin = kNB;  // slot kNB holds +inf: "no boundary in this cell"
-            for (int k = 0; k < kNB; ++k) {
-                const float t = bounds[k];
-                if (t < lo) ++below;
-                else if (t < hi) { ++inside; kin = k; }
-            }
-            if (inside > 1) use_grid = false;
-            cell = (static_cast<uint32_t>(below) << 8) | (4u * static_cast<uint32_t>(kin));
-        }
-        use_grid = __syncthreads_and(use_grid ? 1 : 0) != 0;
-    }
+    // ---- codebook set-up
+    CodeCtx<kOut> cc;
+    cc.setup(bounds, cent, log2nb, lane);
+    if (CodeCtx<kOut>::k4) cc.use_grid = __syncthreads_and(cc.use_grid ? 1 : 0) != 0;
 
     // This workgroup's rows: an even share [r_begin, r_end) of all rows, taken rpg rows per group
     // (the last group of the share may be partial), so every workgroup does the same work.
@@ -368,149 +548,135 @@ rpbh_quant_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int 
         const bool wave_busy = log2nb > 6 || r0 + ((64 * (tid >> 6)) >> log2nb) < r_end;
         if (wave_busy) {
         double acc[kH];
-        load_block_fwht(buf, tid, acc);
+        load_block_fwht(buf + tid * kBlockPitch, acc);
 
         const int64_t row = r0 + rg;
         const bool valid = row < r_end;
 
-        if (kOut == kRowInt8) {
-            // amax = max |x'| = fl32(max |8x'| / 8) exactly (rounding is monotone), reduced over the row
-            double m = 0.0;
-#pragma unroll
-            for (int b = 0; b < kH; ++b) m = fmax(m, fabs(acc[b]));
-            const float amax = row_max(static_cast<float>(m * 0.125), log2nb, reinterpret_cast<float*>(red));
-            float s = amax / 127.0f;
-            if (scale_bf16) s = bf16_to_f32(f32_to_bf16(s));
-            // q = rne(fl32(x'/s)) with x'/s = y/(8s), y = fl32(8x'), and no division per element:
-            // r = RN(1/(8s)), q0 = RN(y*r), e = y - q0*(8s) (exact by fma), q1 = RN(q0 + e*r) is
-            // the correctly rounded quotient (Markstein's correction step), and adding 1.5*2^23
-            // rounds q1 half-to-even into the low mantissa bits, whose low byte is the code.
-            const float s8 = s * 8.0f;
-            const float r8 = 1.0f / s8;
-            constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
-            uint32_t w[kH / 4];
-#pragma unroll
-            for (int q = 0; q < kH / 4; ++q) {
-                float t[4];
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const float y = static_cast<float>(acc[4 * q + p]);
-                    const float q0 = y * r8;
-                    const float q1 = fmaf(fmaf(-q0, s8, y), r8, q0);
-                    t[p] = q1 + kMagic;
-                }
-                const uint32_t lo = __builtin_amdgcn_perm(__float_as_uint(t[1]), __float_as_uint(t[0]), 0x0c0c0400u);
-                const uint32_t hi = __builtin_amdgcn_perm(__float_as_uint(t[3]), __float_as_uint(t[2]), 0x04000c0cu);
-                w[q] = lo | hi;
-            }
-            // fl32(8x')/(8s) equals x'/s while x' is normal; with amax >= 2^-103 a subnormal x' gives
-            // code 0 either way.  Tinier rows (and all-zero rows) take the exact path.
-            const bool fast = amax >= 0x1p-103f;
-            if (!fast) {
-                // exact: q = rne(fl32(x'/s)), x' = fl32(8x' / 8); transform again from LDS (still intact)
-#pragma unroll
-                for (int q = 0; q < kH / 4; ++q) w[q] = 0u;
-                if (s != 0.0f) {
-                    double a2[kH];
-                    load_block_fwht(buf, tid, a2);
-                    for (int b = 0; b < kH; ++b) {
-                        const float xr = static_cast<float>(a2[b] * 0.125);
-                        float r = rintf(xr / s);
-                        r = fminf(fmaxf(r, -127.0f), 127.0f);
-                        w[b >> 2] |= (static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xffu) << ((b & 3) * 8);
-                    }
-                }
-            }
-            if (valid) {
-                uint4* o = reinterpret_cast<uint4*>(static_cast<int8_t*>(out) + row * d + blk * kH);
-#pragma unroll
-                for (int q = 0; q < kH / 16; ++q) o[q] = make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
-                if (blk == 0) {
-                    if (scale_bf16)
-                        static_cast<uint16_t*>(scale_out)[row] = static_cast<uint16_t>(f32_to_bf16(s));
-                    else
-                        static_cast<float*>(scale_out)[row] = s;
-                }
-            }
-        } else {
-            // x' = fl32(8x' / 8), exactly the oracle's rotated value for every input
-            float xr[kH];
-            double ss = 0.0;
-#pragma unroll
-            for (int b = 0; b < kH; ++b) {
-                xr[b] = static_cast<float>(acc[b] * 0.125);
-                const double f = static_cast<double>(xr[b]);
-                ss = fma(f, f, ss);
-            }
-            ss = row_sum(ss, log2nb, red);
-            const float s = static_cast<float>(sqrt(ss));
-            const float den = (eps == 0.0f) ? s : s + eps;
-            // codes per 32-bit word: packed, or one per byte before the int8 table lookup
-            constexpr int kSlot = kLut ? 8 : kBits;
-            constexpr int kPerWord = 32 / kSlot;
-            uint32_t w[kH / kPerWord];
-#pragma unroll
-            for (int q = 0; q < kH / kPerWord; ++q) w[q] = 0u;
-            if (den != 0.0f) {
-                // u = fl32(x'/den); code = #{k : t_k < u} = #{k : x' >= Y_k}, Y_k exact per row
-                if (k2) {
-                    float Y[3];
-#pragma unroll
-                    for (int k = 0; k < 3; ++k) Y[k] = exact_threshold(tb[k], den);
-#pragma unroll
-                    for (int b = 0; b < kH; ++b) {
-                        const uint32_t code = (xr[b] >= Y[0] ? 1u : 0u) + (xr[b] >= Y[1] ? 1u : 0u) + (xr[b] >= Y[2] ? 1u : 0u);
-                        w[b / kPerWord] |= code << ((b % kPerWord) * kSlot);
-                    }
-                } else if (use_grid) {
-                    // my slot holds Y_kidx (slot 15: +inf); cells hold (#below << 8) | 4*slot
-                    const float myY = kidx < kNB ? exact_threshold(my_t, den) : __builtin_inff();
-                    const float ka = 4.0f * grid_k / den;      // 4 * cell units per unit of x'
-                    const int base4 = 4 * lane_base;
-#pragma unroll
-                    for (int b = 0; b < kH; ++b) {
-                        const int a = static_cast<int>(__builtin_amdgcn_fmed3f(fmaf(xr[b], ka, 128.0f), 0.0f, 255.0f));
-                        const uint32_t e = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(a, static_cast<int>(cell)));
-                        const float Yk = __int_as_float(__builtin_amdgcn_ds_bpermute(static_cast<int>(e) + base4, __float_as_int(myY)));
-                        const uint32_t code = (e >> 8) + (xr[b] >= Yk ? 1u : 0u);
-                        w[b / kPerWord] |= code << ((b % kPerWord) * kSlot);
-                    }
-                } else {
-                    // a general codebook, or too few lanes per row for the slot table: divide and count
-#pragma unroll
-                    for (int b = 0; b < kH; ++b) {
-                        const float u = xr[b] / den;
-                        uint32_t code = 0;
-                        for (int k = 0; k < kNB; ++k) code += (bounds[k] < u) ? 1u : 0u;
-                        w[b / kPerWord] |= code << ((b % kPerWord) * kSlot);
-                    }
-                }
-            } else {
-                // zero row with eps = 0: u = 0 for every element
-                uint32_t code = 0;
-                for (int k = 0; k < kNB; ++k) code += (bounds[k] < 0.0f) ? 1u : 0u;
-#pragma unroll
-                for (int b = 0; b < kH; ++b) w[b / kPerWord] |= code << ((b % kPerWord) * kSlot);
-            }
-            if (kLut) {
-#pragma unroll
-                for (int q = 0; q < kH / kPerWord; ++q) w[q] = k4 ? lut16_x4(lut, w[q]) : lut4_x4(lut, w[q]);
-            }
-            if (valid) {
-                uint4* o = reinterpret_cast<uint4*>(static_cast<uint8_t*>(out) + (row * d + blk * kH) * kSlot / 8);
-#pragma unroll
-                for (int q = 0; q < kH / kPerWord / 4; ++q) o[q] = make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
-                if (blk == 0) {
-                    if (scale_bf16)
-                        static_cast<uint16_t*>(scale_out)[row] = static_cast<uint16_t>(f32_to_bf16(s));
-                    else
-                        static_cast<float*>(scale_out)[row] = s;
-                }
-            }
-        }
+        BlockOut res;
+        quantize_block<kOut>(acc, buf + tid * kBlockPitch, log2nb, red, cc, bounds, eps, scale_bf16, res);
+        if (valid) store_block<kOut>(res, out, scale_out, scale_bf16, row, blk, d);
         }
         if (kBufs == 1) __syncthreads();  // every lane has read its block before the buffer is restaged
     }
+}
+
+// ---- d <= 4096: one wave per unit of 4096 consecutive elements (4096 / d whole rows, 64
+//      blocks, one per lane).  A row never spans waves, so the waves of a workgroup share only the
+//      permutation tables and never synchronise after the prologue: each wave stages its unit into
+//      its own LDS buffer (LDS operations of one wave execute in order, so its reads see its
+//      writes), transforms, quantises and stores, while its next unit's loads are in flight.
+constexpr int kUnit = 4096;
+constexpr int kWaveBuf = 64 * kBlockPitch;
+constexpr int kWaveMaxD = 4096;
+
+template <int kOut>
+__global__ void __launch_bounds__(kThreads, 2)
+rpbh_wave_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int log2d,
+                      const int32_t* __restrict__ perm, const int8_t* __restrict__ signs, void* __restrict__ out,
+                      void* __restrict__ scale_out, int scale_bf16, const float* __restrict__ bounds, float eps,
+                      const float* __restrict__ cent) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    // LDS: [scatter offset of each source column, u32[d]][its sign mask, u16[d]][one buffer per wave]
+    uint32_t* tab_off = reinterpret_cast<uint32_t*>(smem);
+    uint16_t* tab_sgn = reinterpret_cast<uint16_t*>(smem + 4 * d);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    unsigned char* buf = smem + 6 * d + wave * kWaveBuf;
+    const int log2nb = log2d - 6;
+    const uint32_t dmask = static_cast<uint32_t>(d - 1);
+
+    // Destination position j (block j / 64, slot j % 64) takes source column perm[j] with sign
+    // signs[j]: the table entry of that column holds j's LDS offset and sign bit.
+    for (int j = 4 * tid; j < d; j += 4 * kThreads) {
+        const int4 pv = *reinterpret_cast<const int4*>(perm + j);
+        const uint32_t sv = *reinterpret_cast<const uint32_t*>(signs + j);
+        const int pj[4] = {pv.x, pv.y, pv.z, pv.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t c = static_cast<uint32_t>(pj[e]) & dmask;
+            const uint32_t jj = static_cast<uint32_t>(j + e);
+            tab_off[c] = (jj >> 6) * kBlockPitch + (jj & 63u) * 2u;
+            tab_sgn[c] = (sv >> (8 * e + 7)) & 1u ? 0x8000u : 0u;
+        }
+    }
+    CodeCtx<kOut> cc;
+    cc.setup(bounds, cent, log2nb, lane);
+    if (CodeCtx<kOut>::k4) cc.use_grid = __syncthreads_and(cc.use_grid ? 1 : 0) != 0;
+    __syncthreads();   // tables complete
+
+    const int64_t total = rows * static_cast<int64_t>(d);
+    const int64_t units = (total + kUnit - 1) / kUnit;
+    const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
+    int64_t u = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + wave;
+
+    // chunk i of a unit, for this lane: 8 elements at unit offset 512 i + 8 lane
+    uint4 pre[8];
+    auto load_unit = [&](int64_t uu) {
+        const int64_t e0 = uu * kUnit + 8 * lane;
+        if (uu * kUnit + kUnit <= total) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) pre[i] = *reinterpret_cast<const uint4*>(x + e0 + 512 * i);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int64_t e = e0 + 512 * i;
+                pre[i] = e < total ? *reinterpret_cast<const uint4*>(x + e) : make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+    };
+    if (u < units) load_unit(u);
+    const uint32_t row_bytes = static_cast<uint32_t>((d >> 6) * kBlockPitch);
+    // A unit's codes are stored after the next unit is staged and its successor's loads issued, so
+    // waiting for those loads never waits for the stores as well.
+    BlockOut res;
+    int64_t res_row = -1;
+    const int blk = lane & ((1 << log2nb) - 1);
+    for (; u < units; u += nwaves) {
+        // ---- stage: signs, then scatter each element to its rotated block slot
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t pos = 512u * i + 8u * lane;
+            const uint32_t col = pos & dmask;
+            unsigned char* rb = buf + (pos >> log2d) * row_bytes;
+            const uint4 m = *reinterpret_cast<const uint4*>(tab_sgn + col);
+            const uint4 o0 = *reinterpret_cast<const uint4*>(tab_off + col);
+            const uint4 o1 = *reinterpret_cast<const uint4*>(tab_off + col + 4);
+            const uint32_t w[4] = {pre[i].x ^ m.x, pre[i].y ^ m.y, pre[i].z ^ m.z, pre[i].w ^ m.w};
+            const uint32_t off[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                *reinterpret_cast<uint16_t*>(rb + off[k]) =
+                    static_cast<uint16_t>((k & 1) ? (w[k >> 1] >> 16) : (w[k >> 1] & 0xffffu));
+        }
+        if (res_row >= 0 && res_row < rows) store_block<kOut>(res, out, scale_out, scale_bf16, res_row, blk, d);
+        if (u + nwaves < units) load_unit(u + nwaves);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the unit is staged (this wave's LDS writes)
+
+        double acc[kH];
+        load_block_fwht(buf + lane * kBlockPitch, acc);
+        quantize_block<kOut>(acc, buf + lane * kBlockPitch, log2nb, nullptr, cc, bounds, eps, scale_bf16, res);
+        res_row = u * (kUnit >> log2d) + (lane >> log2nb);
+        asm volatile("" ::: "memory");   // this unit's block reads precede the next unit's staging
+    }
+    if (res_row >= 0 && res_row < rows) store_block<kOut>(res, out, scale_out, scale_bf16, res_row, blk, d);
+}
+
+template <int kOut>
+hipError_t launch_wave(const RowArgs& a, int log2d, hipStream_t stream) {
+    auto kernel = rpbh_wave_bf16_kernel<kOut>;
+    const size_t lds = 6 * static_cast<size_t>(a.d) + static_cast<size_t>(kThreads / 64) * kWaveBuf;
+    int per_cu = 0;
+    const hipError_t e = kernel_blocks_per_cu(reinterpret_cast<const void*>(kernel), kThreads, lds, &per_cu);
+    if (e != hipSuccess) return e;
+    const int64_t cap = static_cast<int64_t>(per_cu) * device_cu_count();
+    const int64_t units = (a.rows * a.d + kUnit - 1) / kUnit;
+    const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(cap, (units + kThreads / 64 - 1) / (kThreads / 64)));
+    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), lds, stream,
+                       static_cast<const uint16_t*>(a.x), a.rows, a.d, log2d, a.perm, a.signs, a.out, a.scale,
+                       a.scale_bf16 ? 1 : 0, a.bounds, a.eps, a.centroids);
+    return hipGetLastError();
 }
 
 template <int kNC, int kOut>
@@ -537,9 +703,8 @@ hipError_t launch_t(const RowArgs& a, int log2d, hipStream_t stream) {
 
 template <int kOut>
 hipError_t launch_nc(const RowArgs& a, int log2d, hipStream_t stream) {
-    switch (a.d > 2048 ? a.d / 2048 : 1) {
-        case 1: return launch_t<1, kOut>(a, log2d, stream);
-        case 2: return launch_t<2, kOut>(a, log2d, stream);
+    if (a.d <= kWaveMaxD) return launch_wave<kOut>(a, log2d, stream);
+    switch (a.d / 2048) {
         case 4: return launch_t<4, kOut>(a, log2d, stream);
         case 8: return launch_t<8, kOut>(a, log2d, stream);
     }
