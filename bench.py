@@ -258,6 +258,86 @@ def bench_codebook(args, torch, rtq, workloads, variant, mode=None):
             "rpbh_frac_hbm": q_bytes / (quant_burst * 1e-3) / 1e9 / PEAK_HBM_GBPS}
 
 
+def bench_ablation(args, torch, rtq, workloads):
+    """The transform ablation at the W8A8 DiT shape (OrbitQuant article, sections 2.3 and 3.3): RPBH
+    against block Hadamard without the permutation (perm = identity, same signs) and against a dense
+    Haar rotation applied as a bf16 GEMM (the vendor library, hipBLASLt through torch.matmul).
+    Times: rotate-and-quantise launches and rotation alone, each a burst over rotating input
+    copies. Quality: relative Frobenius error of the W8A8 output against the exact fp64 product on
+    64 sampled tokens, with the workload's outlier channels spread as drawn and packed into the first
+    blocks (the same column order applied to x and W leaves W x unchanged)."""
+    d, N = workloads.DIT_HIDDEN, workloads.DIT_MLP
+    xh = workloads.dit_activations_bf16(d)
+    T = xh.shape[0]
+    seed = workloads.RPBH_SEED[d]
+    R = rtq.Rpbh.from_seed(seed, d)
+    BH = rtq.Rpbh.without_permutation(seed, d)
+    Q = torch.from_numpy(workloads.haar_orthogonal(seed, d)).cuda()
+    Qt16 = Q.t().contiguous().to(torch.bfloat16)
+    xs = _copies(_bf16_dev(xh, torch), 512 << 20, torch)
+    codes = torch.empty((T, d), dtype=torch.int8, device="cuda")
+    scale = torch.empty(T, dtype=torch.float32, device="cuda")
+    rot16 = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    n = max(20, args.steps)
+
+    def quant(desc):
+        return lambda i: rtq.quantize_rows(xs[i % len(xs)], codes, scale, desc, rtq.RTQ_INT8)
+
+    def dense_rotate(i):
+        torch.matmul(xs[i % len(xs)], Qt16, out=rot16)
+
+    def dense_rotate_quant(i):
+        dense_rotate(i)
+        rtq.quantize_rows(rot16, codes, scale, None, rtq.RTQ_INT8)
+
+    def rpbh_rotate(i):
+        rtq.rpbh_rotate(xs[i % len(xs)], rot16, R)
+
+    for f in (quant(R), quant(BH), dense_rotate_quant, rpbh_rotate):
+        _prewarm(f, torch, 0.1)
+    t = {"rpbh_quantize_ms": _burst_ms(n, quant(R), torch),
+         "block_hadamard_quantize_ms": _burst_ms(n, quant(BH), torch),
+         "dense_rotate_then_quantize_ms": _burst_ms(n, dense_rotate_quant, torch),
+         "rpbh_rotate_only_ms": _burst_ms(n, rpbh_rotate, torch),
+         "dense_rotate_only_ms": _burst_ms(n, dense_rotate, torch)}
+    t["dense_over_rpbh_rotate_only"] = t["dense_rotate_only_ms"] / t["rpbh_rotate_only_ms"]
+    t["dense_over_rpbh_rotate_quantize"] = t["dense_rotate_then_quantize_ms"] / t["rpbh_quantize_ms"]
+    t["block_hadamard_over_rpbh"] = t["block_hadamard_quantize_ms"] / t["rpbh_quantize_ms"]
+    del xs
+
+    # quality on 64 sampled tokens
+    rows = np.sort(np.random.default_rng(9).choice(T, 64, replace=False))
+    x32 = workloads.bf16_bits_to_f32(xh[rows])
+    w32 = workloads.bf16_bits_to_f32(workloads.dit_weight_bf16("mlp_up"))
+    quality = {}
+    for layout in ("spread", "clustered"):
+        order = (np.arange(d) if layout == "spread"
+                 else workloads.clustered_order(d, workloads.dit_activation_outlier_channels(d)))
+        xo = np.ascontiguousarray(x32[:, order])
+        wo = np.ascontiguousarray(w32[:, order])
+        ref = xo.astype(np.float64) @ wo.astype(np.float64).T
+        xd, wd = torch.from_numpy(xo).cuda(), torch.from_numpy(wo).cuda()
+        errs = {}
+        for name in ("none", "block_hadamard", "rpbh", "dense_haar"):
+            desc = {"none": None, "block_hadamard": BH, "rpbh": R, "dense_haar": None}[name]
+            xin, win = xd, wd
+            if name == "dense_haar":
+                xin, win = xd @ Q.t(), wd @ Q.t()     # rotated in fp32
+            wq = torch.empty((N, d), dtype=torch.int8, device="cuda")
+            wsc = torch.empty(N, dtype=torch.float32, device="cuda")
+            rtq.quantize_rows(win, wq, wsc, desc, rtq.RTQ_INT8)
+            aq = torch.empty((len(rows), d), dtype=torch.int8, device="cuda")
+            asc = torch.empty(len(rows), dtype=torch.float32, device="cuda")
+            rtq.quantize_rows(xin, aq, asc, desc, rtq.RTQ_INT8)
+            y = torch.empty((len(rows), N), dtype=torch.float32, device="cuda")
+            rtq.qgemm(aq, asc, wq, wsc, y, d)
+            torch.cuda.synchronize()
+            errs[name] = float(np.linalg.norm(y.cpu().numpy() - ref) / np.linalg.norm(ref))
+        quality[layout] = errs
+    return {"shape": f"{T}x{d} activations (rotation), {T}x{d}->{N} (quality, 64 tokens)", **t,
+            "w8a8_rel_error": quality}
+
+
 def cpu_baseline(workloads):
     """The oracle, as written, on a bounded token sample of the W8A8 step, scaled to the full step:
     per-token online cost (dense Pi rotation + INT8 quantise) and per-(token, channel) GEMM cost are
@@ -352,7 +432,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
-    ap.add_argument("--only", choices=["w8a8", "codebook", "all"], default="all",
+    ap.add_argument("--only", choices=["w8a8", "codebook", "ablation", "all"], default="all",
                     help="w8a8: time only the headline step (profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain streaming kernel of known size (bitwise_not over 256 MiB of int8, "
@@ -384,6 +464,9 @@ def main():
             torch.bitwise_not(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
+    if args.only == "ablation":
+        print(json.dumps(bench_ablation(args, torch, rtq, workloads)))
+        return
     if args.only == "codebook":   # the codebook layers only (profiling runs)
         out = {k: bench_codebook(args, torch, rtq, workloads, v) for k, v in
                [("w4a4_dit_attn_out_4608x4096x4096", "w4a4"), ("w2a4_dit_mlp_down_4608x16384x4096", "w2a4")]}
@@ -399,6 +482,7 @@ def main():
                                                                             rtq.RTQ_CODEBOOK)
         extra["w2a4_dit_mlp_down_4608x16384x4096_fp16_lut"] = bench_codebook(args, torch, rtq, workloads, "w2a4",
                                                                              rtq.RTQ_CODEBOOK)
+        extra["transform_ablation"] = bench_ablation(args, torch, rtq, workloads)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(workloads)

@@ -150,6 +150,14 @@ class Rpbh:
         torch = _torch()
         return cls(torch.from_numpy(perm).to(device), torch.from_numpy(signs).to(device))
 
+    @classmethod
+    def without_permutation(cls, seed: int, d: int, device="cuda"):
+        """Block Hadamard with the seeded signs and no permutation (perm = identity): the ablation
+        of the permutation step (OrbitQuant article, sections 2.3 and 3.3)."""
+        _, signs = rpbh_make(seed, d)
+        torch = _torch()
+        return cls(torch.arange(d, dtype=torch.int32, device=device), torch.from_numpy(signs).to(device))
+
     @property
     def c(self):
         return ctypes.byref(self._c)

@@ -427,3 +427,36 @@ def test_rotation_lowers_int8_error_on_outliers():
     e_rot = np.linalg.norm(rot - ref) / np.linalg.norm(ref)
     e_plain = np.linalg.norm(plain - ref) / np.linalg.norm(ref)
     assert e_rot < 0.5 * e_plain
+
+
+def test_transform_ablation_error_ordering():
+    # [OQ] 2.3 / 3.3: with outlier channels packed into one block, block Hadamard without P_pi
+    # leaves them concentrated, so its W8A8 error stays above RPBH's; RPBH is as good as a dense
+    # Haar rotation (the ">25x faster" transform buys nothing worse here), and any rotation beats
+    # none.
+    d = 1024
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((32, d)).astype(np.float32)
+    x[:, :8] *= 40
+    w = (rng.standard_normal((256, d)) * 0.02).astype(np.float32)
+    perm, signs = oracle.rpbh_descriptor(9, d)
+    transforms = {
+        "block_hadamard": oracle.rpbh_dense(d, 64, np.arange(d, dtype=np.int32), signs),
+        "rpbh": oracle.rpbh_dense(d, 64, perm, signs),
+        "haar": workloads.haar_orthogonal(9, d).astype(np.float64),
+    }
+    ref = oracle.matmul_f64(x, w)
+    qa, sa, _ = oracle.quantize_int8(x, False)
+    qw, sw, _ = oracle.quantize_int8(w, False)
+    err = {"none": np.linalg.norm(oracle.rescale_int8(oracle.gemm_int8(qa, qw), sa, sw) - ref)}
+    for name, pi in transforms.items():
+        err[name] = np.linalg.norm(oracle.qlinear_int8(x, pi, oracle.weights_int8(w, pi, False))["y"] - ref)
+    assert err["none"] > 2 * err["block_hadamard"]
+    assert err["block_hadamard"] > 1.3 * err["rpbh"]
+    assert err["rpbh"] < 1.25 * err["haar"]
+
+
+def test_haar_input_is_orthogonal():
+    # the dense comparison rotation is orthogonal (Q^T Q = I to fp32 rounding)
+    q = workloads.haar_orthogonal(5, 256).astype(np.float64)
+    assert np.abs(q.T @ q - np.eye(256)).max() < 1e-6

@@ -161,3 +161,32 @@ def small_case(seed: int, rows: int, d: int, dist: str = "t3", outlier_frac=0.01
     if dist == "normal":
         return gaussian_activations(seed, [seed, 7], rows, d, max(1, int(round(outlier_frac * d))), gain)
     raise ValueError(dist)
+
+
+# --------------------------------------------------------------------------
+# Inputs for the transform ablation (block Hadamard without the permutation, dense rotation).
+
+def dit_activation_outlier_channels(d: int) -> np.ndarray:
+    """The channels dit_activations_bf16(d) scales by x50 (sorted)."""
+    oseed = 3004 if d == DIT_HIDDEN else 5004
+    return _outlier_columns(oseed, d, 0.01)
+
+
+def clustered_order(d: int, first: np.ndarray) -> np.ndarray:
+    """A column order that puts the channels `first` at the front (so they fill the first
+    ceil(len/64) blocks of 64) and keeps the rest in place order.  Applying it to the columns of
+    both x and W leaves W x unchanged."""
+    first = np.asarray(first, np.int64)
+    rest = np.setdiff1d(np.arange(d, dtype=np.int64), first)
+    return np.concatenate([first, rest])
+
+
+@functools.lru_cache(maxsize=None)
+def haar_orthogonal(seed: int, d: int) -> np.ndarray:
+    """A Haar-distributed random orthogonal matrix [d][d] (fp32): the Q factor of a seeded
+    Gaussian matrix, with the signs fixed by R's diagonal so the distribution is uniform."""
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal((d, d))
+    q, r = np.linalg.qr(g)
+    q *= np.sign(np.diag(r))[None, :]
+    return q.astype(np.float32)
