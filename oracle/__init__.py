@@ -186,7 +186,7 @@ def pack(codes: np.ndarray, bits: int) -> np.ndarray:
     rows, d = codes.shape
     out = np.empty((rows, d * bits // 8), np.uint8)
     if _load().orc_pack(codes, rows, d, bits, out) != 0:
-        raise ValueError("bits must be 2, 4 or 8 and divide the row")
+        raise ValueError("bits must be 2, 3, 4, 6 or 8 with d * bits a multiple of 8")
     return out
 
 
@@ -195,7 +195,7 @@ def unpack(packed: np.ndarray, d: int, bits: int) -> np.ndarray:
     rows = packed.shape[0]
     out = np.empty((rows, d), np.uint8)
     if _load().orc_unpack(packed, rows, d, bits, out) != 0:
-        raise ValueError("bits must be 2, 4 or 8 and divide the row")
+        raise ValueError("bits must be 2, 3, 4, 6 or 8 with d * bits a multiple of 8")
     return out
 
 

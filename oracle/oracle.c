@@ -237,33 +237,44 @@ ORC_API void orc_quant_codebook_rows(const float *v, int64_t rows, int32_t d, in
     }
 }
 
-/* b-bit packing, least-significant bits first: element j of a row lands in
- * byte j*b/8 at bit offset (j mod 8/b)*b.  bits is 2 or 4 (8 is a copy). */
+/* b-bit packing, least-significant bits first: the codes of a row form one little-endian bit
+ * stream, element j in bits [j*b, j*b + b).  For b = 2 and 4 this is byte j*b/8 at bit offset
+ * (j mod 8/b)*b; for b = 3 and 6 a code may straddle two bytes (8 3-bit codes per 3 bytes, 4
+ * 6-bit codes per 3 bytes).  bits is 2, 3, 4, 6 or 8 (8 is a copy); d*b must be a multiple of 8. */
+static int pack_bits_ok(int32_t d, int32_t bits)
+{
+    if (bits != 2 && bits != 3 && bits != 4 && bits != 6 && bits != 8) return 0;
+    return ((int64_t)d * bits) % 8 == 0;
+}
+
 ORC_API int orc_pack(const uint8_t *codes, int64_t rows, int32_t d, int32_t bits, uint8_t *packed)
 {
-    if (bits != 2 && bits != 4 && bits != 8) return -1;
-    int per_byte = 8 / bits;
-    if (d % per_byte != 0) return -1;
+    if (!pack_bits_ok(d, bits)) return -1;
     int64_t row_bytes = (int64_t)d * bits / 8;
     memset(packed, 0, (size_t)(rows * row_bytes));
     for (int64_t r = 0; r < rows; ++r)
         for (int32_t j = 0; j < d; ++j) {
             unsigned c = codes[(size_t)r * d + j] & ((1u << bits) - 1u);
-            packed[(size_t)(r * row_bytes + j / per_byte)] |= (uint8_t)(c << ((j % per_byte) * bits));
+            for (int b = 0; b < bits; ++b) {
+                int64_t bit = (int64_t)j * bits + b;
+                if ((c >> b) & 1u) packed[(size_t)(r * row_bytes + bit / 8)] |= (uint8_t)(1u << (bit % 8));
+            }
         }
     return 0;
 }
 
 ORC_API int orc_unpack(const uint8_t *packed, int64_t rows, int32_t d, int32_t bits, uint8_t *codes)
 {
-    if (bits != 2 && bits != 4 && bits != 8) return -1;
-    int per_byte = 8 / bits;
-    if (d % per_byte != 0) return -1;
+    if (!pack_bits_ok(d, bits)) return -1;
     int64_t row_bytes = (int64_t)d * bits / 8;
     for (int64_t r = 0; r < rows; ++r)
         for (int32_t j = 0; j < d; ++j) {
-            unsigned byte = packed[(size_t)(r * row_bytes + j / per_byte)];
-            codes[(size_t)r * d + j] = (uint8_t)((byte >> ((j % per_byte) * bits)) & ((1u << bits) - 1u));
+            unsigned c = 0;
+            for (int b = 0; b < bits; ++b) {
+                int64_t bit = (int64_t)j * bits + b;
+                c |= (unsigned)((packed[(size_t)(r * row_bytes + bit / 8)] >> (bit % 8)) & 1u) << b;
+            }
+            codes[(size_t)r * d + j] = (uint8_t)c;
         }
     return 0;
 }

@@ -251,7 +251,7 @@ def test_int8_codes_by_brute_force_round_half_even():
 
 # ---------------------------------------------------------------- codebook
 
-@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 6])
 def test_lloyd_max_optimality_conditions(bits):
     # [OQ] 4.2: Lloyd-Max codebook for a Gaussian.  Centroids are the
     # conditional means of their cells, boundaries the midpoints
@@ -385,6 +385,31 @@ def test_pack_examples_and_roundtrip():
         assert np.array_equal(oracle.unpack(oracle.pack(allc, bits), allc.shape[1], bits), allc)
 
 
+def test_pack_bit_stream_for_three_and_six_bits():
+    # 3- and 6-bit codes (the W3A3 / W4A6 variants, OrbitQuant article 3.2-3.3) continue the
+    # LSB-first rule as one little-endian bit stream per row: element j in bits [j*b, j*b + b).
+    # Worked by hand: 3-bit codes 1..7,0 -> sum c_j 2^(3j) = 0x1F58D1 -> bytes D1 58 1F;
+    # 6-bit codes 1, 2, 3, 63 -> 0xFC3081 -> bytes 81 30 FC.
+    c3 = np.array([[1, 2, 3, 4, 5, 6, 7, 0]], np.uint8)
+    assert list(oracle.pack(c3, 3)[0]) == [0xD1, 0x58, 0x1F]
+    c6 = np.array([[1, 2, 3, 63]], np.uint8)
+    assert list(oracle.pack(c6, 6)[0]) == [0x81, 0x30, 0xFC]
+    # every pair of codes in every position of a 24-bit group survives the round trip
+    for bits in (3, 6):
+        per = 24 // bits
+        rng = np.random.default_rng(bits)
+        c = rng.integers(0, 1 << bits, size=(64, 8 * per)).astype(np.uint8)
+        assert np.array_equal(oracle.unpack(oracle.pack(c, bits), c.shape[1], bits), c)
+        # one set code at each position lights exactly its own bits
+        for j in range(per):
+            one = np.zeros((1, per), np.uint8)
+            one[0, j] = (1 << bits) - 1
+            word = int.from_bytes(bytes(oracle.pack(one, bits)[0]), "little")
+            assert word == ((1 << bits) - 1) << (bits * j)
+    with pytest.raises(ValueError):
+        oracle.pack(np.zeros((1, 4), np.uint8), 3)      # 12 bits: not whole bytes
+
+
 # ---------------------------------------------------------------- products
 
 def test_int8_gemm_matches_integer_matmul():
@@ -460,3 +485,15 @@ def test_haar_input_is_orthogonal():
     # the dense comparison rotation is orthogonal (Q^T Q = I to fp32 rounding)
     q = workloads.haar_orthogonal(5, 256).astype(np.float64)
     assert np.abs(q.T @ q - np.eye(256)).max() < 1e-6
+
+
+@pytest.mark.parametrize("bits,mse", [(3, 0.034548), (4, 0.009501)])
+def test_lloyd_max_mse_matches_max_table(bits, mse):
+    # Max (1960), "Quantizing for minimum distortion" (outside the pages): the minimum mean-square
+    # error of an L-level quantiser of N(0,1); recomputed here by quadrature over the oracle's cells.
+    cb = oracle.lloyd_max(bits, 1)
+    c, t = cb["c_unit"], cb["t_unit"]
+    edges = np.concatenate([[-np.inf], t, [np.inf]])
+    err = sum(scipy.integrate.quad(lambda x, ck=c[k]: (x - ck) ** 2 * scipy.stats.norm.pdf(x),
+                                   edges[k], edges[k + 1])[0] for k in range(len(c)))
+    assert abs(err - mse) < 2e-6
