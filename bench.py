@@ -210,8 +210,10 @@ def bench_codebook(args, torch, rtq, workloads, variant, mode=None):
     fp16 LUT product."""
     mode = rtq.RTQ_CODEBOOK_I8 if mode is None else mode
     i8 = mode == rtq.RTQ_CODEBOOK_I8
-    if variant == "w4a4":
-        d, N, bits_w = workloads.DIT_HIDDEN, workloads.DIT_HIDDEN, 4
+    bits_a = 4
+    if variant in ("w4a4", "w3a3", "w4a6"):     # the attention-output shape
+        d, N = workloads.DIT_HIDDEN, workloads.DIT_HIDDEN
+        bits_w, bits_a = {"w4a4": (4, 4), "w3a3": (3, 3), "w4a6": (4, 6)}[variant]
         wh = workloads.w4a4_weight_bf16()
     else:
         d, N, bits_w = workloads.DIT_MLP, workloads.DIT_HIDDEN, 2
@@ -219,14 +221,14 @@ def bench_codebook(args, torch, rtq, workloads, variant, mode=None):
     xh = workloads.dit_activations_bf16(d)
     T = xh.shape[0]
     R = rtq.Rpbh.from_seed(workloads.RPBH_SEED[d], d)
-    cb_a, cb_w = rtq.Codebook.for_dim(d, 4), rtq.Codebook.for_dim(d, bits_w)
+    cb_a, cb_w = rtq.Codebook.for_dim(d, bits_a), rtq.Codebook.for_dim(d, bits_w)
     w = _bf16_dev(wh, torch)
     wc = torch.empty((N, d * bits_w // 8), dtype=torch.uint8, device="cuda")
     wn = torch.empty(N, dtype=torch.bfloat16, device="cuda")
     rtq.quantize_rows(w, wc, wn, R, rtq.RTQ_CODEBOOK, cb_w, 0.0)
     del w
     xs = _copies(_bf16_dev(xh, torch), 512 << 20, torch)
-    codes = torch.empty((T, d if i8 else d // 2), dtype=torch.int8 if i8 else torch.uint8, device="cuda")
+    codes = torch.empty((T, d if i8 else d * bits_a // 8), dtype=torch.int8 if i8 else torch.uint8, device="cuda")
     norm = torch.empty(T, dtype=torch.float32, device="cuda")
     y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
 
@@ -246,11 +248,12 @@ def bench_codebook(args, torch, rtq, workloads, variant, mode=None):
     wall, tq, tg = _time_pairs(steps, quant, gemm, torch)
     quant_burst = _burst_ms(max(20, steps), quant, torch)
     flops = 2.0 * T * d * N
-    q_bytes = T * (2 * d + (d if i8 else d // 2) + 4)
+    q_bytes = T * (2 * d + (d if i8 else d * bits_a // 8) + 4)
     gemm_tflops = flops / (tg.mean() * 1e-3) / 1e12
     peak = PEAK_INT8_TOPS if i8 else PEAK_F16_TFLOPS
     return {"mode": "codebook on INT8 MFMA (int8 codebook values)" if i8 else "codebook, fp16 LUT on fp16 MFMA",
-            "T": T, "d": d, "N": N, "step_ms": wall * 1e3 / steps, "quant_ms": quant_burst,
+            "T": T, "d": d, "N": N, "bits_w": bits_w, "bits_a": bits_a, "step_ms": wall * 1e3 / steps,
+            "quant_ms": quant_burst,
             "quant_event_span_ms": float(tq.mean()),
             "gemm_ms": float(tg.mean()), "TFLOP/s": flops / (wall / steps) / 1e12,
             "gemm_TFLOP/s": gemm_tflops, "gemm_peak": peak, "gemm_frac_peak": gemm_tflops / peak,
@@ -469,7 +472,8 @@ def main():
         return
     if args.only == "codebook":   # the codebook layers only (profiling runs)
         out = {k: bench_codebook(args, torch, rtq, workloads, v) for k, v in
-               [("w4a4_dit_attn_out_4608x4096x4096", "w4a4"), ("w2a4_dit_mlp_down_4608x16384x4096", "w2a4")]}
+               [("w4a4_dit_attn_out_4608x4096x4096", "w4a4"), ("w2a4_dit_mlp_down_4608x16384x4096", "w2a4"),
+                ("w3a3_dit_attn_out_4608x4096x4096", "w3a3"), ("w4a6_dit_attn_out_4608x4096x4096", "w4a6")]}
         print(json.dumps(out))
         return
     r = bench_w8a8(args, torch, rtq, workloads)
@@ -482,6 +486,8 @@ def main():
                                                                             rtq.RTQ_CODEBOOK)
         extra["w2a4_dit_mlp_down_4608x16384x4096_fp16_lut"] = bench_codebook(args, torch, rtq, workloads, "w2a4",
                                                                              rtq.RTQ_CODEBOOK)
+        extra["w3a3_dit_attn_out_4608x4096x4096"] = bench_codebook(args, torch, rtq, workloads, "w3a3")
+        extra["w4a6_dit_attn_out_4608x4096x4096"] = bench_codebook(args, torch, rtq, workloads, "w4a6")
         extra["transform_ablation"] = bench_ablation(args, torch, rtq, workloads)
     cpu = None
     if not args.no_cpu_baseline:

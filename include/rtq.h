@@ -118,10 +118,15 @@ rtq_status rtq_rpbh_rotate(const void* x, rtq_dtype xt, void* y, rtq_dtype yt, i
  *   CODEBOOK:  s = ||x'||_2 (summed in double, rounded to fp32); u_j = x'_j / (s + eps) in fp32
  *              (0 when s + eps == 0); code_j = #{k : boundaries[k] < u_j}.  The norm s is stored as
  *              scale_t: BF16 for weights (eps = 0), F32 for activations (eps > 0, e.g. 1e-8).
- *              codes: uint8[rows][d * bits / 8], element j at byte j*bits/8, bit (j mod 8/bits)*bits
- *              (least significant first).  cb->bits must be 2 or 4.
+ *              codes: uint8[rows][d * bits / 8], the row's codes as one little-endian bit stream,
+ *              element j in bits [j*bits, j*bits + bits) (least significant first; for 2 and 4
+ *              bits: byte j*bits/8, bit (j mod 8/bits)*bits).  cb->bits 2, 3 or 4 (the 3-bit codes
+ *              of the W3A3 variant, OrbitQuant article 3.2-3.3, need BF16 x and R != NULL).
  *   CODEBOOK_I8: the CODEBOOK codes, written as their int8 codebook values v[code] (see
- *              RTQ_CODEBOOK_I8): codes int8[rows][d].  cb needs centroids and boundaries.
+ *              RTQ_CODEBOOK_I8): codes int8[rows][d].  cb needs centroids and boundaries;
+ *              cb->bits 2, 3, 4 or 6 (3 and 6, as for W3A3 / W4A6 activations, need BF16 x and
+ *              R != NULL; 6-bit codes are searched among the row's exact thresholds for d >= 4096,
+ *              and counted boundary by boundary below that).
  *   scale  [rows] of scale_t.
  * rows == 0 is a no-op. */
 rtq_status rtq_quantize_rows(const void* x, rtq_dtype xt, int64_t rows, int32_t d, const rtq_rpbh* R,
@@ -141,8 +146,8 @@ rtq_status rtq_quantize_rows(const void* x, rtq_dtype xt, int64_t rows, int32_t 
  *   CODEBOOK_I8: a_codes int8[T][d] holds the activations' int8 codebook values (rtq_quantize_rows
  *              in this mode), w_codes packed codes [N][d*bits_w/8]; acc = sum_j a[t][j] v_w[qw]
  *              exactly in int32, y = acc * a_scale[t] * w_scale[n] / (S_a S_w) in fp32; yt F32 or
- *              BF16.  cb_a (centroids, bits 2 or 4) gives S_a; cb_w (centroids, bits 2 or 4) the
- *              weight values.  N <= 2^22, d a multiple of 64.
+ *              BF16.  cb_a (centroids, bits 2, 3, 4 or 6) gives S_a; cb_w (centroids, bits 2, 3 or
+ *              4) the weight values.  N <= 2^22, d a multiple of 64.
  * T == 0 is a no-op. */
 rtq_status rtq_qgemm(const void* a_codes, const float* a_scale, int64_t T, const void* w_codes,
                      const void* w_scale, rtq_dtype w_scale_t, int64_t N, int32_t d, rtq_qmode mode,

@@ -20,11 +20,16 @@ __device__ __forceinline__ float codebook_int8_scale(const float* c, int L) {
     return 127.0f / m;
 }
 
+// The value v_k of one entry (any L, e.g. the 64 of a 6-bit codebook held one per lane).
+__device__ __forceinline__ int codebook_int8_value(const float* c, int k, float s) {
+    return static_cast<int>(rintf(c[k] * s));
+}
+
 // The L <= 16 values v_k as bytes: entry k in byte k % 4 of word k / 4.
 __device__ __forceinline__ void codebook_int8_table(const float* c, int L, float s, uint32_t (&lut)[4]) {
     lut[0] = lut[1] = lut[2] = lut[3] = 0u;
     for (int k = 0; k < L; ++k) {
-        const uint32_t v = static_cast<uint32_t>(static_cast<int>(rintf(c[k] * s))) & 0xffu;
+        const uint32_t v = static_cast<uint32_t>(codebook_int8_value(c, k, s)) & 0xffu;
         lut[k >> 2] |= v << (8 * (k & 3));
     }
 }
@@ -36,6 +41,11 @@ __device__ __forceinline__ uint32_t lut16_x4(const uint32_t (&lut)[4], uint32_t 
     const uint32_t hi = __builtin_amdgcn_perm(lut[3], lut[2], b & 0x07070707u);
     const uint32_t m = __builtin_amdgcn_perm(0u, 0u, ((b >> 3) & 0x01010101u) | 0x0C0C0C0Cu);
     return (hi & m) | (lo & ~m);
+}
+
+// 4 codes (one per byte, 0..7) -> their 4 int8 values (table in lut[0..1]).
+__device__ __forceinline__ uint32_t lut8_x4(const uint32_t (&lut)[4], uint32_t b) {
+    return __builtin_amdgcn_perm(lut[1], lut[0], b);
 }
 
 // 4 codes (one per byte, 0..3) -> their 4 int8 values (table in lut[0]).

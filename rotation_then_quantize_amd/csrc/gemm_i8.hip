@@ -100,11 +100,12 @@ __device__ __forceinline__ void load_to_lds(v4i rsrc, uint32_t voff, uint32_t ld
 // Wait until at most n vector-memory operations of this wave are outstanding.
 template <int n>
 __device__ __forceinline__ void wait_vmcnt() {
-    static_assert(n == 0 || n == 2 || n == 3 || n == 4 || n == 8, "add the immediate");
+    static_assert(n == 0 || n == 2 || n == 3 || n == 4 || n == 5 || n == 8, "add the immediate");
     if constexpr (n == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if constexpr (n == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
     if constexpr (n == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
     if constexpr (n == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    if constexpr (n == 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
     if constexpr (n == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
 }
 
@@ -144,6 +145,19 @@ __device__ __forceinline__ void decode2(const uint32_t (&lut)[4], const uint32_t
         out[4 * i + 1] = __builtin_amdgcn_perm(t23l, t01l, 0x07060302u);
         out[4 * i + 2] = __builtin_amdgcn_perm(t23h, t01h, 0x05040100u);
         out[4 * i + 3] = __builtin_amdgcn_perm(t23h, t01h, 0x07060302u);
+    }
+}
+
+// 32 packed 3-bit codes (one LSB-first bit stream over 3 words) -> 32 int8 values in order (8
+// words); lut[0..1] hold the 8 values.  Group g of 4 codes is the 12 bits at 12g: its codes are
+// spread into the 4 selector bytes of one v_perm_b32.
+__device__ __forceinline__ void decode3(const uint32_t (&lut)[4], const uint32_t (&in)[3], uint32_t (&out)[8]) {
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+        const int bit = 12 * g, w = bit >> 5, sh = bit & 31;
+        const uint32_t v = sh + 12 <= 32 ? in[w] >> sh : __builtin_amdgcn_alignbit(in[w + 1], in[w], sh);
+        const uint32_t sel = (v & 7u) | ((v << 5) & 0x700u) | ((v << 10) & 0x70000u) | ((v << 15) & 0x7000000u);
+        out[g] = __builtin_amdgcn_perm(lut[1], lut[0], sel);
     }
 }
 
@@ -203,7 +217,7 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
     // stages ahead and decoded to int8 codebook values into the stage ring one stage ahead.
     constexpr bool kCoded = kWBits < 8;
     constexpr int kRawStage = raw_stage_bytes(kWBits);
-    constexpr int kCodeLoads = kWBits == 4 ? 1 : 2;     // LDS-writing loads per thread per code stage
+    constexpr int kCodeLoads = kWBits == 4 ? 1 : (kWBits == 3 ? 3 : 2);   // LDS-writing loads per thread per code stage
     static_assert(!kCoded || kYKind != 2, "raw accumulators only for int8 weights");
     constexpr int kThreads = 64 * kWaves;
     constexpr int WN = BN / kWavesN;                           // columns per wave
@@ -293,7 +307,8 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
     };
     // Packed weight codes of stage st -> raw slot st % kRawSlots, laid out [row][BK * bits / 8].
     // 4-bit: one 16-byte load per thread (thread t: row t / 2, half t % 2 of the row's 32 bytes);
-    // 2-bit: two 4-byte loads per thread (load q, thread t: bytes q * 2048 + 4t of the slot).
+    // 2-bit: two 4-byte loads per thread (load q, thread t: bytes q * 2048 + 4t of the slot);
+    // 3-bit: three such loads (rows of 24 bytes).
     const uint32_t raw_base = lds_base + static_cast<uint32_t>(kLds);
     auto issue_codes = [&](int st) {
         const uint32_t slot = raw_base + static_cast<uint32_t>((st % kRawSlots) * kRawStage);
@@ -306,6 +321,14 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
             for (int q = 0; q < 2; ++q) {
                 const int b = q * 2048 + 4 * tid;                 // byte within the slot
                 const uint32_t off = static_cast<uint32_t>((b >> 4) * wrow + (kbeg + st) * 16 + (b & 15));
+                load_to_lds4(rsw, off, slot + q * 2048 + static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave * 256)));
+            }
+        } else if constexpr (kWBits == 3) {
+#pragma unroll
+            for (int q = 0; q < 3; ++q) {
+                const int b = q * 2048 + 4 * tid;                 // byte within the slot
+                const int row = b / 24;
+                const uint32_t off = static_cast<uint32_t>(row * wrow + (kbeg + st) * 24 + (b - 24 * row));
                 load_to_lds4(rsw, off, slot + q * 2048 + static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave * 256)));
             }
         }
@@ -325,6 +348,10 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
             const uint2 x = *reinterpret_cast<const uint2*>(raw + 8 * tid);
             const uint32_t in[2] = {x.x, x.y};
             decode2(lut, in, v);
+        } else if constexpr (kWBits == 3) {
+            const uint32_t* xr = reinterpret_cast<const uint32_t*>(raw + 12 * tid);
+            const uint32_t in[3] = {xr[0], xr[1], xr[2]};
+            decode3(lut, in, v);
         }
         const int row = tid >> 1, c0 = 2 * (tid & 1), sw = (row >> 2) & 3;
         int8_t* wb = lds + (st & (kStages - 1)) * kStageBytes + kOpBytes + row * BK;
@@ -633,6 +660,11 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
     }
 }
 
+// The launch tag of the split counters.  One sequence for every kernel variant: a workspace may
+// pass between products of different weight widths (or be recycled by an allocator), and a tag
+// reused from another variant's sequence would read that launch's arrivals as this one's.
+std::atomic<unsigned int> g_split_epoch{0};
+
 template <int kWavesN, int kWBits>
 hipError_t launch_config(const GemmI8Args& g, hipStream_t stream) {
     using KernelFn = void (*)(const int8_t*, const float*, const int8_t*, const void*, int64_t, int64_t, int,
@@ -689,9 +721,8 @@ hipError_t launch_config(const GemmI8Args& g, hipStream_t stream) {
         while (split & (split - 1)) split &= split - 1;
         if ((slots / kXcds) % std::max<int64_t>(split, 1) != 0) split = 1;
         if (split >= 2) {
-            static std::atomic<unsigned int> epoch{0};
-            unsigned int e = ++epoch;
-            if (e == 0) e = ++epoch;
+            unsigned int e = ++g_split_epoch;
+            if (e == 0) e = ++g_split_epoch;
             unsigned char* ws = static_cast<unsigned char*>(g.workspace);
             sp = SplitArgs{static_cast<int>(whole), static_cast<int>(split), reinterpret_cast<v4i*>(ws),
                            reinterpret_cast<unsigned long long*>(ws + static_cast<size_t>(slots) * BM * BN * 4), e};
@@ -721,10 +752,13 @@ hipError_t launch_gemm_i8(const GemmI8Args& g, hipStream_t stream) {
     switch (g.w_bits) {
         case 8: return launch_config<kDefaultWavesN, 8>(g, stream);
         case 4:
-            if (g.cent_a == nullptr || g.cent_w == nullptr || g.a_bits < 1 || g.a_bits > 4) return hipErrorInvalidValue;
+            if (g.cent_a == nullptr || g.cent_w == nullptr || g.a_bits < 1 || g.a_bits > 6) return hipErrorInvalidValue;
             return launch_config<kDefaultWavesN, 4>(g, stream);
+        case 3:
+            if (g.cent_a == nullptr || g.cent_w == nullptr || g.a_bits < 1 || g.a_bits > 6) return hipErrorInvalidValue;
+            return launch_config<kDefaultWavesN, 3>(g, stream);
         case 2:
-            if (g.cent_a == nullptr || g.cent_w == nullptr || g.a_bits < 1 || g.a_bits > 4) return hipErrorInvalidValue;
+            if (g.cent_a == nullptr || g.cent_w == nullptr || g.a_bits < 1 || g.a_bits > 6) return hipErrorInvalidValue;
             return launch_config<kDefaultWavesN, 2>(g, stream);
     }
     return hipErrorInvalidValue;

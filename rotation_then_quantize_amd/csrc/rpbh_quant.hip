@@ -196,8 +196,11 @@ template <int kOut>
 struct CodeCtx {
     static constexpr bool k4 = kOut == kRowCode4 || kOut == kRowLut4;
     static constexpr bool k2 = kOut == kRowCode2 || kOut == kRowLut2;
-    static constexpr bool kLut = kOut == kRowLut4 || kOut == kRowLut2;
-    static constexpr int kBits = k4 ? 4 : (k2 ? 2 : 8);
+    static constexpr bool k3 = kOut == kRowCode3 || kOut == kRowLut3;
+    static constexpr bool k6 = kOut == kRowLut6;
+    static constexpr bool kLut = kOut == kRowLut4 || kOut == kRowLut2 || kOut == kRowLut3 || kOut == kRowLut6;
+    static constexpr bool kGrid = k4 || k3;   // boundary grid for 8 and 16 levels
+    static constexpr int kBits = k4 ? 4 : (k2 ? 2 : (k3 ? 3 : (k6 ? 6 : 8)));
     static constexpr int kNB = (1 << kBits) - 1;
     int lane_base = 0;
     int kidx = 0;                 // my threshold slot
@@ -206,23 +209,30 @@ struct CodeCtx {
     uint32_t cell = 0;
     float grid_k = 0.0f;
     bool use_grid = false;        // per lane here: the caller makes it uniform over the workgroup
+    bool use_bsearch = false;     // 64 levels: thresholds one per lane of a 64-lane row, binary search
     uint32_t lut[4] = {0u, 0u, 0u, 0u};
+    int lutv = 0;                 // 64 levels: lane k holds the int8 value of code k
 
     __device__ __forceinline__ void setup(const float* __restrict__ bounds, const float* __restrict__ cent,
                                           int log2nb, int lane) {
         const int row_lanes = (1 << log2nb) < 64 ? (1 << log2nb) : 64;   // lanes of my row in my wave
         lane_base = lane & ~(row_lanes - 1);
         kidx = lane - lane_base;
-        if (kLut) codebook_int8_table(cent, 1 << kBits, codebook_int8_scale(cent, 1 << kBits), lut);
+        if (kLut && !k6) codebook_int8_table(cent, 1 << kBits, codebook_int8_scale(cent, 1 << kBits), lut);
+        if (k6) {
+            lutv = codebook_int8_value(cent, lane, codebook_int8_scale(cent, 64));
+            use_bsearch = row_lanes == 64;
+            if (use_bsearch && kidx < kNB) my_t = bounds[kidx];
+        }
         if (k2) {
 #pragma unroll
             for (int k = 0; k < 3; ++k) tb[k] = bounds[k];
         }
-        if (k4) {
+        if (kGrid) {
             if (kidx < kNB) my_t = bounds[kidx];
             // grid over [-tmax, tmax] with 40 cells of width tmax/20; 64 cells in all (end cells clamp)
             const float tmax = fmaxf(fabsf(bounds[0]), fabsf(bounds[kNB - 1]));
-            use_grid = row_lanes >= 16 && tmax > 0.0f;
+            use_grid = row_lanes >= kNB + 1 && tmax > 0.0f;
             if (use_grid) {
                 grid_k = 20.0f / tmax;                 // cell units per unit of u
                 const int j = lane;                    // cell index, 0..63
@@ -252,7 +262,7 @@ struct BlockOut {
 // Bytes per output element (8 codes per 64 bits for 4-bit codes etc., in bits).
 template <int kOut>
 constexpr int out_bits() {
-    return kOut == kRowCode4 ? 4 : (kOut == kRowCode2 ? 2 : 8);
+    return kOut == kRowCode4 ? 4 : (kOut == kRowCode2 ? 2 : (kOut == kRowCode3 ? 3 : 8));
 }
 
 // Quantise a lane's rotated block (acc = 8 x' in fp64: the lane's 64 outputs of its row) with the
@@ -265,6 +275,8 @@ __device__ __forceinline__ void quantize_block(double (&acc)[kH], const unsigned
                                                BlockOut& res) {
     constexpr bool k4 = CodeCtx<kOut>::k4;
     constexpr bool k2 = CodeCtx<kOut>::k2;
+    constexpr bool k3 = CodeCtx<kOut>::k3;
+    constexpr bool k6 = CodeCtx<kOut>::k6;
     constexpr bool kLut = CodeCtx<kOut>::kLut;
     constexpr int kBits = CodeCtx<kOut>::kBits;
     constexpr int kNB = CodeCtx<kOut>::kNB;
@@ -336,11 +348,18 @@ __device__ __forceinline__ void quantize_block(double (&acc)[kH], const unsigned
         double ss = row_sum((ss4[0] + ss4[1]) + (ss4[2] + ss4[3]), log2nb, red);
         const float s = static_cast<float>(sqrt(ss));
         const float den = (eps == 0.0f) ? s : s + eps;
-        // codes per 32-bit word: packed, or one per byte before the int8 table lookup
+        // codes as one LSB-first bit stream of kSlot-bit fields: packed codes (2, 3, 4 bits), or one
+        // byte per code before the int8 table lookup (6-bit codes are looked up as they are found)
         constexpr int kSlot = kLut ? 8 : kBits;
-        constexpr int kPerWord = 32 / kSlot;
+        constexpr int kWords = kH * kSlot / 32;
+        auto put = [&](int b, uint32_t code) {
+            if constexpr (k6) code = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(static_cast<int>(4 * code), cc.lutv)) & 0xffu;
+            const int p = b * kSlot, q = p >> 5, sh = p & 31;
+            w[q] |= code << sh;
+            if (sh + kSlot > 32) w[q + 1] |= code >> (32 - sh);
+        };
 #pragma unroll
-        for (int q = 0; q < kH / kPerWord; ++q) w[q] = 0u;
+        for (int q = 0; q < kWords; ++q) w[q] = 0u;
         if (den != 0.0f) {
             // u = fl32(x'/den); code = #{k : t_k < u} = #{k : x' >= Y_k}, Y_k exact per row
             if (k2) {
@@ -350,7 +369,20 @@ __device__ __forceinline__ void quantize_block(double (&acc)[kH], const unsigned
 #pragma unroll
                 for (int b = 0; b < kH; ++b) {
                     const uint32_t code = (xr[b] >= Y[0] ? 1u : 0u) + (xr[b] >= Y[1] ? 1u : 0u) + (xr[b] >= Y[2] ? 1u : 0u);
-                    w[b / kPerWord] |= code << ((b % kPerWord) * kSlot);
+                    put(b, code);
+                }
+            } else if (k6 && cc.use_bsearch) {
+                // my lane holds Y_kidx (lane 63: +inf); code = #{k : x' >= Y_k} by binary search
+                const float myY = cc.kidx < kNB ? exact_threshold(cc.my_t, den) : __builtin_inff();
+#pragma unroll
+                for (int b = 0; b < kH; ++b) {
+                    int lo = 0;
+#pragma unroll
+                    for (int step = 32; step >= 1; step >>= 1) {
+                        const float t = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (lo + step - 1), __float_as_int(myY)));
+                        lo += xr[b] >= t ? step : 0;
+                    }
+                    put(b, static_cast<uint32_t>(lo));
                 }
             } else if (cc.use_grid) {
                 // my slot holds Y_kidx (slot 15: +inf); cells hold (#below << 8) | 4*slot
@@ -363,7 +395,7 @@ __device__ __forceinline__ void quantize_block(double (&acc)[kH], const unsigned
                     const uint32_t e = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(a, static_cast<int>(cc.cell)));
                     const float Yk = __int_as_float(__builtin_amdgcn_ds_bpermute(static_cast<int>(e) + base4, __float_as_int(myY)));
                     const uint32_t code = (e >> 8) + (xr[b] >= Yk ? 1u : 0u);
-                    w[b / kPerWord] |= code << ((b % kPerWord) * kSlot);
+                    put(b, code);
                 }
             } else {
                 // a general codebook, or too few lanes per row for the slot table: divide and count
@@ -372,7 +404,7 @@ __device__ __forceinline__ void quantize_block(double (&acc)[kH], const unsigned
                     const float u = xr[b] / den;
                     uint32_t code = 0;
                     for (int k = 0; k < kNB; ++k) code += (bounds[k] < u) ? 1u : 0u;
-                    w[b / kPerWord] |= code << ((b % kPerWord) * kSlot);
+                    put(b, code);
                 }
             }
         } else {
@@ -380,11 +412,12 @@ __device__ __forceinline__ void quantize_block(double (&acc)[kH], const unsigned
             uint32_t code = 0;
             for (int k = 0; k < kNB; ++k) code += (bounds[k] < 0.0f) ? 1u : 0u;
 #pragma unroll
-            for (int b = 0; b < kH; ++b) w[b / kPerWord] |= code << ((b % kPerWord) * kSlot);
+            for (int b = 0; b < kH; ++b) put(b, code);
         }
-        if (kLut) {
+        if (kLut && !k6) {
 #pragma unroll
-            for (int q = 0; q < kH / kPerWord; ++q) w[q] = k4 ? lut16_x4(cc.lut, w[q]) : lut4_x4(cc.lut, w[q]);
+            for (int q = 0; q < kWords; ++q)
+                w[q] = k4 ? lut16_x4(cc.lut, w[q]) : (k3 ? lut8_x4(cc.lut, w[q]) : lut4_x4(cc.lut, w[q]));
         }
         res.s = s;
     }
@@ -395,9 +428,15 @@ template <int kOut>
 __device__ __forceinline__ void store_block(const BlockOut& res, void* __restrict__ out, void* __restrict__ scale_out,
                                             int scale_bf16, int64_t row, int blk, int d) {
     constexpr int kWords = kH * out_bits<kOut>() / 32;
-    uint4* o = reinterpret_cast<uint4*>(static_cast<uint8_t*>(out) + (row * d + blk * kH) * out_bits<kOut>() / 8);
+    if constexpr (kWords % 4 == 0) {
+        uint4* o = reinterpret_cast<uint4*>(static_cast<uint8_t*>(out) + (row * d + blk * kH) * out_bits<kOut>() / 8);
 #pragma unroll
-    for (int q = 0; q < kWords / 4; ++q) o[q] = make_uint4(res.w[4 * q], res.w[4 * q + 1], res.w[4 * q + 2], res.w[4 * q + 3]);
+        for (int q = 0; q < kWords / 4; ++q) o[q] = make_uint4(res.w[4 * q], res.w[4 * q + 1], res.w[4 * q + 2], res.w[4 * q + 3]);
+    } else {   // 3-bit codes: 24 bytes per block, 8-byte aligned
+        uint2* o = reinterpret_cast<uint2*>(static_cast<uint8_t*>(out) + (row * d + blk * kH) * out_bits<kOut>() / 8);
+#pragma unroll
+        for (int q = 0; q < kWords / 2; ++q) o[q] = make_uint2(res.w[2 * q], res.w[2 * q + 1]);
+    }
     if (blk == 0) {
         if (scale_bf16)
             static_cast<uint16_t*>(scale_out)[row] = static_cast<uint16_t>(f32_to_bf16(res.s));
@@ -488,7 +527,7 @@ rpbh_quant_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int 
     // ---- codebook set-up
     CodeCtx<kOut> cc;
     cc.setup(bounds, cent, log2nb, lane);
-    if (CodeCtx<kOut>::k4) cc.use_grid = __syncthreads_and(cc.use_grid ? 1 : 0) != 0;
+    if (CodeCtx<kOut>::kGrid) cc.use_grid = __syncthreads_and(cc.use_grid ? 1 : 0) != 0;
 
     // This workgroup's rows: an even share [r_begin, r_end) of all rows, taken rpg rows per group
     // (the last group of the share may be partial), so every workgroup does the same work.
@@ -603,7 +642,7 @@ rpbh_wave_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int l
     }
     CodeCtx<kOut> cc;
     cc.setup(bounds, cent, log2nb, lane);
-    if (CodeCtx<kOut>::k4) cc.use_grid = __syncthreads_and(cc.use_grid ? 1 : 0) != 0;
+    if (CodeCtx<kOut>::kGrid) cc.use_grid = __syncthreads_and(cc.use_grid ? 1 : 0) != 0;
     __syncthreads();   // tables complete
 
     const int64_t total = rows * static_cast<int64_t>(d);
@@ -716,7 +755,8 @@ hipError_t launch_nc(const RowArgs& a, int log2d, hipStream_t stream) {
 bool rpbh_quant_bf16_supported(const RowArgs& a) {
     return a.x_bf16 && a.perm != nullptr &&
            (a.out_kind == kRowInt8 || a.out_kind == kRowCode4 || a.out_kind == kRowCode2 ||
-            a.out_kind == kRowLut4 || a.out_kind == kRowLut2) && a.d >= 64 &&
+            a.out_kind == kRowLut4 || a.out_kind == kRowLut2 || a.out_kind == kRowCode3 ||
+            a.out_kind == kRowLut3 || a.out_kind == kRowLut6) && a.d >= 64 &&
            a.d <= kMaxD;
 }
 
@@ -730,6 +770,9 @@ hipError_t launch_rpbh_quant_bf16(const RowArgs& a, hipStream_t stream) {
         case kRowCode2: return launch_nc<kRowCode2>(a, log2d, stream);
         case kRowLut4: return launch_nc<kRowLut4>(a, log2d, stream);
         case kRowLut2: return launch_nc<kRowLut2>(a, log2d, stream);
+        case kRowCode3: return launch_nc<kRowCode3>(a, log2d, stream);
+        case kRowLut3: return launch_nc<kRowLut3>(a, log2d, stream);
+        case kRowLut6: return launch_nc<kRowLut6>(a, log2d, stream);
         default: break;
     }
     return hipErrorInvalidValue;

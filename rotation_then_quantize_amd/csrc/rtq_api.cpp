@@ -79,7 +79,8 @@ rtq_status check_float_dtype(rtq_dtype t, const char* name) {
 
 rtq_status check_codebook(const rtq_codebook* cb, const char* name, bool need_centroids, bool need_bounds) {
     if (cb == nullptr) return fail(RTQ_ERR_INVALID_ARG, "%s is NULL", name);
-    if (cb->bits != 2 && cb->bits != 4) return fail(RTQ_ERR_UNSUPPORTED, "%s.bits must be 2 or 4 (got %d)", name, cb->bits);
+    if (cb->bits != 2 && cb->bits != 3 && cb->bits != 4 && cb->bits != 6)
+        return fail(RTQ_ERR_UNSUPPORTED, "%s.bits must be 2, 3, 4 or 6 (got %d)", name, cb->bits);
     if (need_centroids && cb->centroids == nullptr) return fail(RTQ_ERR_INVALID_ARG, "%s.centroids is NULL", name);
     if (need_bounds && cb->boundaries == nullptr) return fail(RTQ_ERR_INVALID_ARG, "%s.boundaries is NULL", name);
     return RTQ_OK;
@@ -115,17 +116,24 @@ rtq_status plan_quantize(const void* x, rtq_dtype xt, int64_t rows, int32_t d, c
     } else if (mode == RTQ_CODEBOOK) {
         RTQ_TRY(check_codebook(cb, "cb", false, true));
         if (!(eps >= 0.0f) || std::isinf(eps)) return fail(RTQ_ERR_INVALID_ARG, "eps must be finite and >= 0");
-        a.out_kind = cb->bits == 4 ? rtq::kRowCode4 : rtq::kRowCode2;
+        if (cb->bits == 6) return fail(RTQ_ERR_UNSUPPORTED, "packed 6-bit codes are not supported (use RTQ_CODEBOOK_I8)");
+        a.out_kind = cb->bits == 4 ? rtq::kRowCode4 : (cb->bits == 3 ? rtq::kRowCode3 : rtq::kRowCode2);
         a.bounds = cb->boundaries;
     } else if (mode == RTQ_CODEBOOK_I8) {
         RTQ_TRY(check_codebook(cb, "cb", true, true));
         if (!(eps >= 0.0f) || std::isinf(eps)) return fail(RTQ_ERR_INVALID_ARG, "eps must be finite and >= 0");
-        a.out_kind = cb->bits == 4 ? rtq::kRowLut4 : rtq::kRowLut2;
+        a.out_kind = cb->bits == 4 ? rtq::kRowLut4
+                     : cb->bits == 3 ? rtq::kRowLut3
+                     : cb->bits == 6 ? rtq::kRowLut6
+                                     : rtq::kRowLut2;
         a.bounds = cb->boundaries;
         a.centroids = cb->centroids;
     } else {
         return fail(RTQ_ERR_INVALID_ARG, "unknown mode %d", static_cast<int>(mode));
     }
+    if ((a.out_kind == rtq::kRowCode3 || a.out_kind == rtq::kRowLut3 || a.out_kind == rtq::kRowLut6) &&
+        (!a.x_bf16 || a.perm == nullptr))
+        return fail(RTQ_ERR_UNSUPPORTED, "3- and 6-bit codes need bf16 rows and a rotation descriptor");
     *out = a;
     return RTQ_OK;
 }
@@ -164,6 +172,8 @@ rtq_status plan_gemm(const void* a_codes, const float* a_scale, int64_t T, const
         RTQ_TRY(check_codebook(cb_a, "cb_a", true, false));
         RTQ_TRY(check_codebook(cb_w, "cb_w", true, false));
         if (cb_a->bits != 4) return fail(RTQ_ERR_UNSUPPORTED, "activation codes must be 4-bit (got %d)", cb_a->bits);
+        if (cb_w->bits != 2 && cb_w->bits != 4)
+            return fail(RTQ_ERR_UNSUPPORTED, "RTQ_CODEBOOK weight codes must be 2- or 4-bit (got %d)", cb_w->bits);
         if (yt != RTQ_F32 && yt != RTQ_BF16) return fail(RTQ_ERR_UNSUPPORTED, "yt must be RTQ_F32 or RTQ_BF16");
         p.lut = true;
         p.cb = rtq::GemmLutArgs{static_cast<const uint8_t*>(a_codes), a_scale, static_cast<const uint8_t*>(w_codes),
@@ -172,6 +182,7 @@ rtq_status plan_gemm(const void* a_codes, const float* a_scale, int64_t T, const
     } else if (mode == RTQ_CODEBOOK_I8) {
         RTQ_TRY(check_codebook(cb_a, "cb_a", true, false));
         RTQ_TRY(check_codebook(cb_w, "cb_w", true, false));
+        if (cb_w->bits == 6) return fail(RTQ_ERR_UNSUPPORTED, "weight codes must be 2-, 3- or 4-bit (got 6)");
         if (yt != RTQ_F32 && yt != RTQ_BF16) return fail(RTQ_ERR_UNSUPPORTED, "yt must be RTQ_F32 or RTQ_BF16");
         if (N > (int64_t(1) << 22)) return fail(RTQ_ERR_UNSUPPORTED, "N too large (max %d)", 1 << 22);
         p.lut = false;
@@ -195,7 +206,7 @@ size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 size_t workspace_bytes(int64_t T, int32_t d, rtq_qmode mode, int32_t bits_a, bool with_split = true) {
     if (T < 0 || d <= 0) return 0;
     size_t code_bytes;
-    if (mode == RTQ_INT8 || (mode == RTQ_CODEBOOK_I8 && (bits_a == 2 || bits_a == 4)))
+    if (mode == RTQ_INT8 || (mode == RTQ_CODEBOOK_I8 && (bits_a == 2 || bits_a == 3 || bits_a == 4 || bits_a == 6)))
         code_bytes = static_cast<size_t>(T) * static_cast<size_t>(d);
     else if (mode == RTQ_CODEBOOK && (bits_a == 2 || bits_a == 4))
         code_bytes = static_cast<size_t>(T) * static_cast<size_t>(d) * static_cast<size_t>(bits_a) / 8;

@@ -16,6 +16,9 @@ enum RowOut : int {
     kRowCode2 = 4,    // 2-bit Lloyd-Max codes (packed) + row norm
     kRowLut4 = 5,     // 4-bit Lloyd-Max codes written as their int8 codebook values (1 byte each) + norm
     kRowLut2 = 6,     // 2-bit Lloyd-Max codes written as their int8 codebook values + norm
+    kRowCode3 = 7,    // 3-bit Lloyd-Max codes (packed bit stream, 8 codes per 3 bytes) + row norm
+    kRowLut3 = 8,     // 3-bit codes written as their int8 codebook values + norm
+    kRowLut6 = 9,     // 6-bit codes written as their int8 codebook values + norm
 };
 
 struct RowArgs {

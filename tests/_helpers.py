@@ -59,3 +59,21 @@ def rel_fro(a, b):
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def int8_table(centroids):
+    """(S, v) with S = fl32(127 / max|c|) and v_k = rint(fl32(c_k * S)) as int8 (the int8 codebook
+    rule of include/rtq.h, computed with numpy fp32 arithmetic, independently of the library)."""
+    c = np.asarray(centroids, np.float32)
+    s = np.float32(127.0) / np.max(np.abs(c))
+    v = np.rint(c * s).astype(np.int8)
+    return s, v
+
+
+def codes_of(values, table):
+    """Invert the (injective) table: int8 values -> codes."""
+    lookup = {int(v): k for k, v in enumerate(table)}
+    assert len(lookup) == len(table)
+    flat = np.array([lookup.get(int(v), -1) for v in values.ravel()], np.int64)
+    assert (flat >= 0).all(), "value outside the codebook table"
+    return flat.reshape(values.shape)

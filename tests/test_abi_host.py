@@ -108,7 +108,12 @@ def test_quantize_rows_validation():
     assert call(rows=-1) == rtq.RTQ_ERR_INVALID_ARG
     assert call(cb=ctypes.byref(cb)) == rtq.RTQ_ERR_INVALID_ARG         # INT8 takes no codebook
     assert call(mode=rtq.RTQ_CODEBOOK) == rtq.RTQ_ERR_INVALID_ARG       # codebook missing
-    assert call(mode=rtq.RTQ_CODEBOOK, cb=ctypes.byref(_C(3, A, A))) == rtq.RTQ_ERR_UNSUPPORTED
+    assert call(mode=rtq.RTQ_CODEBOOK, cb=ctypes.byref(_C(5, A, A))) == rtq.RTQ_ERR_UNSUPPORTED   # no 5-bit codes
+    assert call(mode=rtq.RTQ_CODEBOOK, cb=ctypes.byref(_C(6, A, A))) == rtq.RTQ_ERR_UNSUPPORTED   # 6-bit: int8 values only
+    # 3- and 6-bit codes come from the bf16 rotate-quantise kernels only
+    assert call(mode=rtq.RTQ_CODEBOOK, cb=ctypes.byref(_C(3, A, A)), xt=rtq.RTQ_F32) == rtq.RTQ_ERR_UNSUPPORTED
+    assert call(mode=rtq.RTQ_CODEBOOK, cb=ctypes.byref(_C(3, A, A)), R=None) == rtq.RTQ_ERR_UNSUPPORTED
+    assert call(mode=rtq.RTQ_CODEBOOK_I8, cb=ctypes.byref(_C(6, A, A)), R=None) == rtq.RTQ_ERR_UNSUPPORTED
     assert call(mode=rtq.RTQ_CODEBOOK, cb=ctypes.byref(cb), eps=-1.0) == rtq.RTQ_ERR_INVALID_ARG
     assert call(mode=7) == rtq.RTQ_ERR_INVALID_ARG
     R_bad_h = _R(256, 32, A, A)
@@ -140,6 +145,10 @@ def test_qgemm_and_qlinear_validation():
     assert call({8: rtq.RTQ_CODEBOOK, 9: ctypes.byref(cb2), 10: ctypes.byref(cb2)}) == rtq.RTQ_ERR_UNSUPPORTED
     assert call({8: rtq.RTQ_CODEBOOK, 9: ctypes.byref(cb4), 10: ctypes.byref(cb2), 12: rtq.RTQ_I32}) == \
         rtq.RTQ_ERR_UNSUPPORTED
+    cb3, cb6 = _C(3, A, A), _C(6, A, A)
+    assert call({8: rtq.RTQ_CODEBOOK, 9: ctypes.byref(cb4), 10: ctypes.byref(cb3)}) == rtq.RTQ_ERR_UNSUPPORTED
+    assert call({8: rtq.RTQ_CODEBOOK_I8, 9: ctypes.byref(cb4), 10: ctypes.byref(cb6)}) == rtq.RTQ_ERR_UNSUPPORTED
+    assert call({8: rtq.RTQ_CODEBOOK_I8, 9: ctypes.byref(cb6), 10: ctypes.byref(cb3), 2: 0}) == rtq.RTQ_OK
     assert call({2: 0}) == rtq.RTQ_OK                                    # T = 0 is a no-op
     # workspace sizing and checks of the fused call
     ws = lib.rtq_rotated_qlinear_workspace
@@ -150,6 +159,9 @@ def test_qgemm_and_qlinear_validation():
     assert ws(4608, 4096, rtq.RTQ_CODEBOOK_I8, 4) == 4608 * 4096 + 18432 + split256
     assert ws(4608, 4096, rtq.RTQ_CODEBOOK, 4) == 4608 * 2048 + 18432
     assert ws(10, 4096, rtq.RTQ_CODEBOOK, 3) == 0
+    assert ws(4608, 4096, rtq.RTQ_CODEBOOK_I8, 3) == ws(4608, 4096, rtq.RTQ_CODEBOOK_I8, 6) == \
+        ws(4608, 4096, rtq.RTQ_CODEBOOK_I8, 4)
+    assert ws(4608, 4096, rtq.RTQ_CODEBOOK_I8, 5) == 0
     R = _R(256, 64, A, A)
     ql = lib.rtq_rotated_qlinear
     args = [A, rtq.RTQ_BF16, 16, ctypes.byref(R), A, A, rtq.RTQ_BF16, 32, rtq.RTQ_INT8, None, None, A, rtq.RTQ_BF16,

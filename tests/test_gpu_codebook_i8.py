@@ -16,7 +16,7 @@ import pytest
 import oracle
 import rotation_then_quantize_amd as rtq
 import workloads
-from _helpers import bf16_host, codebook_mismatches_allowed, dense_pi, rel_fro, to_dev
+from _helpers import bf16_host, codebook_mismatches_allowed, codes_of, dense_pi, int8_table, rel_fro, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -27,23 +27,6 @@ torch = pytest.importorskip("torch")
 def _gpu():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     rtq.load_library()
-
-
-def int8_table(centroids):
-    """(S, v) with S = fl32(127 / max|c|) and v_k = rint(fl32(c_k * S)) as int8."""
-    c = np.asarray(centroids, np.float32)
-    s = np.float32(127.0) / np.max(np.abs(c))
-    v = np.rint(c * s).astype(np.int8)
-    return s, v
-
-
-def codes_of(values, table):
-    """Invert the (injective) table: int8 values -> codes."""
-    lookup = {int(v): k for k, v in enumerate(table)}
-    assert len(lookup) == len(table)
-    flat = np.array([lookup.get(int(v), -1) for v in values.ravel()], np.int64)
-    assert (flat >= 0).all(), "value outside the codebook table"
-    return flat.reshape(values.shape)
 
 
 def test_int8_tables_are_injective_and_symmetric():
