@@ -69,6 +69,10 @@ def _load():
     lib.orc_to_bf16.restype = None
     lib.orc_quant_int8_rows.argtypes = [F32P, c_i64, c_i32, c_int, I8P, F32P, ctypes.c_void_p]
     lib.orc_quant_int8_rows.restype = None
+    lib.orc_quant_int8_asym_rows.argtypes = [F32P, c_i64, c_i32, c_int, I8P, F32P, I32P, I64P, ctypes.c_void_p]
+    lib.orc_quant_int8_asym_rows.restype = None
+    lib.orc_gemm_int8_asym.argtypes = [I8P, I32P, I8P, I32P, c_i64, c_i64, c_i32, I64P]
+    lib.orc_gemm_int8_asym.restype = None
     lib.orc_quant_codebook_rows.argtypes = [F32P, c_i64, c_i32, c_int, c_f32, c_i32, F32P, U8P, F32P,
                                             ctypes.c_void_p]
     lib.orc_quant_codebook_rows.restype = None
@@ -166,6 +170,29 @@ def quantize_int8(v: np.ndarray, scale_bf16: bool):
     pre = np.empty((rows, d), np.float32)
     _load().orc_quant_int8_rows(v, rows, d, 1 if scale_bf16 else 0, q, s, pre.ctypes.data)
     return q, s, pre
+
+
+def quantize_int8_asym(v: np.ndarray, scale_bf16: bool):
+    """Asymmetric per-row INT8 (scale + zero point, range widened to contain 0).
+    Returns (q int8, stored scale fp32, zero point int32, code sum int64, pre-rounding v/s)."""
+    v = _c(v, np.float32)
+    rows, d = v.shape
+    q = np.empty((rows, d), np.int8)
+    s = np.empty(rows, np.float32)
+    z = np.empty(rows, np.int32)
+    csum = np.empty(rows, np.int64)
+    pre = np.empty((rows, d), np.float32)
+    _load().orc_quant_int8_asym_rows(v, rows, d, 1 if scale_bf16 else 0, q, s, z, csum, pre.ctypes.data)
+    return q, s, z, csum, pre
+
+
+def gemm_int8_asym(qa: np.ndarray, za: np.ndarray, qw: np.ndarray, zw: np.ndarray) -> np.ndarray:
+    qa, qw = _c(qa, np.int8), _c(qw, np.int8)
+    T, d = qa.shape
+    N = qw.shape[0]
+    acc = np.empty((T, N), np.int64)
+    _load().orc_gemm_int8_asym(qa, _c(za, np.int32), qw, _c(zw, np.int32), T, N, d, acc)
+    return acc
 
 
 def quantize_codebook(v: np.ndarray, bounds: np.ndarray, is_weight: bool, eps: float = 1e-8):
@@ -289,6 +316,23 @@ def qlinear_int8(x: np.ndarray, pi: np.ndarray, wq: dict) -> dict:
     a = activations_int8(x, pi)
     acc = gemm_int8(a["q"], wq["q"])
     y = rescale_int8(acc, a["scale"], wq["scale"])
+    return {"act": a, "acc": acc, "y": y}
+
+
+def weights_int8_asym(w: np.ndarray, pi: np.ndarray, scale_bf16: bool):
+    """Offline: W' = W Pi^T, per-row asymmetric INT8."""
+    _, w_rot = rotate(w, pi)
+    q, s, z, csum, pre = quantize_int8_asym(w_rot, scale_bf16)
+    return {"rot": w_rot, "q": q, "scale": s, "zero": z, "sum": csum, "pre": pre}
+
+
+def qlinear_int8_asym(x: np.ndarray, pi: np.ndarray, wq: dict) -> dict:
+    """Online: x' = Pi x, per-token asymmetric INT8 (fp32 scale), the zero-point product, rescale."""
+    _, x_rot = rotate(x, pi)
+    q, s, z, csum, pre = quantize_int8_asym(x_rot, False)
+    a = {"rot": x_rot, "q": q, "scale": s, "zero": z, "sum": csum, "pre": pre}
+    acc = gemm_int8_asym(q, z, wq["q"], wq["zero"])
+    y = rescale_int8(acc, s, wq["scale"])
     return {"act": a, "acc": acc, "y": y}
 
 

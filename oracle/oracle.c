@@ -200,6 +200,69 @@ ORC_API void orc_quant_int8_rows(const float *v, int64_t rows, int32_t d, int sc
     }
 }
 
+/* Asymmetric INT8 rows: the scale-and-zero-point form of INT8 ([CR1] section 3 lists per-channel
+ * scales and zero points; [CR3] computes a scale and a zero-point offset), per row.  The range is
+ * widened to contain 0 so that 0 is an exact code: lo = min(min_j v_j, 0), hi = max(max_j v_j, 0),
+ * s = fl32(fl32(hi - lo) / 255), stored as bf16 for weights; with the STORED s,
+ * z = clamp(-128 - rne(fl32(lo / s)), -128, 127) and q_j = clamp(rne(fl32(v_j / s)) + z, -128, 127),
+ * so v_j ~ s (q_j - z).  s == 0 (an all-zero row) gives q = 0 and z = 0.  Outputs also the row's
+ * code sum and (optional) the pre-rounding fl32(v_j / s). */
+ORC_API void orc_quant_int8_asym_rows(const float *v, int64_t rows, int32_t d, int scale_is_bf16, int8_t *q,
+                                      float *scale_out, int32_t *zero_out, int64_t *sum_out, float *pre)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const float *vr = v + (size_t)r * d;
+        float lo = 0.0f, hi = 0.0f;
+        for (int32_t j = 0; j < d; ++j) {
+            if (vr[j] < lo) lo = vr[j];
+            if (vr[j] > hi) hi = vr[j];
+        }
+        float s = (hi - lo) / 255.0f;
+        if (scale_is_bf16) s = orc_bf16_value(orc_double_to_bf16((double)s));
+        int z = 0;
+        if (s != 0.0f) {
+            float zr = -128.0f - nearbyintf(lo / s);
+            if (zr > 127.0f) zr = 127.0f;
+            if (zr < -128.0f) zr = -128.0f;
+            z = (int)zr;
+        }
+        scale_out[r] = s;
+        zero_out[r] = z;
+        int64_t sum = 0;
+        for (int32_t j = 0; j < d; ++j) {
+            int code = 0;
+            float t = 0.0f;
+            if (s != 0.0f) {
+                t = vr[j] / s;
+                float rq = nearbyintf(t) + (float)z;
+                if (rq > 127.0f) rq = 127.0f;
+                if (rq < -128.0f) rq = -128.0f;
+                code = (int)rq;
+            }
+            q[(size_t)r * d + j] = (int8_t)code;
+            sum += code;
+            if (pre) pre[(size_t)r * d + j] = t;
+        }
+        sum_out[r] = sum;
+    }
+}
+
+/* The product of asymmetric codes, from its definition: acc[t][n] = sum_j (qa - za_t)(qw - zw_n),
+ * a naive int64 triple loop. */
+ORC_API void orc_gemm_int8_asym(const int8_t *qa, const int32_t *za, const int8_t *qw, const int32_t *zw,
+                                int64_t T, int64_t N, int32_t d, int64_t *acc)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t a = 0;
+            for (int32_t j = 0; j < d; ++j)
+                a += ((int64_t)qa[(size_t)t * d + j] - za[t]) * ((int64_t)qw[(size_t)n * d + j] - zw[n]);
+            acc[(size_t)t * N + n] = a;
+        }
+}
+
 /* Codebook rows ([OQ] section 2.1 steps 2-3 for weights, section 2.2 steps
  * 2-4 for activations).  The row's L2 norm is summed in double and rounded
  * once to fp32.  Weights (is_weight != 0): direction u = v / r in fp32

@@ -497,3 +497,71 @@ def test_lloyd_max_mse_matches_max_table(bits, mse):
     err = sum(scipy.integrate.quad(lambda x, ck=c[k]: (x - ck) ** 2 * scipy.stats.norm.pdf(x),
                                    edges[k], edges[k + 1])[0] for k in range(len(c)))
     assert abs(err - mse) < 2e-6
+
+
+# ---------------------------------------------------------------- asymmetric INT8 (zero points)
+
+def _asym_cases():
+    rng = np.random.default_rng(31)
+    v = rng.standard_normal((6, 512)).astype(np.float32)
+    v[1] = np.abs(v[1]) + 0.5          # all positive
+    v[2] = -np.abs(v[2]) * 3           # all negative
+    v[3] = 0.0                         # zero row
+    v[4] = 0.75                        # constant row
+    v[5] = rng.exponential(1.0, 512).astype(np.float32) - 0.2   # skewed
+    return v
+
+
+@pytest.mark.parametrize("scale_bf16", [False, True])
+def test_int8_asym_reconstruction_bounds(scale_bf16):
+    # [CR1] 3 / [CR3]: scale and zero point per row; v ~ s (q - z).  Zero is an exact code, the
+    # row minimum (or 0) maps to -128, codes stay in [-128, 127], and every element the clamp
+    # leaves alone is within s/2 of its reconstruction; clamped ends are within s.
+    v = _asym_cases()
+    q, s, z, csum, pre = oracle.quantize_int8_asym(v, scale_bf16)
+    assert q.dtype == np.int8 and np.all(z >= -128) and np.all(z <= 127)
+    assert np.array_equal(csum, q.astype(np.int64).sum(1))
+    if scale_bf16:
+        assert np.array_equal(oracle.bf16_bits_to_f32(oracle.to_bf16_bits(s)), s)
+    for r in range(v.shape[0]):
+        if s[r] == 0:
+            assert not v[r].any() and z[r] == 0 and not q[r].any()
+            continue
+        rec = s[r] * (q[r].astype(np.float64) - z[r])
+        err = np.abs(rec - v[r])
+        unclamped = np.rint(pre[r]) + z[r] == q[r]
+        assert np.all(err[unclamped] <= s[r] / 2 * (1 + 1e-6))
+        assert np.all(err <= s[r] * (1 + 1e-6))
+        lo = min(float(v[r].min()), 0.0)
+        assert q[r][v[r] == v[r].min()].min() == -128 or lo == 0.0
+    assert z[1] == -128                                     # lo = 0 for a positive row: 0 -> -128
+    assert z[2] == 127 and q[2].max() <= 127                # hi = 0 for a negative row: 0 -> 127
+    # the constant row 0.75: range [0, 0.75], every element at the top code, reconstructed exactly
+    assert np.all(q[4] == 127) and z[4] == -128 and np.allclose(s[4] * 255, 0.75, rtol=2 ** -8 if scale_bf16 else 1e-6)
+
+
+def test_int8_asym_product_equals_integer_definition_and_expansion():
+    rng = np.random.default_rng(32)
+    qa = rng.integers(-128, 128, size=(5, 192)).astype(np.int8)
+    qw = rng.integers(-128, 128, size=(7, 192)).astype(np.int8)
+    za = rng.integers(-128, 128, size=5).astype(np.int32)
+    zw = rng.integers(-128, 128, size=7).astype(np.int32)
+    acc = oracle.gemm_int8_asym(qa, za, qw, zw)
+    a64, w64 = qa.astype(np.int64), qw.astype(np.int64)
+    assert np.array_equal(acc, (a64 - za[:, None]) @ (w64 - zw[:, None]).T)
+    # the four-term form the product's epilogue uses
+    d = qa.shape[1]
+    expand = a64 @ w64.T - zw[None, :] * a64.sum(1)[:, None] - za[:, None] * w64.sum(1)[None, :] + \
+        d * za[:, None].astype(np.int64) * zw[None, :]
+    assert np.array_equal(acc, expand)
+
+
+def test_int8_asym_beats_symmetric_on_skewed_rows():
+    # a zero point spends all 256 levels on [lo, hi]: on one-sided rows the step halves
+    rng = np.random.default_rng(33)
+    v = (rng.exponential(1.0, size=(8, 1024))).astype(np.float32)
+    qs, ss, _ = oracle.quantize_int8(v, False)
+    qa, sa, za, _, _ = oracle.quantize_int8_asym(v, False)
+    e_sym = np.linalg.norm(ss[:, None] * qs - v)
+    e_asym = np.linalg.norm(sa[:, None] * (qa.astype(np.float64) - za[:, None]) - v)
+    assert e_asym < 0.6 * e_sym
