@@ -261,6 +261,51 @@ def bench_codebook(args, torch, rtq, workloads, variant, mode=None):
             "rpbh_frac_hbm": q_bytes / (quant_burst * 1e-3) / 1e9 / PEAK_HBM_GBPS}
 
 
+def bench_w8a8_asym(args, torch, rtq, workloads):
+    """The W8A8 DiT layer with asymmetric INT8 (a scale and a zero point per row) on both operands:
+    the zero-point quantiser (bf16 weight scales offline, fp32 token scales online) and the product
+    with its zero-point correction in the epilogue."""
+    d, N = workloads.DIT_HIDDEN, workloads.DIT_MLP
+    xh = workloads.dit_activations_bf16(d)
+    T = xh.shape[0]
+    R = rtq.Rpbh.from_seed(workloads.RPBH_SEED[d], d)
+    w = _bf16_dev(workloads.dit_weight_bf16("mlp_up"), torch)
+    wq = torch.empty((N, d), dtype=torch.int8, device="cuda")
+    ws_ = torch.empty(N, dtype=torch.bfloat16, device="cuda")
+    wz = torch.empty(N, dtype=torch.int32, device="cuda")
+    wsum = torch.empty(N, dtype=torch.int32, device="cuda")
+    rtq.quantize_rows_asym(w, wq, ws_, wz, wsum, R)
+    del w
+    xs = _copies(_bf16_dev(xh, torch), 512 << 20, torch)
+    codes = torch.empty((T, d), dtype=torch.int8, device="cuda")
+    scale = torch.empty(T, dtype=torch.float32, device="cuda")
+    zero = torch.empty(T, dtype=torch.int32, device="cuda")
+    csum = torch.empty(T, dtype=torch.int32, device="cuda")
+    y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    split_ws = torch.empty(rtq.qgemm_workspace(), dtype=torch.uint8, device="cuda")
+
+    def quant(i):
+        rtq.quantize_rows_asym(xs[i % len(xs)], codes, scale, zero, csum, R)
+
+    def gemm(i):
+        rtq.qgemm_asym(codes, scale, zero, csum, wq, ws_, wz, wsum, y, d, workspace=split_ws)
+
+    _prewarm(lambda i: (quant(i), gemm(i)), torch, 0.25)
+    for i in range(args.warmup):
+        quant(i)
+        gemm(i)
+    steps = max(5, args.steps // 2)
+    wall, tq, tg = _time_pairs(steps, quant, gemm, torch)
+    quant_burst = _burst_ms(max(20, steps), quant, torch)
+    flops = 2.0 * T * d * N
+    q_bytes = T * (2 * d + d + 12)
+    return {"T": T, "d": d, "N": N, "step_ms": wall * 1e3 / steps, "quant_ms": quant_burst,
+            "quant_event_span_ms": float(tq.mean()), "gemm_ms": float(tg.mean()),
+            "TFLOP/s": flops / (wall / steps) / 1e12, "gemm_TFLOP/s": flops / (tg.mean() * 1e-3) / 1e12,
+            "gemm_frac_peak": flops / (tg.mean() * 1e-3) / 1e12 / PEAK_INT8_TOPS,
+            "rpbh_bytes": q_bytes, "rpbh_GB/s": q_bytes / (quant_burst * 1e-3) / 1e9}
+
+
 def bench_ablation(args, torch, rtq, workloads):
     """The transform ablation at the W8A8 DiT shape (OrbitQuant article, sections 2.3 and 3.3): RPBH
     against block Hadamard without the permutation (perm = identity, same signs) and against a dense
@@ -435,7 +480,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
-    ap.add_argument("--only", choices=["w8a8", "codebook", "ablation", "all"], default="all",
+    ap.add_argument("--only", choices=["w8a8", "codebook", "ablation", "asym", "all"], default="all",
                     help="w8a8: time only the headline step (profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain streaming kernel of known size (bitwise_not over 256 MiB of int8, "
@@ -467,6 +512,9 @@ def main():
             torch.bitwise_not(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
+    if args.only == "asym":
+        print(json.dumps(bench_w8a8_asym(args, torch, rtq, workloads)))
+        return
     if args.only == "ablation":
         print(json.dumps(bench_ablation(args, torch, rtq, workloads)))
         return
@@ -488,6 +536,7 @@ def main():
                                                                              rtq.RTQ_CODEBOOK)
         extra["w3a3_dit_attn_out_4608x4096x4096"] = bench_codebook(args, torch, rtq, workloads, "w3a3")
         extra["w4a6_dit_attn_out_4608x4096x4096"] = bench_codebook(args, torch, rtq, workloads, "w4a6")
+        extra["w8a8_asym_dit_mlp_up_4608x4096x16384"] = bench_w8a8_asym(args, torch, rtq, workloads)
         extra["transform_ablation"] = bench_ablation(args, torch, rtq, workloads)
     cpu = None
     if not args.no_cpu_baseline:

@@ -187,6 +187,40 @@ rtq_status rtq_rotated_qlinear(const void* x, rtq_dtype xt, int64_t T, const rtq
  * bits_a is ignored for RTQ_INT8.  Returns 0 for invalid arguments. */
 size_t rtq_rotated_qlinear_workspace(int64_t T, int32_t d, rtq_qmode mode, int32_t bits_a);
 
+/* ---- Asymmetric INT8: a scale and a zero point per row (the scale-and-zero-point INT8 the pages
+ * name: "INT8旋转量化是什么" section 3 lists per-channel scales and zero points; the int8
+ * image-model page computes a scale and a zero-point offset).  With the range widened to contain 0,
+ * lo = min(min_j x'_j, 0), hi = max(max_j x'_j, 0): s = fl32(fl32(hi - lo) / 255) (stored as
+ * scale_t; the STORED value divides), z = clamp(-128 - rne(fl32(lo / s)), -128, 127),
+ * q_j = clamp(rne(fl32(x'_j / s)) + z, -128, 127), so x'_j ~ s (q_j - z); s == 0 gives q = 0, z = 0.
+ *   x [rows][d] BF16 (F32 rows are not supported: RTQ_ERR_UNSUPPORTED); R required (the rotation
+ *   as in rtq_quantize_rows).  codes int8[rows][d]; scale [rows] of scale_t (F32 or BF16);
+ *   zero int32[rows]; code_sum int32[rows] = sum_j q_j (the product's zero-point correction needs
+ *   it).  All DEVICE pointers, caller-owned; rows == 0 is a no-op. */
+rtq_status rtq_quantize_rows_asym(const void* x, rtq_dtype xt, int64_t rows, int32_t d, const rtq_rpbh* R,
+                                  int8_t* codes, void* scale, rtq_dtype scale_t, int32_t* zero, int32_t* code_sum,
+                                  void* stream);
+
+/* The product of asymmetric codes: acc[t][n] = sum_j (qa[t][j] - za[t]) (qw[n][j] - zw[n]), exact in
+ * int32 (evaluated as acc' - zw sum(qa) - za (sum(qw) - d zw) from the int8 products acc'), then
+ * y = acc * a_scale[t] * w_scale[n] in fp32, stored as yt (F32, BF16, or RTQ_I32 for acc itself).
+ * a_codes int8[T][d], a_scale fp32[T], a_zero/a_sum int32[T]; w_codes int8[N][d], w_scale [N] of
+ * w_scale_t, w_zero/w_sum int32[N]; workspace as for rtq_qgemm_ws (may be NULL). */
+rtq_status rtq_qgemm_asym(const int8_t* a_codes, const float* a_scale, const int32_t* a_zero, const int32_t* a_sum,
+                          int64_t T, const int8_t* w_codes, const void* w_scale, rtq_dtype w_scale_t,
+                          const int32_t* w_zero, const int32_t* w_sum, int64_t N, int32_t d, void* y, rtq_dtype yt,
+                          void* workspace, size_t ws_bytes, void* stream);
+
+/* The online asymmetric layer: rtq_quantize_rows_asym of x (fp32 token scales) into `workspace`, then
+ * rtq_qgemm_asym on the same stream.  workspace: at least rtq_rotated_qlinear_asym_workspace(T, R->d)
+ * bytes (codes, scales, zero points and code sums, each 256-byte aligned, then the product's
+ * K-split region; a workspace without that region is accepted and the product is not split). */
+rtq_status rtq_rotated_qlinear_asym(const void* x, rtq_dtype xt, int64_t T, const rtq_rpbh* R, const int8_t* w_codes,
+                                    const void* w_scale, rtq_dtype w_scale_t, const int32_t* w_zero,
+                                    const int32_t* w_sum, int64_t N, void* y, rtq_dtype yt, void* workspace,
+                                    size_t ws_bytes, void* stream);
+size_t rtq_rotated_qlinear_asym_workspace(int64_t T, int32_t d);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* rtq_last_error(void);
 

@@ -24,7 +24,8 @@ RTQ_INT8, RTQ_CODEBOOK, RTQ_CODEBOOK_I8 = 0, 1, 2
 
 EXPORTS = ("rtq_rpbh_make", "rtq_lloyd_max", "rtq_rpbh_rotate", "rtq_quantize_rows", "rtq_qgemm",
            "rtq_qgemm_ws", "rtq_qgemm_workspace", "rtq_rotated_qlinear", "rtq_rotated_qlinear_workspace",
-           "rtq_last_error")
+           "rtq_quantize_rows_asym", "rtq_qgemm_asym", "rtq_rotated_qlinear_asym",
+           "rtq_rotated_qlinear_asym_workspace", "rtq_last_error")
 
 
 class RtqError(RuntimeError):
@@ -68,10 +69,16 @@ def load_library():
     lib.rtq_rotated_qlinear.argtypes = [vp, i32, i64, R, vp, vp, i32, i64, i32, C, C, vp, i32, vp, sz, vp]
     lib.rtq_rotated_qlinear_workspace.argtypes = [i64, i32, i32, i32]
     lib.rtq_rotated_qlinear_workspace.restype = sz
+    lib.rtq_quantize_rows_asym.argtypes = [vp, i32, i64, i32, R, vp, vp, i32, vp, vp, vp]
+    lib.rtq_qgemm_asym.argtypes = [vp, vp, vp, vp, i64, vp, vp, i32, vp, vp, i64, i32, vp, i32, vp, sz, vp]
+    lib.rtq_rotated_qlinear_asym.argtypes = [vp, i32, i64, R, vp, vp, i32, vp, vp, i64, vp, i32, vp, sz, vp]
+    lib.rtq_rotated_qlinear_asym_workspace.argtypes = [i64, i32]
+    lib.rtq_rotated_qlinear_asym_workspace.restype = sz
     lib.rtq_last_error.argtypes = []
     lib.rtq_last_error.restype = ctypes.c_char_p
     for name in ("rtq_rpbh_make", "rtq_lloyd_max", "rtq_rpbh_rotate", "rtq_quantize_rows", "rtq_qgemm",
-                 "rtq_qgemm_ws", "rtq_rotated_qlinear"):
+                 "rtq_qgemm_ws", "rtq_rotated_qlinear", "rtq_quantize_rows_asym", "rtq_qgemm_asym",
+                 "rtq_rotated_qlinear_asym"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -247,4 +254,43 @@ def rotated_qlinear(x, R: Rpbh, w_codes, w_scale, y, mode: int = RTQ_INT8, cb_a:
                                               _dtype_code(w_scale), w_codes.shape[0], mode, _cb(cb_a), _cb(cb_w),
                                               _ptr(y), _dtype_code(y), _ptr(workspace), workspace.numel(),
                                               _stream(stream)))
+    return y
+
+
+# ------------------------------------------------------------------ asymmetric INT8
+
+def quantize_rows_asym(x, codes, scale, zero, code_sum, R: Rpbh, stream=None):
+    """Rotate and quantise each row with a scale and a zero point (int8 codes, scale, int32 zero
+    point, int32 code sum per row)."""
+    rows, d = x.shape
+    _check(load_library().rtq_quantize_rows_asym(_ptr(x), _dtype_code(x), rows, d, R.c, _ptr(codes), _ptr(scale),
+                                                 _dtype_code(scale), _ptr(zero), _ptr(code_sum), _stream(stream)))
+    return codes, scale, zero, code_sum
+
+
+def qgemm_asym(a_codes, a_scale, a_zero, a_sum, w_codes, w_scale, w_zero, w_sum, y, d: int, stream=None,
+               workspace=None):
+    """y = a_scale * w_scale * sum_j (qa - za)(qw - zw)."""
+    T, N = a_codes.shape[0], w_codes.shape[0]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().rtq_qgemm_asym(_ptr(a_codes), _ptr(a_scale), _ptr(a_zero), _ptr(a_sum), T, _ptr(w_codes),
+                                         _ptr(w_scale), _dtype_code(w_scale), _ptr(w_zero), _ptr(w_sum), N, d, _ptr(y),
+                                         _dtype_code(y), _ptr(workspace), ws_bytes, _stream(stream)))
+    return y
+
+
+def rotated_qlinear_asym_workspace(T: int, d: int) -> int:
+    return int(load_library().rtq_rotated_qlinear_asym_workspace(T, d))
+
+
+def rotated_qlinear_asym(x, R: Rpbh, w_codes, w_scale, w_zero, w_sum, y, workspace=None, stream=None):
+    """The online asymmetric layer: rotate + quantise x with zero points, then the zero-point product."""
+    torch = _torch()
+    T = x.shape[0]
+    if workspace is None:
+        workspace = torch.empty(max(rotated_qlinear_asym_workspace(T, R.d), 16), dtype=torch.uint8, device=x.device)
+    _check(load_library().rtq_rotated_qlinear_asym(_ptr(x), _dtype_code(x), T, R.c, _ptr(w_codes), _ptr(w_scale),
+                                                   _dtype_code(w_scale), _ptr(w_zero), _ptr(w_sum), w_codes.shape[0],
+                                                   _ptr(y), _dtype_code(y), _ptr(workspace), workspace.numel(),
+                                                   _stream(stream)))
     return y

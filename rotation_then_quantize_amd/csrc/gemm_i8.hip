@@ -205,13 +205,24 @@ __device__ __forceinline__ void tile_of(int lin, int tiles_m, int tiles_n, int* 
 constexpr int raw_stage_bytes(int w_bits) { return w_bits < 8 ? BN * BK * w_bits / 8 : 0; }
 constexpr int kRawSlots = 3;
 constexpr int lds_bytes(int w_bits) { return kLds + kRawSlots * raw_stage_bytes(w_bits); }
+// Asymmetric INT8 (int8 weights only): zero points and code sums of the tile's rows and columns,
+// two int32 arrays of BM + BN behind the scales (where coded weights keep their raw slots).
+constexpr int kAsymBytes = 2 * (BM + BN) * static_cast<int>(sizeof(int32_t));
 
-template <int kWavesN, int kYKind, bool kWScaleBF16, bool kVec, int kWBits>
+// Zero points and code sums of asymmetric INT8 operands (all null: symmetric codes).
+struct AsymArgs {
+    const int32_t* a_zero;   // [T]
+    const int32_t* a_sum;    // [T]  sum_j qa[t][j]
+    const int32_t* w_zero;   // [N]
+    const int32_t* w_sum;    // [N]  sum_j qw[n][j]
+};
+
+template <int kWavesN, int kYKind, bool kWScaleBF16, bool kVec, int kWBits, bool kAsym>
 __global__ void __launch_bounds__(64 * kWavesM * kWavesN, 1)
 gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, const int8_t* __restrict__ W,
                const void* __restrict__ w_scale, int64_t T, int64_t N, int d, void* __restrict__ Y,
                int tiles_m, int tiles_n, const float* __restrict__ cent_a, int a_bits,
-               const float* __restrict__ cent_w, SplitArgs sp) {
+               const float* __restrict__ cent_w, SplitArgs sp, AsymArgs za) {
     constexpr int kWaves = kWavesM * kWavesN;
     // kWBits < 8: W holds packed codebook codes; they are loaded into a ring of raw LDS slots two
     // stages ahead and decoded to int8 codebook values into the stage ring one stage ahead.
@@ -253,6 +264,9 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
     float* s_as = reinterpret_cast<float*>(lds + kRingBytes);
     float* s_ws = s_as + BM;
     int* s_flag = reinterpret_cast<int*>(s_ws + BN);
+    static_assert(!kAsym || !kCoded, "zero points with int8 weights only");
+    int* s_z = reinterpret_cast<int*>(lds + kLds);   // kAsym: zero points, rows then columns
+    int* s_e = s_z + BM + BN;                        // kAsym: sum_j qa (rows), sum_j qw - d zw (columns)
     const int nk_all = d / BK;
     int kbeg = 0, nk = nk_all;   // the current work item's K stages
 
@@ -363,8 +377,27 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
     // The tile's token scales (entries 0..255) and output-row scales (256..511), one or two per
     // thread, staged in LDS behind the ring for the epilogue.
     float sc[kScalesPerThread];
+    int zr[kScalesPerThread], er[kScalesPerThread];
     float alpha = 1.0f;   // codebook operands: 1 / (S_a S_w), folded into the token scales
     auto load_scales = [&]() {
+        if constexpr (kAsym) {
+#pragma unroll
+            for (int r = 0; r < kScalesPerThread; ++r) {
+                const int k = tid + r * kThreads;
+                zr[r] = 0;
+                er[r] = 0;
+                if (k < BM) {
+                    if (m0 + k < T) {
+                        zr[r] = za.a_zero[m0 + k];
+                        er[r] = za.a_sum[m0 + k];
+                    }
+                } else if (n0 + (k - BM) < N) {
+                    const int64_t n = n0 + (k - BM);
+                    zr[r] = za.w_zero[n];
+                    er[r] = za.w_sum[n] - d * zr[r];
+                }
+            }
+        }
         if (kYKind == 2) return;
 #pragma unroll
         for (int r = 0; r < kScalesPerThread; ++r) {
@@ -429,6 +462,13 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
         if (kYKind != 2) {
 #pragma unroll
             for (int r = 0; r < kScalesPerThread; ++r) s_as[tid + r * kThreads] = sc[r];   // s_ws follows s_as
+        }
+        if constexpr (kAsym) {
+#pragma unroll
+            for (int r = 0; r < kScalesPerThread; ++r) {
+                s_z[tid + r * kThreads] = zr[r];
+                s_e[tid + r * kThreads] = er[r];
+            }
         }
         // stages 0 and 1 (and codes 0..2) have landed, with everything issued before them
         // (e.g. the previous tile's stores); only stage 2 may be in flight
@@ -559,6 +599,21 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
             return v;
         };
 
+        // Zero points: sum_j (qa - za)(qw - zw) = acc - zw * sum(qa) - za * (sum(qw) - d zw), exact
+        // in int32 (24-bit multiplies: |zero| <= 128, |sums| <= 2^22).
+        auto correct = [&](v4i a, int row, int col) -> v4i {
+            if constexpr (kAsym) {
+                const int A = s_z[row], B = s_e[row];
+                const v4i C = *reinterpret_cast<const v4i*>(s_z + BM + col);
+                const v4i E = *reinterpret_cast<const v4i*>(s_e + BM + col);
+                a.x -= __mul24(C.x, B) + __mul24(A, E.x);
+                a.y -= __mul24(C.y, B) + __mul24(A, E.y);
+                a.z -= __mul24(C.z, B) + __mul24(A, E.z);
+                a.w -= __mul24(C.w, B) + __mul24(A, E.w);
+            }
+            return a;
+        };
+
         // ---- epilogue.  The MFMA computed the transposed tile (W fragment first), so a lane holds
         // D[n][t] at n = 8*(r/4) + 4*(lane/32) + r%4, t = lane % 32: four consecutive output columns
         // of one token row per group r/4.  Each wave copies its raw int32 block, 16 token rows at a
@@ -606,13 +661,14 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
                         const int8_t* src = stg + r * kPitch + c * kPerChunk * 4;
                         v4i out;
                         if (kYKind == 2) {
-                            out = add_others(*reinterpret_cast<const v4i*>(src), trow, col);
+                            out = correct(add_others(*reinterpret_cast<const v4i*>(src), trow, col), trow, col);
                         } else {
                             const float as = s_as[trow];
                             float y[kPerChunk];
 #pragma unroll
                             for (int h4 = 0; h4 < kPerChunk / 4; ++h4) {
-                                const v4i a = add_others(*reinterpret_cast<const v4i*>(src + 16 * h4), trow, col + 4 * h4);
+                                const v4i a = correct(add_others(*reinterpret_cast<const v4i*>(src + 16 * h4), trow, col + 4 * h4),
+                                                      trow, col + 4 * h4);
                                 const float4 ws = *reinterpret_cast<const float4*>(s_ws + col + 4 * h4);
                                 y[4 * h4 + 0] = static_cast<float>(a.x) * as * ws.x;
                                 y[4 * h4 + 1] = static_cast<float>(a.y) * as * ws.y;
@@ -665,22 +721,23 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
 // reused from another variant's sequence would read that launch's arrivals as this one's.
 std::atomic<unsigned int> g_split_epoch{0};
 
-template <int kWavesN, int kWBits>
+template <int kWavesN, int kWBits, bool kAsym>
 hipError_t launch_config(const GemmI8Args& g, hipStream_t stream) {
     using KernelFn = void (*)(const int8_t*, const float*, const int8_t*, const void*, int64_t, int64_t, int,
-                              void*, int, int, const float*, int, const float*, SplitArgs);
+                              void*, int, int, const float*, int, const float*, SplitArgs, AsymArgs);
     constexpr int kYKinds = kWBits == 8 ? 3 : 2;   // raw int32 output only for int8 weights
-    constexpr int kLdsBytes = lds_bytes(kWBits);
+    constexpr int kLdsBytes = lds_bytes(kWBits) + (kAsym ? kAsymBytes : 0);
+    static_assert(kLdsBytes <= 160 * 1024, "LDS");
     // [w_scale bf16][N % 8 == 0][y kind]
     static const KernelFn kernels[2][2][3] = {
-        {{gemm_i8_kernel<kWavesN, 0, false, false, kWBits>, gemm_i8_kernel<kWavesN, 1, false, false, kWBits>,
-          kYKinds > 2 ? gemm_i8_kernel<kWavesN, kYKinds - 1, false, false, kWBits> : nullptr},
-         {gemm_i8_kernel<kWavesN, 0, false, true, kWBits>, gemm_i8_kernel<kWavesN, 1, false, true, kWBits>,
-          kYKinds > 2 ? gemm_i8_kernel<kWavesN, kYKinds - 1, false, true, kWBits> : nullptr}},
-        {{gemm_i8_kernel<kWavesN, 0, true, false, kWBits>, gemm_i8_kernel<kWavesN, 1, true, false, kWBits>,
-          kYKinds > 2 ? gemm_i8_kernel<kWavesN, kYKinds - 1, true, false, kWBits> : nullptr},
-         {gemm_i8_kernel<kWavesN, 0, true, true, kWBits>, gemm_i8_kernel<kWavesN, 1, true, true, kWBits>,
-          kYKinds > 2 ? gemm_i8_kernel<kWavesN, kYKinds - 1, true, true, kWBits> : nullptr}}};
+        {{gemm_i8_kernel<kWavesN, 0, false, false, kWBits, kAsym>, gemm_i8_kernel<kWavesN, 1, false, false, kWBits, kAsym>,
+          kYKinds > 2 ? gemm_i8_kernel<kWavesN, kYKinds - 1, false, false, kWBits, kAsym> : nullptr},
+         {gemm_i8_kernel<kWavesN, 0, false, true, kWBits, kAsym>, gemm_i8_kernel<kWavesN, 1, false, true, kWBits, kAsym>,
+          kYKinds > 2 ? gemm_i8_kernel<kWavesN, kYKinds - 1, false, true, kWBits, kAsym> : nullptr}},
+        {{gemm_i8_kernel<kWavesN, 0, true, false, kWBits, kAsym>, gemm_i8_kernel<kWavesN, 1, true, false, kWBits, kAsym>,
+          kYKinds > 2 ? gemm_i8_kernel<kWavesN, kYKinds - 1, true, false, kWBits, kAsym> : nullptr},
+         {gemm_i8_kernel<kWavesN, 0, true, true, kWBits, kAsym>, gemm_i8_kernel<kWavesN, 1, true, true, kWBits, kAsym>,
+          kYKinds > 2 ? gemm_i8_kernel<kWavesN, kYKinds - 1, true, true, kWBits, kAsym> : nullptr}}};
     static const hipError_t attr_err = [] {
         hipError_t e = hipSuccess;
         for (auto& a : kernels)
@@ -732,7 +789,8 @@ hipError_t launch_config(const GemmI8Args& g, hipStream_t stream) {
     const KernelFn k = kernels[g.w_scale_bf16 ? 1 : 0][(g.N % 8) == 0 ? 1 : 0][g.y_kind];
     hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(64 * kWavesM * kWavesN), kLdsBytes, stream, g.a,
                        g.a_scale, g.w, g.w_scale, g.T, g.N, g.d, g.y, static_cast<int>(tiles_m),
-                       static_cast<int>(tiles_n), g.cent_a, g.a_bits, g.cent_w, sp);
+                       static_cast<int>(tiles_n), g.cent_a, g.a_bits, g.cent_w, sp,
+                       AsymArgs{g.a_zero, g.a_sum, g.w_zero, g.w_sum});
     return hipGetLastError();
 }
 
@@ -749,17 +807,21 @@ hipError_t launch_gemm_i8(const GemmI8Args& g, hipStream_t stream) {
     if (g.T <= 0 || g.N <= 0) return hipSuccess;
     if (g.d % BK != 0 || g.d > 16384) return hipErrorInvalidValue;
     if (g.N > (int64_t(1) << 22)) return hipErrorInvalidValue;   // 32-bit store offsets within a row block
+    const bool asym = g.a_zero != nullptr;
+    if (asym != (g.a_sum != nullptr) || asym != (g.w_zero != nullptr) || asym != (g.w_sum != nullptr))
+        return hipErrorInvalidValue;
+    if (asym) return g.w_bits == 8 ? launch_config<kDefaultWavesN, 8, true>(g, stream) : hipErrorInvalidValue;
     switch (g.w_bits) {
-        case 8: return launch_config<kDefaultWavesN, 8>(g, stream);
+        case 8: return launch_config<kDefaultWavesN, 8, false>(g, stream);
         case 4:
             if (g.cent_a == nullptr || g.cent_w == nullptr || g.a_bits < 1 || g.a_bits > 6) return hipErrorInvalidValue;
-            return launch_config<kDefaultWavesN, 4>(g, stream);
+            return launch_config<kDefaultWavesN, 4, false>(g, stream);
         case 3:
             if (g.cent_a == nullptr || g.cent_w == nullptr || g.a_bits < 1 || g.a_bits > 6) return hipErrorInvalidValue;
-            return launch_config<kDefaultWavesN, 3>(g, stream);
+            return launch_config<kDefaultWavesN, 3, false>(g, stream);
         case 2:
             if (g.cent_a == nullptr || g.cent_w == nullptr || g.a_bits < 1 || g.a_bits > 6) return hipErrorInvalidValue;
-            return launch_config<kDefaultWavesN, 2>(g, stream);
+            return launch_config<kDefaultWavesN, 2, false>(g, stream);
     }
     return hipErrorInvalidValue;
 }

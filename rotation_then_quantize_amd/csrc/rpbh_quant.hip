@@ -257,6 +257,14 @@ struct CodeCtx {
 struct BlockOut {
     uint32_t w[kH / 4];
     float s;
+    int32_t z;      // asymmetric INT8: the row's zero point
+    int32_t sum;    // asymmetric INT8: the row's code sum
+};
+
+// Extra per-row outputs of asymmetric INT8 rows (null otherwise).
+struct RowExtra {
+    int32_t* zero;
+    int32_t* sum;
 };
 
 // Bytes per output element (8 codes per 64 bits for 4-bit codes etc., in bits).
@@ -281,7 +289,78 @@ __device__ __forceinline__ void quantize_block(double (&acc)[kH], const unsigned
     constexpr int kBits = CodeCtx<kOut>::kBits;
     constexpr int kNB = CodeCtx<kOut>::kNB;
     uint32_t* w = res.w;
-    if (kOut == kRowInt8) {
+    if constexpr (kOut == kRowInt8Asym) {
+        // lo = min(min x', 0), hi = max(max x', 0): fl32(extremes of 8x' / 8) (rounding is monotone),
+        // reduced over the row; s = fl32(fl32(hi - lo) / 255) (then bf16 when stored so), and with
+        // the stored s: z = clamp(-128 - rne(fl32(lo / s)), -128, 127), q = clamp(rne(fl32(x'/s)) + z)
+        double mx4[kH / 4], mn4[kH / 4];
+#pragma unroll
+        for (int k = 0; k < kH / 4; ++k) {
+            mx4[k] = fmax(fmax(acc[4 * k], acc[4 * k + 1]), fmax(acc[4 * k + 2], acc[4 * k + 3]));
+            mn4[k] = fmin(fmin(acc[4 * k], acc[4 * k + 1]), fmin(acc[4 * k + 2], acc[4 * k + 3]));
+        }
+#pragma unroll
+        for (int k = 0; k < kH / 16; ++k) {
+            mx4[k] = fmax(fmax(mx4[4 * k], mx4[4 * k + 1]), fmax(mx4[4 * k + 2], mx4[4 * k + 3]));
+            mn4[k] = fmin(fmin(mn4[4 * k], mn4[4 * k + 1]), fmin(mn4[4 * k + 2], mn4[4 * k + 3]));
+        }
+        const double bmx = fmax(fmax(fmax(mx4[0], mx4[1]), fmax(mx4[2], mx4[3])), 0.0);
+        const double bmn = fmin(fmin(fmin(mn4[0], mn4[1]), fmin(mn4[2], mn4[3])), 0.0);
+        // three row reductions back to back: each crosses waves (d > 4096) through its own part of
+        // the reduction scratch (floats 0-3, floats 4-7, doubles 4-7), so none overwrites another's
+        // values while they are read
+        float* red_hi = reinterpret_cast<float*>(red);
+        float* red_lo = red ? reinterpret_cast<float*>(red) + 4 : nullptr;
+        double* red_sum = red ? red + 4 : nullptr;
+        const float hi = row_max(static_cast<float>(bmx * 0.125), log2nb, red_hi);
+        const float lo = -row_max(static_cast<float>(-bmn * 0.125), log2nb, red_lo);
+        float s = (hi - lo) / 255.0f;
+        if (scale_bf16) s = bf16_to_f32(f32_to_bf16(s));
+        int z = 0;
+        if (s != 0.0f) z = static_cast<int>(fminf(fmaxf(-128.0f - rintf(lo / s), -128.0f), 127.0f));
+        // the quotient as in the symmetric path (Markstein's correction step, then 1.5*2^23 rounds
+        // it half-to-even into the low mantissa bits); here the whole integer is taken, z added and
+        // the sum clamped
+        const float s8 = s * 8.0f;
+        const float r8 = 1.0f / s8;
+        constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+        const int zoff = z - 0x4B400000;       // bits of kMagic, subtracted back out
+        int csum = 0;
+#pragma unroll
+        for (int q = 0; q < kH / 4; ++q) {
+            int c[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const float y = static_cast<float>(acc[4 * q + p]);
+                const float q0 = y * r8;
+                const float q1 = fmaf(fmaf(-q0, s8, y), r8, q0);
+                c[p] = min(max(__float_as_int(q1 + kMagic) + zoff, -128), 127);
+                csum += c[p];
+            }
+            w[q] = (static_cast<uint32_t>(c[0]) & 0xffu) | ((static_cast<uint32_t>(c[1]) & 0xffu) << 8) |
+                   ((static_cast<uint32_t>(c[2]) & 0xffu) << 16) | (static_cast<uint32_t>(c[3]) << 24);
+        }
+        // fl32(8x')/(8s) equals x'/s while x' is normal; with hi - lo >= 2^-100 a subnormal x' has
+        // |x'/s| < 2^-17 and rounds to 0 either way.  Tinier rows take the exact path.
+        if (!(hi - lo >= 0x1p-100f)) {
+            csum = 0;
+#pragma unroll
+            for (int q = 0; q < kH / 4; ++q) w[q] = 0u;
+            if (s != 0.0f) {
+                double a2[kH];
+                load_block_fwht(block, a2);
+                for (int b = 0; b < kH; ++b) {
+                    const float xr = static_cast<float>(a2[b] * 0.125);
+                    const int code = static_cast<int>(fminf(fmaxf(rintf(xr / s) + static_cast<float>(z), -128.0f), 127.0f));
+                    csum += code;
+                    w[b >> 2] |= (static_cast<uint32_t>(code) & 0xffu) << ((b & 3) * 8);
+                }
+            }
+        }
+        res.s = s;
+        res.z = z;
+        res.sum = static_cast<int32_t>(row_sum(static_cast<double>(csum), log2nb, red_sum));
+    } else if constexpr (kOut == kRowInt8) {
         // amax = max |x'| = fl32(max |8x'| / 8) exactly (rounding is monotone), reduced over the row;
         // the block maximum as a tree (no serial chain of 64 dependent maxima)
         double m4[kH / 4];
@@ -426,7 +505,7 @@ __device__ __forceinline__ void quantize_block(double (&acc)[kH], const unsigned
 // Store a lane's quantised block (block `blk` of row `row`) and, from the row's first block, its scale.
 template <int kOut>
 __device__ __forceinline__ void store_block(const BlockOut& res, void* __restrict__ out, void* __restrict__ scale_out,
-                                            int scale_bf16, int64_t row, int blk, int d) {
+                                            int scale_bf16, RowExtra ex, int64_t row, int blk, int d) {
     constexpr int kWords = kH * out_bits<kOut>() / 32;
     if constexpr (kWords % 4 == 0) {
         uint4* o = reinterpret_cast<uint4*>(static_cast<uint8_t*>(out) + (row * d + blk * kH) * out_bits<kOut>() / 8);
@@ -442,6 +521,10 @@ __device__ __forceinline__ void store_block(const BlockOut& res, void* __restric
             static_cast<uint16_t*>(scale_out)[row] = static_cast<uint16_t>(f32_to_bf16(res.s));
         else
             static_cast<float*>(scale_out)[row] = res.s;
+        if constexpr (kOut == kRowInt8Asym) {
+            ex.zero[row] = res.z;
+            ex.sum[row] = res.sum;
+        }
     }
 }
 
@@ -451,7 +534,7 @@ __global__ void __launch_bounds__(kThreads, 2)
 rpbh_quant_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int log2d, int log2nb,
                        const int32_t* __restrict__ perm, const int8_t* __restrict__ signs, void* __restrict__ out,
                        void* __restrict__ scale_out, int scale_bf16, const float* __restrict__ bounds, float eps,
-                       const float* __restrict__ cent) {
+                       const float* __restrict__ cent, RowExtra ex) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     // LDS: [row buffer(s) | prologue scratch overlaid][sign masks, d x u16 (kNC >= 4)][reduction]
     // d <= 4096: two row buffers, so staging group g+1 never waits for readers of group g
@@ -594,7 +677,7 @@ rpbh_quant_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int 
 
         BlockOut res;
         quantize_block<kOut>(acc, buf + tid * kBlockPitch, log2nb, red, cc, bounds, eps, scale_bf16, res);
-        if (valid) store_block<kOut>(res, out, scale_out, scale_bf16, row, blk, d);
+        if (valid) store_block<kOut>(res, out, scale_out, scale_bf16, ex, row, blk, d);
         }
         if (kBufs == 1) __syncthreads();  // every lane has read its block before the buffer is restaged
     }
@@ -614,7 +697,7 @@ __global__ void __launch_bounds__(kThreads, 2)
 rpbh_wave_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int log2d,
                       const int32_t* __restrict__ perm, const int8_t* __restrict__ signs, void* __restrict__ out,
                       void* __restrict__ scale_out, int scale_bf16, const float* __restrict__ bounds, float eps,
-                      const float* __restrict__ cent) {
+                      const float* __restrict__ cent, RowExtra ex) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     // LDS: [scatter offset of each source column, u32[d]][its sign mask, u16[d]][one buffer per wave]
     uint32_t* tab_off = reinterpret_cast<uint32_t*>(smem);
@@ -689,7 +772,7 @@ rpbh_wave_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int l
                 *reinterpret_cast<uint16_t*>(rb + off[k]) =
                     static_cast<uint16_t>((k & 1) ? (w[k >> 1] >> 16) : (w[k >> 1] & 0xffffu));
         }
-        if (res_row >= 0 && res_row < rows) store_block<kOut>(res, out, scale_out, scale_bf16, res_row, blk, d);
+        if (res_row >= 0 && res_row < rows) store_block<kOut>(res, out, scale_out, scale_bf16, ex, res_row, blk, d);
         if (u + nwaves < units) load_unit(u + nwaves);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the unit is staged (this wave's LDS writes)
 
@@ -699,7 +782,7 @@ rpbh_wave_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int l
         res_row = u * (kUnit >> log2d) + (lane >> log2nb);
         asm volatile("" ::: "memory");   // this unit's block reads precede the next unit's staging
     }
-    if (res_row >= 0 && res_row < rows) store_block<kOut>(res, out, scale_out, scale_bf16, res_row, blk, d);
+    if (res_row >= 0 && res_row < rows) store_block<kOut>(res, out, scale_out, scale_bf16, ex, res_row, blk, d);
 }
 
 template <int kOut>
@@ -714,7 +797,7 @@ hipError_t launch_wave(const RowArgs& a, int log2d, hipStream_t stream) {
     const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(cap, (units + kThreads / 64 - 1) / (kThreads / 64)));
     hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), lds, stream,
                        static_cast<const uint16_t*>(a.x), a.rows, a.d, log2d, a.perm, a.signs, a.out, a.scale,
-                       a.scale_bf16 ? 1 : 0, a.bounds, a.eps, a.centroids);
+                       a.scale_bf16 ? 1 : 0, a.bounds, a.eps, a.centroids, RowExtra{a.zero, a.sum});
     return hipGetLastError();
 }
 
@@ -736,7 +819,7 @@ hipError_t launch_t(const RowArgs& a, int log2d, hipStream_t stream) {
     const int grid = static_cast<int>((ngroups + per_wg - 1) / per_wg);
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), lds, stream, static_cast<const uint16_t*>(a.x), a.rows,
                        a.d, log2d, log2nb, a.perm, a.signs, a.out, a.scale, a.scale_bf16 ? 1 : 0, a.bounds, a.eps,
-                       a.centroids);
+                       a.centroids, RowExtra{a.zero, a.sum});
     return hipGetLastError();
 }
 
@@ -754,7 +837,7 @@ hipError_t launch_nc(const RowArgs& a, int log2d, hipStream_t stream) {
 
 bool rpbh_quant_bf16_supported(const RowArgs& a) {
     return a.x_bf16 && a.perm != nullptr &&
-           (a.out_kind == kRowInt8 || a.out_kind == kRowCode4 || a.out_kind == kRowCode2 ||
+           (a.out_kind == kRowInt8 || a.out_kind == kRowInt8Asym || a.out_kind == kRowCode4 || a.out_kind == kRowCode2 ||
             a.out_kind == kRowLut4 || a.out_kind == kRowLut2 || a.out_kind == kRowCode3 ||
             a.out_kind == kRowLut3 || a.out_kind == kRowLut6) && a.d >= 64 &&
            a.d <= kMaxD;
@@ -766,6 +849,7 @@ hipError_t launch_rpbh_quant_bf16(const RowArgs& a, hipStream_t stream) {
     while ((1 << log2d) < a.d) ++log2d;
     switch (a.out_kind) {
         case kRowInt8: return launch_nc<kRowInt8>(a, log2d, stream);
+        case kRowInt8Asym: return launch_nc<kRowInt8Asym>(a, log2d, stream);
         case kRowCode4: return launch_nc<kRowCode4>(a, log2d, stream);
         case kRowCode2: return launch_nc<kRowCode2>(a, log2d, stream);
         case kRowLut4: return launch_nc<kRowLut4>(a, log2d, stream);

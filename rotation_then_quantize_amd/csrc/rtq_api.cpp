@@ -216,6 +216,31 @@ size_t workspace_bytes(int64_t T, int32_t d, rtq_qmode mode, int32_t bits_a, boo
            (with_split && mode != RTQ_CODEBOOK ? align256(rtq::gemm_i8_workspace_bytes()) : 0);
 }
 
+
+rtq_status plan_gemm_asym(const int8_t* a_codes, const float* a_scale, const int32_t* a_zero, const int32_t* a_sum,
+                          int64_t T, const int8_t* w_codes, const void* w_scale, rtq_dtype w_scale_t,
+                          const int32_t* w_zero, const int32_t* w_sum, int64_t N, int32_t d, void* y, rtq_dtype yt,
+                          GemmPlan* p) {
+    RTQ_TRY(plan_gemm(a_codes, a_scale, T, w_codes, w_scale, w_scale_t, N, d, RTQ_INT8, nullptr, nullptr, y, yt, p));
+    const int32_t* ptrs[4] = {a_zero, a_sum, w_zero, w_sum};
+    for (const int32_t* q : ptrs) {
+        if (q == nullptr) return fail(RTQ_ERR_INVALID_ARG, "zero point or code sum pointer is NULL");
+        if (reinterpret_cast<uintptr_t>(q) % 4 != 0) return fail(RTQ_ERR_MISALIGNED, "zero/sum array not 4-byte aligned");
+    }
+    p->i8.a_zero = a_zero;
+    p->i8.a_sum = a_sum;
+    p->i8.w_zero = w_zero;
+    p->i8.w_sum = w_sum;
+    return RTQ_OK;
+}
+
+size_t asym_workspace_bytes(int64_t T, int32_t d, bool with_split) {
+    if (T < 0 || d <= 0) return 0;
+    const size_t rows = static_cast<size_t>(T);
+    return align256(rows * static_cast<size_t>(d)) + 3 * align256(rows * 4) +
+           (with_split ? align256(rtq::gemm_i8_workspace_bytes()) : 0);
+}
+
 }  // namespace
 
 extern "C" {
@@ -343,6 +368,82 @@ rtq_status rtq_rotated_qlinear(const void* x, rtq_dtype xt, int64_t T, const rtq
     const size_t split_off = align256(code_bytes) + align256(static_cast<size_t>(T) * sizeof(float));
     gp.i8.workspace = ws + split_off;
     gp.i8.ws_bytes = ws_bytes - split_off;
+    return hip_status(rtq::launch_gemm_i8(gp.i8, s), "gemm_i8 launch");
+}
+
+// ---- asymmetric INT8 (scale + zero point per row)
+
+rtq_status rtq_quantize_rows_asym(const void* x, rtq_dtype xt, int64_t rows, int32_t d, const rtq_rpbh* R,
+                                  int8_t* codes, void* scale, rtq_dtype scale_t, int32_t* zero, int32_t* code_sum,
+                                  void* stream) {
+    rtq::RowArgs a{};
+    RTQ_TRY(plan_quantize(x, xt, rows, d, R, RTQ_INT8, nullptr, 0.0f, codes, scale, scale_t, &a));
+    if (R == nullptr || xt != RTQ_BF16)
+        return fail(RTQ_ERR_UNSUPPORTED, "asymmetric INT8 needs BF16 rows and a rotation descriptor");
+    if (zero == nullptr || code_sum == nullptr) return fail(RTQ_ERR_INVALID_ARG, "zero or code_sum is NULL");
+    if (reinterpret_cast<uintptr_t>(zero) % 4 != 0 || reinterpret_cast<uintptr_t>(code_sum) % 4 != 0)
+        return fail(RTQ_ERR_MISALIGNED, "zero or code_sum is not 4-byte aligned");
+    a.out_kind = rtq::kRowInt8Asym;
+    a.zero = zero;
+    a.sum = code_sum;
+    if (rows == 0) return ok();
+    return hip_status(rtq::launch_rpbh_rows(a, static_cast<hipStream_t>(stream)), "rpbh_rows launch");
+}
+
+
+rtq_status rtq_qgemm_asym(const int8_t* a_codes, const float* a_scale, const int32_t* a_zero, const int32_t* a_sum,
+                          int64_t T, const int8_t* w_codes, const void* w_scale, rtq_dtype w_scale_t,
+                          const int32_t* w_zero, const int32_t* w_sum, int64_t N, int32_t d, void* y, rtq_dtype yt,
+                          void* workspace, size_t ws_bytes, void* stream) {
+    GemmPlan p{};
+    RTQ_TRY(plan_gemm_asym(a_codes, a_scale, a_zero, a_sum, T, w_codes, w_scale, w_scale_t, w_zero, w_sum, N, d, y, yt,
+                           &p));
+    if (workspace != nullptr && reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+        return fail(RTQ_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+    if (T == 0) return ok();
+    p.i8.workspace = workspace;
+    p.i8.ws_bytes = workspace != nullptr ? ws_bytes : 0;
+    return hip_status(rtq::launch_gemm_i8(p.i8, static_cast<hipStream_t>(stream)), "gemm_i8 launch");
+}
+
+size_t rtq_rotated_qlinear_asym_workspace(int64_t T, int32_t d) { return asym_workspace_bytes(T, d, true); }
+
+rtq_status rtq_rotated_qlinear_asym(const void* x, rtq_dtype xt, int64_t T, const rtq_rpbh* R, const int8_t* w_codes,
+                                    const void* w_scale, rtq_dtype w_scale_t, const int32_t* w_zero,
+                                    const int32_t* w_sum, int64_t N, void* y, rtq_dtype yt, void* workspace,
+                                    size_t ws_bytes, void* stream) {
+    if (R == nullptr) return fail(RTQ_ERR_INVALID_ARG, "rpbh descriptor is NULL");
+    const int32_t d = R->d;
+    RTQ_TRY(check_d(d));
+    if (yt == RTQ_I32) return fail(RTQ_ERR_UNSUPPORTED, "rtq_rotated_qlinear_asym produces F32 or BF16 output");
+    const size_t need = asym_workspace_bytes(T < 0 ? 0 : T, d, false);
+    if (workspace == nullptr) return fail(RTQ_ERR_INVALID_ARG, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return fail(RTQ_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+    if (ws_bytes < need) return fail(RTQ_ERR_INVALID_ARG, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    const size_t rows = static_cast<size_t>(T < 0 ? 0 : T);
+    int8_t* a_codes = reinterpret_cast<int8_t*>(ws);
+    size_t off = align256(rows * static_cast<size_t>(d));
+    float* a_scale = reinterpret_cast<float*>(ws + off);
+    off += align256(rows * 4);
+    int32_t* a_zero = reinterpret_cast<int32_t*>(ws + off);
+    off += align256(rows * 4);
+    int32_t* a_sum = reinterpret_cast<int32_t*>(ws + off);
+    off += align256(rows * 4);
+    rtq::RowArgs qa{};
+    RTQ_TRY(plan_quantize(x, xt, T, d, R, RTQ_INT8, nullptr, 0.0f, a_codes, a_scale, RTQ_F32, &qa));
+    if (xt != RTQ_BF16) return fail(RTQ_ERR_UNSUPPORTED, "asymmetric INT8 needs BF16 rows");
+    qa.out_kind = rtq::kRowInt8Asym;
+    qa.zero = a_zero;
+    qa.sum = a_sum;
+    GemmPlan gp{};
+    RTQ_TRY(plan_gemm_asym(a_codes, a_scale, a_zero, a_sum, T, w_codes, w_scale, w_scale_t, w_zero, w_sum, N, d, y, yt,
+                           &gp));
+    if (T == 0) return ok();
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    RTQ_TRY(hip_status(rtq::launch_rpbh_rows(qa, s), "rpbh_rows launch"));
+    gp.i8.workspace = ws + off;
+    gp.i8.ws_bytes = ws_bytes - off;
     return hip_status(rtq::launch_gemm_i8(gp.i8, s), "gemm_i8 launch");
 }
 

@@ -19,6 +19,7 @@ enum RowOut : int {
     kRowCode3 = 7,    // 3-bit Lloyd-Max codes (packed bit stream, 8 codes per 3 bytes) + row norm
     kRowLut3 = 8,     // 3-bit codes written as their int8 codebook values + norm
     kRowLut6 = 9,     // 6-bit codes written as their int8 codebook values + norm
+    kRowInt8Asym = 10,  // asymmetric INT8 codes + per-row scale, zero point and code sum
 };
 
 struct RowArgs {
@@ -35,6 +36,8 @@ struct RowArgs {
     const float* bounds;    // codebook boundaries (device), 2^bits - 1 entries
     float eps;
     const float* centroids = nullptr;   // codebook centroids (device), 2^bits entries (kRowLut*)
+    int32_t* zero = nullptr;            // kRowInt8Asym: per-row zero point
+    int32_t* sum = nullptr;             // kRowInt8Asym: per-row sum of the codes
 };
 
 hipError_t launch_rpbh_rows(const RowArgs& a, hipStream_t stream);
@@ -69,6 +72,11 @@ struct GemmI8Args {
     const float* cent_a = nullptr;   // activation codebook centroids (device), 2^a_bits
     int a_bits = 0;
     const float* cent_w = nullptr;   // weight codebook centroids (device), 2^w_bits
+    // asymmetric INT8 (int8 weights): zero points and code sums of both operands, all or none
+    const int32_t* a_zero = nullptr;
+    const int32_t* a_sum = nullptr;
+    const int32_t* w_zero = nullptr;
+    const int32_t* w_sum = nullptr;
     // optional workspace (gemm_i8_workspace_bytes()): lets the last, partial round of tiles be
     // split along K over the otherwise idle CUs
     void* workspace = nullptr;

@@ -193,3 +193,46 @@ def test_product_path_has_no_oracle_or_fallback():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "oracle.c" not in text and "liboracle" not in text, f
+
+
+def test_asym_validation():
+    lib = rtq.load_library()
+    R = _R(256, 64, A, A)
+    q = lib.rtq_quantize_rows_asym
+    ok = [A, rtq.RTQ_BF16, 8, 256, ctypes.byref(R), A, A, rtq.RTQ_F32, A, A, None]
+
+    def call(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return q(*a)
+
+    assert call(a1=rtq.RTQ_F32) == rtq.RTQ_ERR_UNSUPPORTED          # bf16 rows only
+    assert call(a4=None) == rtq.RTQ_ERR_UNSUPPORTED                 # rotation required
+    assert call(a8=None) == rtq.RTQ_ERR_INVALID_ARG                 # zero points missing
+    assert call(a9=A + 2) == rtq.RTQ_ERR_MISALIGNED
+    assert call(a2=0) == rtq.RTQ_OK
+    g = lib.rtq_qgemm_asym
+    base = [A, A, A, A, 16, A, A, rtq.RTQ_BF16, A, A, 32, 256, A, rtq.RTQ_BF16, None, 0, None]
+
+    def gcall(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return g(*a)
+
+    assert gcall(a2=None) == rtq.RTQ_ERR_INVALID_ARG
+    assert gcall(a9=A + 1) == rtq.RTQ_ERR_MISALIGNED
+    assert gcall(a11=100) == rtq.RTQ_ERR_INVALID_ARG
+    assert gcall(a4=0) == rtq.RTQ_OK
+    ws = lib.rtq_rotated_qlinear_asym_workspace
+    split256 = (lib.rtq_qgemm_workspace() + 255) // 256 * 256
+    assert ws(4608, 4096) == 4608 * 4096 + 3 * 18432 + split256
+    ql = lib.rtq_rotated_qlinear_asym
+    args = [A, rtq.RTQ_BF16, 16, ctypes.byref(R), A, A, rtq.RTQ_BF16, A, A, 32, A, rtq.RTQ_BF16, A, 1 << 20, None]
+    a = list(args); a[13] = 16
+    assert ql(*a) == rtq.RTQ_ERR_INVALID_ARG and "workspace too small" in rtq.last_error()
+    a = list(args); a[1] = rtq.RTQ_F32
+    assert ql(*a) == rtq.RTQ_ERR_UNSUPPORTED
+    a = list(args); a[2] = 0
+    assert ql(*a) == rtq.RTQ_OK
