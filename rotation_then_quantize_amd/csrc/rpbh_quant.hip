@@ -553,11 +553,26 @@ rpbh_quant_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int 
 
     // ---- once per workgroup: inverse permutation and source-side signs.  All loads are issued
     //      before any LDS store so their latencies overlap.
-    // scatter addresses (LDS byte offsets < 65536); at d = 16384 they are kept as 16-bit pairs
-    constexpr bool kPackAddr = kNC >= 8;
-    uint32_t addr[kPackAddr ? kNC * 4 : kNC * 8];
+    // d = 16384: a thread's 64 scatter addresses would take 32 registers even as 16-bit pairs (and
+    // spill); there the table entry of a source column holds its slot's offset / 2 (15 bits) and
+    // its sign (bit 15), read with the chunk.  d <= 8192: addresses in registers, signs in LDS.
+    constexpr bool kTabAddr = kNC >= 8;
+    uint32_t addr[kTabAddr ? 1 : kNC * 8];
     uint4 msk[kMaskInLds ? 1 : kNC];
-    {
+    if constexpr (kTabAddr) {
+        for (int j = 4 * tid; j < d; j += 4 * kThreads) {
+            const int4 pv = *reinterpret_cast<const int4*>(perm + j);
+            const uint32_t sv = *reinterpret_cast<const uint32_t*>(signs + j);
+            const int pj[4] = {pv.x, pv.y, pv.z, pv.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t c = static_cast<uint32_t>(pj[e]) & dmask;
+                const uint32_t jj = static_cast<uint32_t>(j + e);
+                sg[c] = static_cast<uint16_t>(((jj >> 6) * (kBlockPitch / 2) + (jj & 63u)) |
+                                              ((sv >> (8 * e + 7)) & 1u ? 0x8000u : 0u));
+            }
+        }
+    } else {
         uint16_t* inv = reinterpret_cast<uint16_t*>(smem);     // overlays the row buffer
         constexpr int kPer = kMaxD / 4 / kThreads;             // int4 perm loads per thread at d = 16384
         int4 pv[kPer];
@@ -595,13 +610,7 @@ rpbh_quant_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int 
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 const uint32_t j = (k & 1) ? (iw[k >> 1] >> 16) : (iw[k >> 1] & 0xffffu);
-                const uint32_t a = row_base + (j >> 6) * kBlockPitch + (j & 63u) * 2u;
-                if (kPackAddr) {
-                    if (k & 1) addr[c * 4 + (k >> 1)] |= a << 16;
-                    else addr[c * 4 + (k >> 1)] = a;
-                } else {
-                    addr[c * 8 + k] = a;
-                }
+                addr[c * 8 + k] = row_base + (j >> 6) * kBlockPitch + (j & 63u) * 2u;
             }
             if (!kMaskInLds) msk[c] = *reinterpret_cast<const uint4*>(sg + col);
         }
@@ -651,14 +660,16 @@ rpbh_quant_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int 
             } else {
                 m = msk[i % kNC];
             }
-            const uint32_t w[4] = {pre[i].x ^ m.x, pre[i].y ^ m.y, pre[i].z ^ m.z, pre[i].w ^ m.w};
+            const uint32_t mw[4] = {m.x, m.y, m.z, m.w};
+            uint32_t w[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) w[q] = (&pre[i].x)[q] ^ (kTabAddr ? (mw[q] & 0x80008000u) : mw[q]);
             unsigned char* base = buf + (i - (i % kNC)) * kChunkStride;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 const uint16_t h = static_cast<uint16_t>((k & 1) ? (w[k >> 1] >> 16) : (w[k >> 1] & 0xffffu));
-                const uint32_t a = kPackAddr ? ((k & 1) ? (addr[(i % kNC) * 4 + (k >> 1)] >> 16)
-                                                        : (addr[(i % kNC) * 4 + (k >> 1)] & 0xffffu))
-                                             : addr[(i % kNC) * 8 + k];
+                const uint32_t a = kTabAddr ? ((k & 1) ? (mw[k >> 1] >> 15) & 0xfffeu : (mw[k >> 1] << 1) & 0xfffeu)
+                                            : addr[(i % kNC) * 8 + k];
                 *reinterpret_cast<uint16_t*>(base + a) = h;
             }
         }
