@@ -190,8 +190,19 @@ __device__ __forceinline__ double row_sum(double v, int log2nb, double* red) {
     return v;
 }
 
-// Per-lane codebook state for one launch: the lane's boundary slot, and (4-bit) the lane's cell of
-// the boundary grid; the int8 value table for kRowLut*.
+// Per-lane codebook state for one launch: the lane's boundary slot, the lane's cells of the
+// boundary grid, and the int8 value table for kRowLut*.
+//
+// Boundary grid (3, 4 and 6-bit codes).  kCells cells over u = x' / den: 2 * kHalfSpan of them
+// cover [-tmax, tmax] (tmax = the largest |boundary|) and the two end cells take everything
+// beyond.  Each cell is widened by a small slack, so a boundary near a cell edge belongs to both
+// neighbours, and the grid is used only if no widened cell holds two boundaries (true for the
+// Lloyd-Max tables of 8, 16 and 64 levels: their closest boundaries are 1.9 cells or more apart).  Per row, each wave
+// keeps an LDS table with one 8-byte entry per (row of the wave, cell): the exact threshold Y of
+// the cell's boundary (in x' units; +inf for none), rewritten per row, and the cell's info word,
+// written once by setup() (#{boundaries below the cell} | int8 value of that code << 8 | of the
+// next << 16 | slot of its boundary, kNB for none, << 24), so an element's code is
+// below + (x' >= Y) after one table read.
 template <int kOut>
 struct CodeCtx {
     static constexpr bool k4 = kOut == kRowCode4 || kOut == kRowLut4;
@@ -199,55 +210,78 @@ struct CodeCtx {
     static constexpr bool k3 = kOut == kRowCode3 || kOut == kRowLut3;
     static constexpr bool k6 = kOut == kRowLut6;
     static constexpr bool kLut = kOut == kRowLut4 || kOut == kRowLut2 || kOut == kRowLut3 || kOut == kRowLut6;
-    static constexpr bool kGrid = k4 || k3;   // boundary grid for 8 and 16 levels
+    static constexpr bool kGrid = k4 || k3 || k6;   // boundary grid for 8, 16 and 64 levels
     static constexpr int kBits = k4 ? 4 : (k2 ? 2 : (k3 ? 3 : (k6 ? 6 : 8)));
     static constexpr int kNB = (1 << kBits) - 1;
+    static constexpr int kCells = k6 ? 256 : 64;
+    static constexpr int kHalfSpan = k6 ? 100 : 20;          // cells per tmax
+    static constexpr int kPer = kCells / 64;                 // cells per lane
+    // LDS per wave for the table: rows of the wave x kCells x 8 bytes (up to 8 rows of 64 cells when
+    // rows are shorter than a wave; one row when a row spans waves)
+    static constexpr int kTabBytes = kGrid ? 4096 : 0;
+    static constexpr int kTabBytesRow = kGrid ? kCells * 8 : 0;
     int lane_base = 0;
     int kidx = 0;                 // my threshold slot
     float my_t = __builtin_inff();
     float tb[3] = {0.0f, 0.0f, 0.0f};
-    uint32_t cell = 0;
     float grid_k = 0.0f;
     bool use_grid = false;        // per lane here: the caller makes it uniform over the workgroup
-    bool use_bsearch = false;     // 64 levels: thresholds one per lane of a 64-lane row, binary search
-    uint32_t lut[4] = {0u, 0u, 0u, 0u};
-    int lutv = 0;                 // 64 levels: lane k holds the int8 value of code k
+    bool use_bsearch = false;     // 64 levels without the grid: binary search over lane-held thresholds
 
+    // ctab0: the first wave's table region; the workgroup computes the cell info words once, into
+    // its first row (fill() then copies them into every wave's rows, after a barrier)
     __device__ __forceinline__ void setup(const float* __restrict__ bounds, const float* __restrict__ cent,
-                                          int log2nb, int lane) {
+                                          int log2nb, int lane, uint2* ctab0) {
         const int row_lanes = (1 << log2nb) < 64 ? (1 << log2nb) : 64;   // lanes of my row in my wave
         lane_base = lane & ~(row_lanes - 1);
         kidx = lane - lane_base;
-        if (kLut && !k6) codebook_int8_table(cent, 1 << kBits, codebook_int8_scale(cent, 1 << kBits), lut);
-        if (k6) {
-            lutv = codebook_int8_value(cent, lane, codebook_int8_scale(cent, 64));
-            use_bsearch = row_lanes == 64;
-            if (use_bsearch && kidx < kNB) my_t = bounds[kidx];
-        }
+        constexpr int L = 1 << kBits;
         if (k2) {
 #pragma unroll
             for (int k = 0; k < 3; ++k) tb[k] = bounds[k];
         }
+        if (kGrid && kidx < kNB) my_t = bounds[kidx];
+        if (k6) use_bsearch = row_lanes == 64;
         if (kGrid) {
-            if (kidx < kNB) my_t = bounds[kidx];
-            // grid over [-tmax, tmax] with 40 cells of width tmax/20; 64 cells in all (end cells clamp)
+            const float vs = kLut ? codebook_int8_scale(cent, L) : 0.0f;
             const float tmax = fmaxf(fabsf(bounds[0]), fabsf(bounds[kNB - 1]));
             use_grid = row_lanes >= kNB + 1 && tmax > 0.0f;
             if (use_grid) {
-                grid_k = 20.0f / tmax;                 // cell units per unit of u
-                const int j = lane;                    // cell index, 0..63
-                const float slack = 1.0f / 1024.0f;    // in cell units: covers every rounding error
-                const float lo = (j == 0) ? -__builtin_inff() : (static_cast<float>(j - 32) - slack) / grid_k;
-                const float hi = (j == 63) ? __builtin_inff() : (static_cast<float>(j - 31) + slack) / grid_k;
-                int below = 0, inside = 0, kin = kNB;  // slot kNB holds +inf: "no boundary in this cell"
-                for (int k = 0; k < kNB; ++k) {
-                    const float t = bounds[k];
-                    if (t < lo) ++below;
-                    else if (t < hi) { ++inside; kin = k; }
+                grid_k = static_cast<float>(kHalfSpan) / tmax;   // cell units per unit of u
+                const float slack = 1.0f / 1024.0f;              // in cell units: covers every rounding error
+                static_assert(kCells <= kThreads, "one cell per thread");
+                for (int j = static_cast<int>(threadIdx.x); j < kCells; j += kThreads) {   // cell index
+                    const float lo = (j == 0) ? -__builtin_inff() : (static_cast<float>(j - kCells / 2) - slack) / grid_k;
+                    const float hi = (j == kCells - 1) ? __builtin_inff()
+                                                       : (static_cast<float>(j - kCells / 2 + 1) + slack) / grid_k;
+                    int below = 0, inside = 0, kin = kNB;
+                    for (int k = 0; k < kNB; ++k) {
+                        const float t = bounds[k];
+                        if (t < lo) ++below;
+                        else if (t < hi) { ++inside; kin = k; }
+                    }
+                    if (inside > 1) use_grid = false;
+                    uint32_t v = 0u;
+                    if (kLut) {
+                        v = (static_cast<uint32_t>(codebook_int8_value(cent, below, vs)) & 0xffu) << 8;
+                        if (below + 1 < L) v |= (static_cast<uint32_t>(codebook_int8_value(cent, below + 1, vs)) & 0xffu) << 16;
+                    }
+                    ctab0[j].y = static_cast<uint32_t>(below) | v | (static_cast<uint32_t>(kin) << 24);
                 }
-                if (inside > 1) use_grid = false;
-                cell = (static_cast<uint32_t>(below) << 8) | (4u * static_cast<uint32_t>(kin));
             }
+        }
+    }
+
+    // After setup() and a barrier (with use_grid made uniform): the info words into every row of
+    // this wave's table (the first wave's first row already holds them).
+    __device__ __forceinline__ void fill(int log2nb, int lane, uint2* ctab, const uint2* ctab0) const {
+        if (!kGrid || !use_grid) return;
+        const int row_lanes = (1 << log2nb) < 64 ? (1 << log2nb) : 64;
+        const bool first = ctab == ctab0;
+#pragma unroll
+        for (int p = 0; p < kPer; ++p) {
+            const uint32_t ci = ctab0[lane + 64 * p].y;
+            for (int r = first ? 1 : 0; r < 64 / row_lanes; ++r) ctab[r * kCells + lane + 64 * p].y = ci;
         }
     }
 };
@@ -275,12 +309,13 @@ constexpr int out_bits() {
 
 // Quantise a lane's rotated block (acc = 8 x' in fp64: the lane's 64 outputs of its row) with the
 // row's scale or norm, reduced over the row's lanes.  Every lane of the workgroup calls this
-// together when rows span several waves (log2nb > 6).
+// together when rows span several waves (log2nb > 6).  ctab: this wave's LDS region for the
+// boundary-grid table (CodeCtx::kTabBytes).
 template <int kOut>
 __device__ __forceinline__ void quantize_block(double (&acc)[kH], const unsigned char* block, int log2nb,
-                                               double* red, const CodeCtx<kOut>& cc,
-                                               const float* __restrict__ bounds, float eps, int scale_bf16,
-                                               BlockOut& res) {
+                                               double* red, uint2* ctab, const CodeCtx<kOut>& cc,
+                                               const float* __restrict__ bounds, const float* __restrict__ cent,
+                                               float eps, int scale_bf16, BlockOut& res) {
     constexpr bool k4 = CodeCtx<kOut>::k4;
     constexpr bool k2 = CodeCtx<kOut>::k2;
     constexpr bool k3 = CodeCtx<kOut>::k3;
@@ -428,19 +463,61 @@ __device__ __forceinline__ void quantize_block(double (&acc)[kH], const unsigned
         const float s = static_cast<float>(sqrt(ss));
         const float den = (eps == 0.0f) ? s : s + eps;
         // codes as one LSB-first bit stream of kSlot-bit fields: packed codes (2, 3, 4 bits), or one
-        // byte per code before the int8 table lookup (6-bit codes are looked up as they are found)
+        // byte per code (kRowLut*: its int8 value; the grid table holds the values, the other paths
+        // look codes up afterwards, or as they are found for 6-bit codes)
         constexpr int kSlot = kLut ? 8 : kBits;
         constexpr int kWords = kH * kSlot / 32;
-        auto put = [&](int b, uint32_t code) {
-            if constexpr (k6) code = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(static_cast<int>(4 * code), cc.lutv)) & 0xffu;
+        auto put_bits = [&](int b, uint32_t v) {
             const int p = b * kSlot, q = p >> 5, sh = p & 31;
-            w[q] |= code << sh;
-            if (sh + kSlot > 32) w[q + 1] |= code >> (32 - sh);
+            w[q] |= v << sh;
+            if (sh + kSlot > 32) w[q + 1] |= v >> (32 - sh);
         };
+        // 64 levels off the grid: lane k holds the int8 value of code k
+        const int lutv = k6 && !cc.use_grid ? codebook_int8_value(cent, threadIdx.x & 63, codebook_int8_scale(cent, 64)) : 0;
+        auto put = [&](int b, uint32_t code) {
+            if constexpr (k6) code = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(static_cast<int>(4 * code), lutv)) & 0xffu;
+            put_bits(b, code);
+        };
+        bool values_done = false;   // the words already hold int8 values
 #pragma unroll
         for (int q = 0; q < kWords; ++q) w[q] = 0u;
-        if (den != 0.0f) {
-            // u = fl32(x'/den); code = #{k : t_k < u} = #{k : x' >= Y_k}, Y_k exact per row
+        // u = fl32(x'/den); code = #{k : t_k < u} = #{k : x' >= Y_k}, Y_k exact per row
+        if (CodeCtx<kOut>::kGrid && cc.use_grid) {
+            // Every lane of the wave takes part (table entries of one row are written by lanes
+            // of every row, and cross-lane reads see only active lanes), so a row with
+            // den = 0 runs here too, with den = 1: its x' are all zero, and x' = 0 against the
+            // thresholds for den = 1 gives #{k : t_k < 0}, the code of u = 0.
+            const float dn = den != 0.0f ? den : 1.0f;
+            // my slot holds Y_kidx; the wave's table gets one entry per (row of the wave, cell)
+            const float myY = cc.kidx < kNB ? exact_threshold(cc.my_t, dn) : __builtin_inff();
+            constexpr int kCells = CodeCtx<kOut>::kCells;
+            const int row_lanes = log2nb < 6 ? 1 << log2nb : 64;
+            for (int r = 0; r < 64 / row_lanes; ++r) {
+#pragma unroll
+                for (int p = 0; p < CodeCtx<kOut>::kPer; ++p) {
+                    uint2* ent = ctab + r * kCells + 64 * p + (threadIdx.x & 63);
+                    const int slot = static_cast<int>(ent->y >> 24);
+                    const float y = __int_as_float(__builtin_amdgcn_ds_bpermute(
+                        4 * (r * row_lanes + (slot < kNB ? slot : 0)), __float_as_int(myY)));
+                    ent->x = __float_as_uint(slot < kNB ? y : __builtin_inff());
+                }
+            }
+            // (the wave's LDS accesses execute in order: its reads below see these writes)
+            const uint2* rt = ctab + (cc.lane_base / row_lanes) * kCells;
+            const float ka = 8.0f * cc.grid_k / dn;       // table bytes per unit of x'
+            constexpr float kMid = 4.0f * kCells, kTop = 8.0f * kCells - 1.0f;
+#pragma unroll
+            for (int b = 0; b < kH; ++b) {
+                const int a = static_cast<int>(__builtin_amdgcn_fmed3f(fmaf(xr[b], ka, kMid), 0.0f, kTop));
+                const uint2 e = rt[a >> 3];
+                const bool ge = xr[b] >= __uint_as_float(e.x);
+                if constexpr (kLut)
+                    put_bits(b, (e.y >> (ge ? 16 : 8)) & 0xffu);
+                else
+                    put_bits(b, (e.y & 0xffu) + (ge ? 1u : 0u));
+            }
+            values_done = kLut;
+        } else if (den != 0.0f) {
             if (k2) {
                 float Y[3];
 #pragma unroll
@@ -463,19 +540,6 @@ __device__ __forceinline__ void quantize_block(double (&acc)[kH], const unsigned
                     }
                     put(b, static_cast<uint32_t>(lo));
                 }
-            } else if (cc.use_grid) {
-                // my slot holds Y_kidx (slot 15: +inf); cells hold (#below << 8) | 4*slot
-                const float myY = cc.kidx < kNB ? exact_threshold(cc.my_t, den) : __builtin_inff();
-                const float ka = 4.0f * cc.grid_k / den;      // 4 * cc.cell units per unit of x'
-                const int base4 = 4 * cc.lane_base;
-#pragma unroll
-                for (int b = 0; b < kH; ++b) {
-                    const int a = static_cast<int>(__builtin_amdgcn_fmed3f(fmaf(xr[b], ka, 128.0f), 0.0f, 255.0f));
-                    const uint32_t e = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(a, static_cast<int>(cc.cell)));
-                    const float Yk = __int_as_float(__builtin_amdgcn_ds_bpermute(static_cast<int>(e) + base4, __float_as_int(myY)));
-                    const uint32_t code = (e >> 8) + (xr[b] >= Yk ? 1u : 0u);
-                    put(b, code);
-                }
             } else {
                 // a general codebook, or too few lanes per row for the slot table: divide and count
 #pragma unroll
@@ -493,10 +557,12 @@ __device__ __forceinline__ void quantize_block(double (&acc)[kH], const unsigned
 #pragma unroll
             for (int b = 0; b < kH; ++b) put(b, code);
         }
-        if (kLut && !k6) {
+        if (kLut && !k6 && !values_done) {
+            uint32_t lut[4];
+            codebook_int8_table(cent, 1 << kBits, codebook_int8_scale(cent, 1 << kBits), lut);
 #pragma unroll
             for (int q = 0; q < kWords; ++q)
-                w[q] = k4 ? lut16_x4(cc.lut, w[q]) : (k3 ? lut8_x4(cc.lut, w[q]) : lut4_x4(cc.lut, w[q]));
+                w[q] = k4 ? lut16_x4(lut, w[q]) : (k3 ? lut8_x4(lut, w[q]) : lut4_x4(lut, w[q]));
         }
         res.s = s;
     }
@@ -543,6 +609,9 @@ rpbh_quant_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int 
     constexpr int kBufs = kMaskInLds ? 1 : 2;
     uint16_t* sg = reinterpret_cast<uint16_t*>(smem + (kMaskInLds ? kRowBuf : 2 * d));
     double* red = reinterpret_cast<double*>(smem + kBufs * kRowBuf + (kMaskInLds ? 2 * d : 0));
+    // behind the reduction scratch: each wave's boundary-grid table (codebook kinds)
+    uint2* ctab0 = reinterpret_cast<uint2*>(smem + kBufs * kRowBuf + (kMaskInLds ? 2 * d : 0) + 64);
+    uint2* ctab = ctab0 + (threadIdx.x >> 6) * (CodeCtx<kOut>::kTabBytesRow / 8);   // a row spans waves: one row each
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -618,8 +687,9 @@ rpbh_quant_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int 
 
     // ---- codebook set-up
     CodeCtx<kOut> cc;
-    cc.setup(bounds, cent, log2nb, lane);
+    cc.setup(bounds, cent, log2nb, lane, ctab0);
     if (CodeCtx<kOut>::kGrid) cc.use_grid = __syncthreads_and(cc.use_grid ? 1 : 0) != 0;
+    cc.fill(log2nb, lane, ctab, ctab0);
 
     // This workgroup's rows: an even share [r_begin, r_end) of all rows, taken rpg rows per group
     // (the last group of the share may be partial), so every workgroup does the same work.
@@ -687,7 +757,7 @@ rpbh_quant_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int 
         const bool valid = row < r_end;
 
         BlockOut res;
-        quantize_block<kOut>(acc, buf + tid * kBlockPitch, log2nb, red, cc, bounds, eps, scale_bf16, res);
+        quantize_block<kOut>(acc, buf + tid * kBlockPitch, log2nb, red, ctab, cc, bounds, cent, eps, scale_bf16, res);
         if (valid) store_block<kOut>(res, out, scale_out, scale_bf16, ex, row, blk, d);
         }
         if (kBufs == 1) __syncthreads();  // every lane has read its block before the buffer is restaged
@@ -717,6 +787,8 @@ rpbh_wave_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int l
     const int lane = tid & 63;
     const int wave = tid >> 6;
     unsigned char* buf = smem + 6 * d + wave * kWaveBuf;
+    uint2* ctab0 = reinterpret_cast<uint2*>(smem + 6 * d + (kThreads / 64) * kWaveBuf);
+    uint2* ctab = ctab0 + wave * (CodeCtx<kOut>::kTabBytes / 8);
     const int log2nb = log2d - 6;
     const uint32_t dmask = static_cast<uint32_t>(d - 1);
 
@@ -735,8 +807,9 @@ rpbh_wave_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int l
         }
     }
     CodeCtx<kOut> cc;
-    cc.setup(bounds, cent, log2nb, lane);
+    cc.setup(bounds, cent, log2nb, lane, ctab0);
     if (CodeCtx<kOut>::kGrid) cc.use_grid = __syncthreads_and(cc.use_grid ? 1 : 0) != 0;
+    cc.fill(log2nb, lane, ctab, ctab0);
     __syncthreads();   // tables complete
 
     const int64_t total = rows * static_cast<int64_t>(d);
@@ -789,7 +862,7 @@ rpbh_wave_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int l
 
         double acc[kH];
         load_block_fwht(buf + lane * kBlockPitch, acc);
-        quantize_block<kOut>(acc, buf + lane * kBlockPitch, log2nb, nullptr, cc, bounds, eps, scale_bf16, res);
+        quantize_block<kOut>(acc, buf + lane * kBlockPitch, log2nb, nullptr, ctab, cc, bounds, cent, eps, scale_bf16, res);
         res_row = u * (kUnit >> log2d) + (lane >> log2nb);
         asm volatile("" ::: "memory");   // this unit's block reads precede the next unit's staging
     }
@@ -799,7 +872,8 @@ rpbh_wave_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int l
 template <int kOut>
 hipError_t launch_wave(const RowArgs& a, int log2d, hipStream_t stream) {
     auto kernel = rpbh_wave_bf16_kernel<kOut>;
-    const size_t lds = 6 * static_cast<size_t>(a.d) + static_cast<size_t>(kThreads / 64) * kWaveBuf;
+    const size_t lds = 6 * static_cast<size_t>(a.d) +
+                       static_cast<size_t>(kThreads / 64) * (kWaveBuf + CodeCtx<kOut>::kTabBytes);
     int per_cu = 0;
     const hipError_t e = kernel_blocks_per_cu(reinterpret_cast<const void*>(kernel), kThreads, lds, &per_cu);
     if (e != hipSuccess) return e;
@@ -818,8 +892,9 @@ hipError_t launch_t(const RowArgs& a, int log2d, hipStream_t stream) {
     const int log2nb = log2d - 6;
     const int64_t rpg = kThreads >> log2nb;
     const int64_t ngroups = (a.rows + rpg - 1) / rpg;
-    const size_t lds = kNC >= 4 ? static_cast<size_t>(kRowBuf) + 2 * static_cast<size_t>(a.d) + 64
-                                : 2 * static_cast<size_t>(kRowBuf) + 64;
+    const size_t lds = (kNC >= 4 ? static_cast<size_t>(kRowBuf) + 2 * static_cast<size_t>(a.d) + 64
+                                 : 2 * static_cast<size_t>(kRowBuf) + 64) +
+                       static_cast<size_t>(kThreads / 64) * CodeCtx<kOut>::kTabBytesRow;
     int per_cu = 0;
     const hipError_t e = kernel_blocks_per_cu(reinterpret_cast<const void*>(kernel), kThreads, lds, &per_cu);
     if (e != hipSuccess) return e;

@@ -148,6 +148,10 @@ def test_quantize_int8_prerotated_rows():
     (16384, 6, 4, False),    # W2A4 activations at d = 16384
     (16384, 9, 2, True),     # W2A4 weights
     (256, 65, 2, False),
+    # several rows per wave with an all-zero weight row (norm 0, eps = 0) among nonzero ones: the
+    # boundary-grid table of every row in the wave is built by lanes of all its rows
+    (1024, 23, 4, True),
+    (512, 21, 3, True),
 ])
 def test_quantize_codebook_matches_oracle(d, rows, bits, weight):
     xf = _case(500 + d + bits, rows, d, "w" if weight else "t3")
