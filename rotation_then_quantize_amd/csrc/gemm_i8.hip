@@ -621,99 +621,110 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
 
         // ---- epilogue.  The MFMA computed the transposed tile (W fragment first), so a lane holds
         // D[n][t] at n = 8*(r/4) + 4*(lane/32) + r%4, t = lane % 32: four consecutive output columns
-        // of one token row per group r/4.  Each wave copies its raw int32 block, 16 token rows at a
-        // time, into a private LDS region (ring slots 2 and 3; rows padded by 16 bytes against bank
-        // conflicts), then reads it back row-contiguously, scales and converts, and stores: the
+        // of one token row per group r/4.  Each wave copies its raw int32 block, one 32-row MFMA
+        // block at a time, into a private LDS region (ring slots 2 and 3; 16-byte chunk c of row r
+        // at chunk c ^ (r % 16), against bank conflicts), then reads it back row-contiguously,
+        // scales and converts, and stores: the
         // lanes of one row write a whole run of the wave's columns (128-512 bytes), so the
         // streaming stores are full cache lines.  Stores go through a descriptor that ends at the
         // tile's last valid row; columns past N are sent past its range.  kVec (N % 8 == 0): an
         // output chunk of 16 bytes is wholly inside or outside [0, N).
         if (epilogue) {
             constexpr int kOutBytes = kYKind == 1 ? 2 : 4;
-            constexpr int kPassRows = 16;
-            constexpr int kPitch = WN * 4 + 16;                    // raw int32 row + pad
+            constexpr int kPassRows = 32;
+            constexpr int kPitch = WN * 4;                         // raw int32 row
             constexpr int kPerChunk = 16 / kOutBytes;              // outputs per 16-byte store
             constexpr int kChunksPerRow = WN / kPerChunk;
             constexpr int kChunksPerLane = kPassRows * kChunksPerRow / 64;
             constexpr uint32_t kOob = 0x80000000u;
             static_assert(kWaves * kPassRows * kPitch <= 2 * kStageBytes, "staging must fit ring slots 2-3");
             int8_t* stg = lds + 2 * kStageBytes + wave * (kPassRows * kPitch);
+            auto swz = [](int row, int chunk) { return (chunk ^ (row & 15)) << 4; };   // byte offset in the row
+            // A lane's read-back chunk is column chunk lane % kChunksPerRow of every row it handles
+            // (64 is a multiple of kChunksPerRow), so its output-column scales are read once per tile.
+            static_assert(64 % kChunksPerRow == 0, "a lane's column chunk is the same in every pass");
+            float wsl[kPerChunk];
+            if constexpr (kYKind != 2) {
+#pragma unroll
+                for (int h4 = 0; h4 < kPerChunk / 4; ++h4) {
+                    const float4 v = *reinterpret_cast<const float4*>(s_ws + wn * WN + (lane % kChunksPerRow) * kPerChunk + 4 * h4);
+                    wsl[4 * h4 + 0] = v.x;
+                    wsl[4 * h4 + 1] = v.y;
+                    wsl[4 * h4 + 2] = v.z;
+                    wsl[4 * h4 + 3] = v.w;
+                }
+            }
             const int rows_y = static_cast<int>(min<int64_t>(BM, T - cm0));
             const __amdgpu_buffer_rsrc_t rsy = __builtin_amdgcn_make_buffer_rsrc(
                 static_cast<int8_t*>(Y) + cm0 * N * kOutBytes, (short)0, static_cast<int>(rows_y * N * kOutBytes),
                 kBufferWord3);
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
+                int8_t* wrow = stg + fr * kPitch;
 #pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    if ((fr >> 4) == half) {
-                        int8_t* wrow = stg + (fr & 15) * kPitch;
+                for (int j = 0; j < TN; ++j)
 #pragma unroll
-                        for (int j = 0; j < TN; ++j)
-#pragma unroll
-                            for (int g = 0; g < 4; ++g)
-                                *reinterpret_cast<v4i*>(wrow + (j * 32 + 8 * g + 4 * fh) * 4) =
-                                    v4i{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                                        acc[i][j][4 * g + 3]};
-                    }
-                    RTQ_LDS_FENCE();   // the wave's rows are in LDS before they are read back
+                    for (int g = 0; g < 4; ++g)
+                        *reinterpret_cast<v4i*>(wrow + swz(fr, 8 * j + 2 * g + fh)) =
+                            v4i{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                RTQ_LDS_FENCE();   // the wave's rows are in LDS before they are read back
 #pragma unroll 1
-                    for (int p = 0; p < kChunksPerLane; ++p) {
-                        const int q = p * 64 + lane;
-                        const int r = q / kChunksPerRow, c = q % kChunksPerRow;
-                        const int trow = wm * WM + i * 32 + half * kPassRows + r;   // row within the tile
-                        const int col = wn * WN + c * kPerChunk;                    // column within the tile
-                        const int8_t* src = stg + r * kPitch + c * kPerChunk * 4;
-                        v4i out;
-                        if (kYKind == 2) {
-                            out = correct(add_others(*reinterpret_cast<const v4i*>(src), trow, col), trow, col);
-                        } else {
-                            const float as = s_as[trow];
-                            float y[kPerChunk];
+                for (int p = 0; p < kChunksPerLane; ++p) {
+                    const int q = p * 64 + lane;
+                    const int r = q / kChunksPerRow, c = q % kChunksPerRow;
+                    const int trow = wm * WM + i * 32 + r;              // row within the tile
+                    const int col = wn * WN + c * kPerChunk;            // column within the tile
+                    const int8_t* src = stg + r * kPitch;
+                    constexpr int kQuads = kPerChunk / 4;               // 16-byte int32 chunks per output chunk
+                    v4i out;
+                    if (kYKind == 2) {
+                        out = correct(add_others(*reinterpret_cast<const v4i*>(src + swz(r, c)), trow, col), trow, col);
+                    } else {
+                        const float as = s_as[trow];
+                        float y[kPerChunk];
 #pragma unroll
-                            for (int h4 = 0; h4 < kPerChunk / 4; ++h4) {
-                                const v4i a = correct(add_others(*reinterpret_cast<const v4i*>(src + 16 * h4), trow, col + 4 * h4),
-                                                      trow, col + 4 * h4);
-                                const float4 ws = *reinterpret_cast<const float4*>(s_ws + col + 4 * h4);
-                                y[4 * h4 + 0] = static_cast<float>(a.x) * as * ws.x;
-                                y[4 * h4 + 1] = static_cast<float>(a.y) * as * ws.y;
-                                y[4 * h4 + 2] = static_cast<float>(a.z) * as * ws.z;
-                                y[4 * h4 + 3] = static_cast<float>(a.w) * as * ws.w;
-                            }
-                            if (kYKind == 0) {
-                                out = v4i{static_cast<int>(__float_as_uint(y[0])), static_cast<int>(__float_as_uint(y[1])),
-                                          static_cast<int>(__float_as_uint(y[2])), static_cast<int>(__float_as_uint(y[3]))};
-                            } else {
-                                uint32_t w[4];
-#pragma unroll
-                                for (int e = 0; e < 4; ++e)
-                                    w[e] = pack_bf16x2(y[2 * e], y[2 * e + 1]);
-                                out = v4i{static_cast<int>(w[0]), static_cast<int>(w[1]), static_cast<int>(w[2]),
-                                          static_cast<int>(w[3])};
-                            }
+                        for (int h4 = 0; h4 < kPerChunk / 4; ++h4) {
+                            const v4i a = correct(add_others(*reinterpret_cast<const v4i*>(src + swz(r, kQuads * c + h4)),
+                                                             trow, col + 4 * h4),
+                                                  trow, col + 4 * h4);
+                            y[4 * h4 + 0] = static_cast<float>(a.x) * as * wsl[4 * h4 + 0];
+                            y[4 * h4 + 1] = static_cast<float>(a.y) * as * wsl[4 * h4 + 1];
+                            y[4 * h4 + 2] = static_cast<float>(a.z) * as * wsl[4 * h4 + 2];
+                            y[4 * h4 + 3] = static_cast<float>(a.w) * as * wsl[4 * h4 + 3];
                         }
-                        const int64_t n = cn0 + col;
-                        const uint32_t off = (static_cast<uint32_t>(trow) * static_cast<uint32_t>(N) +
-                                              static_cast<uint32_t>(n)) * kOutBytes;
-                        if (kVec) {
-                            __builtin_amdgcn_raw_buffer_store_b128(out, rsy, static_cast<int>(n < N ? off : kOob), 0,
-                                                                   kStoreNT);
+                        if (kYKind == 0) {
+                            out = v4i{static_cast<int>(__float_as_uint(y[0])), static_cast<int>(__float_as_uint(y[1])),
+                                      static_cast<int>(__float_as_uint(y[2])), static_cast<int>(__float_as_uint(y[3]))};
                         } else {
-                            const uint32_t w[4] = {static_cast<uint32_t>(out.x), static_cast<uint32_t>(out.y),
-                                                   static_cast<uint32_t>(out.z), static_cast<uint32_t>(out.w)};
+                            uint32_t w[4];
 #pragma unroll
-                            for (int e = 0; e < kPerChunk; ++e) {
-                                const int o = static_cast<int>(n + e < N ? off + e * kOutBytes : kOob);
-                                if (kOutBytes == 4)
-                                    __builtin_amdgcn_raw_buffer_store_b32(w[e], rsy, o, 0, kStoreNT);
-                                else
-                                    __builtin_amdgcn_raw_buffer_store_b16(
-                                        static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1))), rsy, o, 0, kStoreNT);
-                            }
+                            for (int e = 0; e < 4; ++e)
+                                w[e] = pack_bf16x2(y[2 * e], y[2 * e + 1]);
+                            out = v4i{static_cast<int>(w[0]), static_cast<int>(w[1]), static_cast<int>(w[2]),
+                                      static_cast<int>(w[3])};
                         }
                     }
-                    RTQ_LDS_FENCE();   // read back before the next pass overwrites the region
+                    const int64_t n = cn0 + col;
+                    const uint32_t off = (static_cast<uint32_t>(trow) * static_cast<uint32_t>(N) +
+                                          static_cast<uint32_t>(n)) * kOutBytes;
+                    if (kVec) {
+                        __builtin_amdgcn_raw_buffer_store_b128(out, rsy, static_cast<int>(n < N ? off : kOob), 0,
+                                                               kStoreNT);
+                    } else {
+                        const uint32_t w[4] = {static_cast<uint32_t>(out.x), static_cast<uint32_t>(out.y),
+                                               static_cast<uint32_t>(out.z), static_cast<uint32_t>(out.w)};
+#pragma unroll
+                        for (int e = 0; e < kPerChunk; ++e) {
+                            const int o = static_cast<int>(n + e < N ? off + e * kOutBytes : kOob);
+                            if (kOutBytes == 4)
+                                __builtin_amdgcn_raw_buffer_store_b32(w[e], rsy, o, 0, kStoreNT);
+                            else
+                                __builtin_amdgcn_raw_buffer_store_b16(
+                                    static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1))), rsy, o, 0, kStoreNT);
+                        }
+                    }
                 }
+                RTQ_LDS_FENCE();   // read back before the next pass overwrites the region
             }
         }
         RTQ_BARRIER();   // every wave is done with the staging slots and the scales
