@@ -250,8 +250,8 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
     const int wm = wave / kWavesN, wn = wave % kWavesN;
 
     // Whole tiles [0, dp): split into 8 contiguous ranges, one per XCD (block b runs on XCD b % 8),
-    // taken round-robin by that XCD's blocks.  Split tiles [dp, total): unit u = xcd * stride + local
-    // is K range u % split of tile dp + u / split, so the units of one tile sit on one XCD.
+    // taken round-robin by that XCD's blocks.  Split tiles [dp, total): unit u is K range u % split
+    // of tile dp + u / split; the units of one tile sit on one XCD (below).
     const int total = tiles_m * tiles_n;
     const int xcd = blockIdx.x % kXcds;
     const int stride = gridDim.x / kXcds;
@@ -259,8 +259,11 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
     const int dp = sp.dp_tiles;
     const int per = (dp + kXcds - 1) / kXcds;
     const int lin_end = min((xcd + 1) * per, dp);
-    const int unit = xcd * stride + local;
-    const bool has_unit = sp.split > 1 && unit < (total - dp) * sp.split;
+    // split tile tt runs on XCD tt % 8 (so the tail's partial traffic spreads over every XCD's L2),
+    // its K ranges on blocks local = split * (tt / 8) + range of that XCD; unit = tt * split + range
+    const int tail_tile = (local / max(sp.split, 1)) * kXcds + xcd;
+    const int unit = tail_tile * sp.split + local % max(sp.split, 1);
+    const bool has_unit = sp.split > 1 && tail_tile < total - dp;
     int lin = xcd * per + local;
     bool in_tail = lin >= lin_end;
     if (in_tail && !has_unit) return;   // no work for this block: before any barrier
@@ -555,26 +558,56 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
             load_scales();
         }
 
-        // ---- split tile: publish this K range's partial (row-major int32 256 x 256); the last
-        // block of the tile to arrive runs the epilogue and adds the other partials there
+        // ---- staging: the MFMA computed the transposed tile (W fragment first), so a lane holds
+        // D[n][t] at n = 8*(r/4) + 4*(lane/32) + r%4, t = lane % 32: four consecutive output columns
+        // of one token row per group r/4.  stage_block(i) copies a wave's raw int32 rows of MFMA
+        // block i (32 token rows) into its private LDS region (ring slots 2 and 3; 16-byte chunk c of
+        // row r at chunk c ^ (r % 16), against bank conflicts), to be read back row-contiguously.
+        constexpr int kPassRows = 32;
+        constexpr int kPitch = WN * 4;                             // raw int32 row
+        static_assert(kWaves * kPassRows * kPitch <= 2 * kStageBytes, "staging must fit ring slots 2-3");
+        int8_t* stg = lds + 2 * kStageBytes + wave * (kPassRows * kPitch);
+        auto swz = [](int row, int chunk) { return (chunk ^ (row & 15)) << 4; };   // byte offset in the row
+        auto stage_block = [&](int i) {
+            int8_t* wrow = stg + fr * kPitch;
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    *reinterpret_cast<v4i*>(wrow + swz(fr, 8 * j + 2 * g + fh)) =
+                        v4i{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+            RTQ_LDS_FENCE();   // the wave's rows are in LDS before they are read back
+        };
+
+        // ---- split tile: publish this K range's partial (row-major int32 256 x 256, stored through
+        // the staging as whole rows); the last block of the tile to arrive runs the epilogue and
+        // adds the other partials there
         bool epilogue = true;
         int others = 0;                 // first unit of my tile, when summing partials
+        // Partial layout: row-major int32 quads; with bf16 output (where a lane of the epilogue
+        // reads quads 2c and 2c + 1 of a row) a wave's row slice holds its even quads, then its odd
+        // ones, so each load instruction there reads whole lines.
+        constexpr int kQuadsPerRow = WN / 4;
+        auto quad_pos = [](int c) { return kYKind == 1 ? (c & 1) * (kQuadsPerRow / 2) + (c >> 1) : c; };
         if (ctail) {
-            v4i* mine = sp.partials + static_cast<size_t>(unit) * (BM * BN / 4);
+            const __amdgpu_buffer_rsrc_t rsm = __builtin_amdgcn_make_buffer_rsrc(
+                sp.partials + static_cast<size_t>(unit) * (BM * BN / 4), (short)0, BM * BN * 4, kBufferWord3);
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int row = wm * WM + i * 32 + fr, col = wn * WN + j * 32 + 8 * g + 4 * fh;
-                        mine[(row * BN + col) >> 2] =
-                            v4i{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-                    }
-            // All blocks of a split tile run on one XCD (the launcher makes the split divide the
-            // blocks per XCD), so its L2 is the point of coherence: the stores have reached it once
-            // they are acknowledged, the counter's atomic executes there, and the last block reads
-            // the partials with loads that bypass its own L1.
+            for (int i = 0; i < TM; ++i) {
+                stage_block(i);
+#pragma unroll 1
+                for (int p = 0; p < kPassRows * kQuadsPerRow / 64; ++p) {
+                    const int q = p * 64 + lane;
+                    const int r = q / kQuadsPerRow, c = q % kQuadsPerRow;
+                    const v4i v = *reinterpret_cast<const v4i*>(stg + r * kPitch + swz(r, c));
+                    __builtin_amdgcn_raw_buffer_store_b128(v, rsm, ((wm * WM + i * 32 + r) * BN + wn * WN + 4 * quad_pos(c)) * 4,
+                                                           0, 0);
+                }
+                RTQ_LDS_FENCE();   // read back before the next block overwrites the region
+            }
+            // All blocks of a split tile run on one XCD, so its L2 is the point of coherence: the
+            // stores have reached it once they are acknowledged, the counter's atomic executes
+            // there, and the last block reads the partials with loads that bypass its own L1.
             RTQ_WAIT_ALL_VMEM();
             __syncthreads();
             if (tid == 0)
@@ -587,16 +620,17 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
         // int32 quad (4 consecutive columns) at (row, col) of the tile: mine plus the other K ranges'
         const __amdgpu_buffer_rsrc_t rsp = __builtin_amdgcn_make_buffer_rsrc(
             sp.partials + static_cast<size_t>(others) * (BM * BN / 4), (short)0, sp.split * BM * BN * 4, kBufferWord3);
-        // All kMaxSplit loads are issued back to back (the unit's own range and ranges past `split`
-        // are addressed past the descriptor and read as zero), so their latencies overlap.
+        // The other ranges' loads are issued back to back, so their latencies overlap (the branches
+        // are uniform: the split and the block's own range).
         auto add_others = [&](v4i v, int row, int col) -> v4i {
             if (ctail) {
                 v4i part[kMaxSplit];
 #pragma unroll
                 for (int o = 0; o < kMaxSplit; ++o) {
-                    const uint32_t off = others + o == unit ? 0x80000000u
-                                                            : static_cast<uint32_t>((o * BM * BN + row * BN + col) * 4);
-                    part[o] = __builtin_amdgcn_raw_buffer_load_b128(rsp, static_cast<int>(off), 0, kLoadL2);
+                    part[o] = v4i{0, 0, 0, 0};
+                    if (o < sp.split && others + o != unit)
+                        part[o] = __builtin_amdgcn_raw_buffer_load_b128(
+                            rsp, (o * BM * BN + row * BN + wn * WN + 4 * quad_pos((col - wn * WN) >> 2)) * 4, 0, kLoadL2);
                 }
 #pragma unroll
                 for (int o = 0; o < kMaxSplit; ++o) v += part[o];
@@ -619,27 +653,18 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
             return a;
         };
 
-        // ---- epilogue.  The MFMA computed the transposed tile (W fragment first), so a lane holds
-        // D[n][t] at n = 8*(r/4) + 4*(lane/32) + r%4, t = lane % 32: four consecutive output columns
-        // of one token row per group r/4.  Each wave copies its raw int32 block, one 32-row MFMA
-        // block at a time, into a private LDS region (ring slots 2 and 3; 16-byte chunk c of row r
-        // at chunk c ^ (r % 16), against bank conflicts), then reads it back row-contiguously,
-        // scales and converts, and stores: the
+        // ---- epilogue.  Each wave stages its raw int32 block one 32-row MFMA block at a time, reads
+        // it back row-contiguously, scales and converts, and stores: the
         // lanes of one row write a whole run of the wave's columns (128-512 bytes), so the
         // streaming stores are full cache lines.  Stores go through a descriptor that ends at the
         // tile's last valid row; columns past N are sent past its range.  kVec (N % 8 == 0): an
         // output chunk of 16 bytes is wholly inside or outside [0, N).
         if (epilogue) {
             constexpr int kOutBytes = kYKind == 1 ? 2 : 4;
-            constexpr int kPassRows = 32;
-            constexpr int kPitch = WN * 4;                         // raw int32 row
             constexpr int kPerChunk = 16 / kOutBytes;              // outputs per 16-byte store
             constexpr int kChunksPerRow = WN / kPerChunk;
             constexpr int kChunksPerLane = kPassRows * kChunksPerRow / 64;
             constexpr uint32_t kOob = 0x80000000u;
-            static_assert(kWaves * kPassRows * kPitch <= 2 * kStageBytes, "staging must fit ring slots 2-3");
-            int8_t* stg = lds + 2 * kStageBytes + wave * (kPassRows * kPitch);
-            auto swz = [](int row, int chunk) { return (chunk ^ (row & 15)) << 4; };   // byte offset in the row
             // A lane's read-back chunk is column chunk lane % kChunksPerRow of every row it handles
             // (64 is a multiple of kChunksPerRow), so its output-column scales are read once per tile.
             static_assert(64 % kChunksPerRow == 0, "a lane's column chunk is the same in every pass");
@@ -660,14 +685,7 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
                 kBufferWord3);
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
-                int8_t* wrow = stg + fr * kPitch;
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g)
-                        *reinterpret_cast<v4i*>(wrow + swz(fr, 8 * j + 2 * g + fh)) =
-                            v4i{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-                RTQ_LDS_FENCE();   // the wave's rows are in LDS before they are read back
+                stage_block(i);
 #pragma unroll 1
                 for (int p = 0; p < kChunksPerLane; ++p) {
                     const int q = p * 64 + lane;
