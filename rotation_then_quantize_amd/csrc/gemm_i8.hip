@@ -515,13 +515,15 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
                     wait_vmcnt<0>();
             }
             RTQ_BARRIER();   // every wave's part of stage s + 1 is in LDS; stage s - 1 is consumed
-            if (s + 3 < nk) issue_stage(s + 3);   // into stage s - 1's slot
             if (kCoded) {
                 if (s + 4 < nk) issue_codes(s + 4);   // raw slot of codes s + 1, decoded last iteration
                 if (s + 2 < nk) decode_stage(s + 2);  // visible after the next barrier
             }
             read_frags(fa1, fb1, s, frag_off1);
             mfmas(fa0, fb0);
+            // stage s + 3 into stage s - 1's slot, issued behind the first K step's MFMAs (measured
+            // 2% faster than right after the barrier)
+            if (s + 3 < nk) issue_stage(s + 3);
             // (on the last stage this reads an unused slot: unconditional, so the compiler's LDS wait
             // before the next MFMAs does not also cover these reads)
             read_frags(fa0, fb0, s + 1, frag_off0);
