@@ -120,12 +120,13 @@ def test_int8_full_shape_sampled():
 # ---------------------------------------------------------------- K-split of the last round
 
 @pytest.mark.parametrize("T,N,d", [(130, 200, 256), (257, 129, 128), (64, 384, 4096), (33, 70, 16384),
-                                   (300, 700, 2048), (4608, 4096, 8192)])
+                                   (300, 700, 2048), (4608, 4096, 8192), (3328, 5376, 4096)])
 def test_int8_ksplit_accumulators_bit_exact(T, N, d):
     # with a workspace the tiles of a last round that leaves most compute units idle are split
     # along d; the pieces add exactly in int32.  On 256 CUs: d < 2048 never splits; one tile at
     # d = 4096 / 16384 splits 4 / 8 ways; 300 x 700 x 2048 is 6 tiles split 2 ways; 4608 x 4096 is
-    # 288 tiles: one whole round, then 32 tiles split 8 ways.
+    # 288 tiles: one whole round, then 32 tiles split 8 ways; 3328 x 5376 is 273 tiles: 17 split
+    # 4 ways, dealt unevenly over the 8 XCDs (3 on the first, 2 on each other).
     a = _codes(11 + T, T, d)
     w = _codes(12 + N, N, d)
     ws = torch.full((rtq.qgemm_workspace(),), 0x5A, dtype=torch.uint8, device="cuda")   # arbitrary contents
@@ -142,9 +143,10 @@ def test_int8_ksplit_accumulators_bit_exact(T, N, d):
 
 
 @pytest.mark.parametrize("yt", ["f32", "bf16"])
-def test_ksplit_outputs_equal_unsplit(yt):
+@pytest.mark.parametrize("T,N,d", [(300, 700, 2048), (3328, 5376, 4096)])
+def test_ksplit_outputs_equal_unsplit(yt, T, N, d):
     # exact int32 sums, then the same epilogue: split and unsplit products agree bit for bit
-    T, N, d = 300, 700, 2048
+    # (6 tiles split 2 ways; 17 of 273 tiles split 4 ways)
     a = _codes(21, T, d)
     w = _codes(22, N, d)
     rng = np.random.default_rng(23)
