@@ -1,6 +1,6 @@
 // rpbh_quant.hip -- the hot RPBH rotate + quantise kernel for bf16 rows on gfx950.
 //
-// Same arithmetic as rpbh_rows.hip (x' = Pi_d x exactly via fp64 butterflies, OrbitQuant article
+// Same arithmetic as rpbh_rows.hip (x' = Pi_d x via exact fp64 butterflies, OrbitQuant article
 // 2.3; INT8 s = max|x'|/127, q = rne(x'/s), cloud.baidu.com/article/9432521 4; Lloyd-Max codes of
 // x'/(||x'|| + eps), OrbitQuant article 2.1-2.2), organised for HBM throughput:
 //
@@ -450,7 +450,8 @@ __device__ __forceinline__ void quantize_block(double (&acc)[kH], const unsigned
         }
         res.s = s;
     } else {
-        // x' = fl32(8x' / 8), exactly the oracle's rotated value for every input
+        // x' = fl32(8x' / 8): the oracle's rotated value (fp64 sums of bf16 inputs are exact while a
+        // block's magnitudes span at most 2^39)
         float xr[kH];
         double ss4[4] = {0.0, 0.0, 0.0, 0.0};   // four interleaved partial sums: short dependency chains
 #pragma unroll

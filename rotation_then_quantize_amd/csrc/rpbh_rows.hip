@@ -16,10 +16,11 @@
 //      the source side: element k is flipped by the sign of the output slot it is gathered into
 //      (sign[j] with perm[j] == k); the XOR masks for that live in LDS, built once per workgroup.
 //   2. Each lane gathers its 64 inputs through perm (addresses precomputed once per workgroup).
-//   3. FWHT-64 in fp64.  With bf16 inputs every partial sum is exact in fp64, so after the single
-//      rounding to fp32 the rotated value is the correctly rounded Pi v -- identical to a dense
-//      product accumulated exactly.  The 1/8 normalisation is folded into the scale (exact power
-//      of two), so the registers hold 8*v'.
+//   3. FWHT-64 in fp64.  With bf16 inputs (8 significant bits) every partial sum of a block is
+//      exact in fp64 while the block's magnitudes span at most 2^39, so after the single rounding
+//      to fp32 the rotated value is the correctly rounded Pi v -- identical to a dense product
+//      accumulated exactly.  The 1/8 normalisation is folded into the scale (exact power of two),
+//      so the registers hold 8*v'.
 //   4. Row reduction (max |v'| or sum v'^2 in fp64) across the d/64 lanes of the row: xor
 //      shuffles inside a wave, LDS across waves.
 //   5. Quantise, pack, and store 16-byte vectors.
