@@ -450,8 +450,8 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
     }
 
     // Stages 0 and 1 of a tile (and weight codes 0..2) are fetched before the previous tile's
-    // epilogue (which stages its output through ring slots 2 and 3), stage 2 after it.  Order of
-    // the loads matters for the waits: in the loop, iteration s issues stage s + 3 then codes s + 4.
+    // epilogue (which stages its output through ring slots 2 and 3), stage 2 after it.  The waits
+    // count loads by iteration: in the loop, iteration s issues codes s + 4 and stage s + 3.
     auto prefetch_early = [&]() {
         issue_stage(0);
         if (kCoded) {

@@ -22,9 +22,10 @@
 //    2^-103 (subnormals could round differently) take an IEEE-division path.
 //  * Division-free codebook codes: for each row the exact fp32 thresholds Y_k = min{x' : fl32(x' /
 //    (s+eps)) > t_k} are found once (IEEE divisions, a few ulp steps), so code = #{k : x' >= Y_k}
-//    needs no division.  For 16 levels the candidate boundary comes from a 64-cell grid over the
-//    boundary range (table in lanes, fetched with ds_bpermute) and one compare settles the code;
-//    the grid is built so a cell, widened by the rounding slack, holds at most one boundary.
+//    needs no division.  For 8, 16 and 64 levels the candidate boundary comes from a grid over the
+//    boundary range (64 or 256 cells, each holding at most one boundary even when widened by the
+//    rounding slack): one LDS table read per element gives the cell's threshold, the count below
+//    it and the int8 values, and one compare settles the code.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
