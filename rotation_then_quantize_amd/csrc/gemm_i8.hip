@@ -356,23 +356,37 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
         }
     };
     // Raw slot of stage st -> int8 values in the W half of stage st's ring slot.  Thread t decodes
-    // row t / 2, K bytes 32 * (t % 2) .. +32 (two 16-byte chunks of the swizzled row).
+    // row t / 2, K bytes 32 * (t % 2) .. +32 (two 16-byte chunks of the swizzled row).  In the main
+    // loop the raw codes are read right after the barrier and decoded behind the first K step's
+    // MFMAs, so the read's latency is covered (measured 2-3% faster than decoding at the barrier).
     uint32_t lut[4] = {0u, 0u, 0u, 0u};
-    auto decode_stage = [&](int st) {
+    struct RawCodes { uint32_t w[4]; };
+    auto read_raw = [&](int st) -> RawCodes {
         const int8_t* raw = lds + kLds + (st % kRawSlots) * kRawStage;
-        uint32_t v[8];
+        RawCodes r{{0u, 0u, 0u, 0u}};
         if constexpr (kWBits == 4) {
             const v4i x = *reinterpret_cast<const v4i*>(raw + 16 * tid);
-            const uint32_t in[4] = {static_cast<uint32_t>(x.x), static_cast<uint32_t>(x.y),
-                                    static_cast<uint32_t>(x.z), static_cast<uint32_t>(x.w)};
-            decode4(lut, in, v);
+            r.w[0] = static_cast<uint32_t>(x.x); r.w[1] = static_cast<uint32_t>(x.y);
+            r.w[2] = static_cast<uint32_t>(x.z); r.w[3] = static_cast<uint32_t>(x.w);
         } else if constexpr (kWBits == 2) {
             const uint2 x = *reinterpret_cast<const uint2*>(raw + 8 * tid);
-            const uint32_t in[2] = {x.x, x.y};
-            decode2(lut, in, v);
+            r.w[0] = x.x; r.w[1] = x.y;
         } else if constexpr (kWBits == 3) {
             const uint32_t* xr = reinterpret_cast<const uint32_t*>(raw + 12 * tid);
-            const uint32_t in[3] = {xr[0], xr[1], xr[2]};
+            r.w[0] = xr[0]; r.w[1] = xr[1]; r.w[2] = xr[2];
+        }
+        return r;
+    };
+    auto decode_write = [&](int st, const RawCodes& r) {
+        uint32_t v[8];
+        if constexpr (kWBits == 4) {
+            const uint32_t in[4] = {r.w[0], r.w[1], r.w[2], r.w[3]};
+            decode4(lut, in, v);
+        } else if constexpr (kWBits == 2) {
+            const uint32_t in[2] = {r.w[0], r.w[1]};
+            decode2(lut, in, v);
+        } else if constexpr (kWBits == 3) {
+            const uint32_t in[3] = {r.w[0], r.w[1], r.w[2]};
             decode3(lut, in, v);
         }
         const int row = tid >> 1, c0 = 2 * (tid & 1), sw = (row >> 2) & 3;
@@ -382,6 +396,7 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
         *reinterpret_cast<v4i*>(wb + (((c0 + 1) ^ sw) << 4)) =
             v4i{static_cast<int>(v[4]), static_cast<int>(v[5]), static_cast<int>(v[6]), static_cast<int>(v[7])};
     };
+    auto decode_stage = [&](int st) { decode_write(st, read_raw(st)); };
     // The tile's token scales (entries 0..255) and output-row scales (256..511), one or two per
     // thread, staged in LDS behind the ring for the epilogue.
     float sc[kScalesPerThread];
@@ -515,12 +530,14 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
                     wait_vmcnt<0>();
             }
             RTQ_BARRIER();   // every wave's part of stage s + 1 is in LDS; stage s - 1 is consumed
+            RawCodes rc{{0u, 0u, 0u, 0u}};
             if (kCoded) {
                 if (s + 4 < nk) issue_codes(s + 4);   // raw slot of codes s + 1, decoded last iteration
-                if (s + 2 < nk) decode_stage(s + 2);  // visible after the next barrier
+                if (s + 2 < nk) rc = read_raw(s + 2);
             }
             read_frags(fa1, fb1, s, frag_off1);
             mfmas(fa0, fb0);
+            if (kCoded && s + 2 < nk) decode_write(s + 2, rc);   // visible after the next barrier
             // stage s + 3 into stage s - 1's slot, issued behind the first K step's MFMAs (measured
             // 2% faster than right after the barrier)
             if (s + 3 < nk) issue_stage(s + 3);
