@@ -153,10 +153,13 @@ rtq_status rtq_qgemm(const void* a_codes, const float* a_scale, int64_t T, const
                      const void* w_scale, rtq_dtype w_scale_t, int64_t N, int32_t d, rtq_qmode mode,
                      const rtq_codebook* cb_a, const rtq_codebook* cb_w, void* y, rtq_dtype yt, void* stream);
 
-/* rtq_qgemm with a workspace for the INT8-core modes (RTQ_INT8, RTQ_CODEBOOK_I8): the tiles of the
- * last, partial round of 256 x 256 output tiles are split along d over the otherwise idle compute
- * units; each piece stores an int32 partial tile in the workspace and the last piece of a tile to
- * finish adds the others (exact int32 sums, so results equal rtq_qgemm's bit for bit).
+/* rtq_qgemm with a workspace for the INT8-core modes (RTQ_INT8, RTQ_CODEBOOK_I8): a partial last
+ * round of 256 x 256 output tiles is shared along d, so no compute unit idles behind it.  After
+ * at least one full round, the last full round and the remainder are dealt out as equal runs of
+ * K stages that cross tile edges (stream-K); with fewer tiles than compute units, each tile is
+ * cut into equal K ranges.  A piece that holds only part of a tile stores an int32 partial tile
+ * in the workspace, and the last piece of the tile to finish adds the others (exact int32 sums, so
+ * results equal rtq_qgemm's bit for bit).
  *   workspace: device memory of at least rtq_qgemm_workspace() bytes, 16-byte aligned, any
  *   contents (per-tile arrival counters carry a launch tag, so no clearing is needed).  Launches
  *   that share a workspace must not run concurrently.  A smaller or NULL workspace, or the
@@ -166,8 +169,8 @@ rtq_status rtq_qgemm_ws(const void* a_codes, const float* a_scale, int64_t T, co
                         const rtq_codebook* cb_a, const rtq_codebook* cb_w, void* y, rtq_dtype yt,
                         void* workspace, size_t ws_bytes, void* stream);
 
-/* Bytes of workspace rtq_qgemm_ws uses on the current device: one 256 KB int32 partial tile and
- * one 8-byte counter per compute unit (64 MB on a 256-CU MI355X). */
+/* Bytes of workspace rtq_qgemm_ws uses on the current device: two 256 KB int32 partial tiles and
+ * two 8-byte counters per compute unit (128 MB on a 256-CU MI355X). */
 size_t rtq_qgemm_workspace(void);
 
 /* The online layer: rtq_quantize_rows(x, R, mode, cb_a, eps = 1e-8 (CODEBOOK) ...) into `workspace`

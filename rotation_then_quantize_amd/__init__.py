@@ -217,8 +217,8 @@ def quantize_rows(x, codes, scale, R: Rpbh | None = None, mode: int = RTQ_INT8, 
 def qgemm(a_codes, a_scale, w_codes, w_scale, y, d: int, mode: int = RTQ_INT8, cb_a: Codebook | None = None,
           cb_w: Codebook | None = None, stream=None, workspace=None):
     """y = dequantised product of activation and weight codes (rotation already cancelled).
-    With a workspace (qgemm_workspace() bytes) this is rtq_qgemm_ws: the last partial round of
-    tiles is split along d over idle compute units."""
+    With a workspace (qgemm_workspace() bytes) this is rtq_qgemm_ws: a partial last round of tiles
+    is shared along d (stream-K runs after a full round, equal K ranges otherwise)."""
     T = a_codes.shape[0]
     N = w_codes.shape[0]
     lib = load_library()

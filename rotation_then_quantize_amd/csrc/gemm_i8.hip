@@ -166,28 +166,38 @@ __device__ __forceinline__ void decode3(const uint32_t (&lut)[4], const uint32_t
     }
 }
 
-// K-split of the last, partial round of tiles.  Tiles [0, dp_tiles) run whole, data-parallel;
-// each of the remaining tiles is split into `split` K ranges run by `split` blocks.  Every block of
-// a split tile stores its int32 partial tile and arrives on the tile's counter; the last to arrive
-// adds the others' partials and runs the epilogue (no block ever waits for another).  Counters hold
-// (epoch << 32) | arrivals; a counter from an earlier launch (other epoch) counts as zero, so the
-// workspace needs no clearing.
+// Tiles shared along K.  Tiles [0, dp_tiles) run whole, data-parallel; the remaining (shared)
+// tiles are cut along K into runs of blocks: either `split` equal K ranges per tile (a last round
+// that would leave most blocks idle), or stream-K (split 0: a last full round plus a small
+// remainder spread evenly over every block, each run at least one tile long).  Every block whose
+// run meets a tile only in part stores its int32 partial tile and arrives on the tile's counter;
+// the last to arrive adds the others' partials and runs the epilogue (no block ever waits for
+// another; a stream-K tile's second piece to finish skips its own store, see the epilogue).
+// Counters hold (epoch << 32) | arrivals; a counter from an earlier launch (other epoch) counts
+// as zero, so the workspace needs no clearing.
 constexpr int kMaxSplit = 8;
 
 struct SplitArgs {
     int dp_tiles;
-    int split;                      // 1: no split
-    v4i* partials;                  // [units][BM * BN / 4] int32 quads
-    unsigned long long* counters;   // [tail tiles]
+    int split;                      // 1: no shared tiles; >= 2: equal K ranges per tile; 0: stream-K
+    v4i* partials;                  // [block][2][BM * BN / 4] int32 quads (below)
+    unsigned long long* counters;   // [shared tile]
     unsigned int epoch;
 };
 
-// Arrive on a split tile's counter; returns how many blocks of this launch arrived before.
-__device__ unsigned int split_arrive(unsigned long long* c, unsigned int epoch) {
+// Workspace per block slot (one block per compute unit): two partial tiles, since a run meets at
+// most two tiles in part (its first piece and its last), and two counters, since a stream-K launch
+// shares less than two rounds of tiles.
+constexpr int64_t partial_slots_cap(int64_t slots) { return 2 * slots; }
+constexpr int64_t shared_tiles_cap(int64_t slots) { return 2 * slots; }
+
+// Add `add` to a shared tile's counter; returns its low word before, as this launch left it
+// (0 if the counter still holds an earlier launch's tag).
+__device__ unsigned int split_arrive(unsigned long long* c, unsigned int epoch, unsigned int add) {
     unsigned long long cur = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     for (int i = 0; i < (1 << 20); ++i) {   // lock-free: each failed exchange means another block's succeeded
         const bool same = static_cast<unsigned int>(cur >> 32) == epoch;
-        const unsigned long long next = same ? cur + 1ull : ((static_cast<unsigned long long>(epoch) << 32) | 1ull);
+        const unsigned long long next = same ? cur + add : ((static_cast<unsigned long long>(epoch) << 32) | add);
         const unsigned long long seen = atomicCAS(c, cur, next);
         if (seen == cur) return same ? static_cast<unsigned int>(cur) : 0u;
         cur = seen;
@@ -250,8 +260,7 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
     const int wm = wave / kWavesN, wn = wave % kWavesN;
 
     // Whole tiles [0, dp): split into 8 contiguous ranges, one per XCD (block b runs on XCD b % 8),
-    // taken round-robin by that XCD's blocks.  Split tiles [dp, total): unit u is K range u % split
-    // of tile dp + u / split; the units of one tile sit on one XCD (below).
+    // taken round-robin by that XCD's blocks.
     const int total = tiles_m * tiles_n;
     const int xcd = blockIdx.x % kXcds;
     const int stride = gridDim.x / kXcds;
@@ -259,14 +268,25 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
     const int dp = sp.dp_tiles;
     const int per = (dp + kXcds - 1) / kXcds;
     const int lin_end = min((xcd + 1) * per, dp);
-    // split tile tt runs on XCD tt % 8 (so the tail's partial traffic spreads over every XCD's L2),
-    // its K ranges on blocks local = split * (tt / 8) + range of that XCD; unit = tt * split + range
-    const int tail_tile = (local / max(sp.split, 1)) * kXcds + xcd;
-    const int unit = tail_tile * sp.split + local % max(sp.split, 1);
-    const bool has_unit = sp.split > 1 && tail_tile < total - dp;
+    const int nk_all = d / BK;
+    // Shared tiles [dp, total): shared tile st is tile dp + st and runs on XCD st % 8, so all its K
+    // ranges meet in one L2 (and the shared tiles' partial traffic spreads over every XCD).  The
+    // XCD's tiles_x shared tiles form one tile-major sequence of tiles_x * nk_all K stages, cut into
+    // equal runs [g_run, g_end), one per block: blocks_x = tiles_x * split runs (split equal K ranges
+    // per tile), or, with split 0 (stream-K), a run for each of the XCD's blocks; those runs are at
+    // least one tile long, so a tile meets at most two of them.
+    const int shared = total - dp;
+    const int tiles_x = shared > xcd ? (shared - xcd + kXcds - 1) / kXcds : 0;
+    const int blocks_x = sp.split == 0 ? stride : min(stride, tiles_x * sp.split);
+    const int64_t w_x = static_cast<int64_t>(tiles_x) * nk_all;
+    int64_t g_run = 0, g_end = 0;
+    if (sp.split != 1 && local < blocks_x) {
+        g_run = local * w_x / blocks_x;
+        g_end = (local + 1) * w_x / blocks_x;
+    }
     int lin = xcd * per + local;
     bool in_tail = lin >= lin_end;
-    if (in_tail && !has_unit) return;   // no work for this block: before any barrier
+    if (in_tail && g_run >= g_end) return;   // no work for this block: before any barrier
 
     const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
     float* s_as = reinterpret_cast<float*>(lds + kRingBytes);
@@ -275,8 +295,17 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
     static_assert(!kAsym || !kCoded, "zero points with int8 weights only");
     int* s_z = reinterpret_cast<int*>(lds + kLds);   // kAsym: zero points, rows then columns
     int* s_e = s_z + BM + BN;                        // kAsym: sum_j qa (rows), sum_j qw - d zw (columns)
-    const int nk_all = d / BK;
     int kbeg = 0, nk = nk_all;   // the current work item's K stages
+    // The current shared piece: its tile's counter (shared tile index), the first run (XCD-local
+    // block) that meets the tile, the number of runs that do (1: no partials) and this block's
+    // place among them.
+    int ptile = 0, pfirst = 0, pcount = 1, pord = 0;
+    // Partial slot of the o-th run meeting a tile whose first run is `first`: slot [1] of block
+    // `first` (a stream-K tile's head, the last piece of that run), else slot [0] of block
+    // first + o (the first piece of its run; with equal K ranges, a run's only piece).
+    auto piece_slot = [&](int first, int o) {
+        return 2 * ((first + o) * kXcds + xcd) + ((sp.split == 0 && o == 0) ? 1 : 0);
+    };
 
     // Load geometry: instruction q of wave w fills rows 16 * (q * kWaves + w) .. +16 of an operand
     // block; lane L takes row 16 * (q * kWaves + w) + L / 4 and LDS slot L % 4, which holds the
@@ -302,11 +331,21 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
         int tile = l;
         kbeg = 0;
         nk = nk_all;
-        if (tail) {
-            tile = dp + unit / sp.split;
-            const int sg = unit % sp.split;
-            kbeg = sg * nk_all / sp.split;
-            nk = (sg + 1) * nk_all / sp.split - kbeg;
+        if (tail) {   // the next piece of this block's run: up to the end of the run or of the tile
+            const int i = static_cast<int>(g_run / nk_all);
+            const int64_t t0 = static_cast<int64_t>(i) * nk_all;
+            const int64_t t1 = min<int64_t>(g_end, t0 + nk_all);
+            kbeg = static_cast<int>(g_run - t0);
+            nk = static_cast<int>(t1 - g_run);
+            // the run holding stage q is run (blocks_x (q + 1) - 1) / w_x
+            const int first = static_cast<int>((blocks_x * (t0 + 1) - 1) / w_x);
+            const int last = static_cast<int>((blocks_x * (t0 + nk_all) - 1) / w_x);
+            ptile = xcd + kXcds * i;
+            pcount = last - first + 1;
+            pfirst = first;
+            pord = local - first;
+            tile = dp + ptile;
+            g_run = t1;
         }
         int tm, tn;
         tile_of(tile, tiles_m, tiles_n, &tm, &tn);
@@ -560,16 +599,19 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
         RTQ_BARRIER();   // every wave is done reading the ring
 
         const int64_t cm0 = m0, cn0 = n0;
-        const bool ctail = in_tail;
+        const bool ctail = in_tail && pcount > 1;   // a piece of a tile shared with another run
+        const int ctile = ptile, cfirst = pfirst, ccount = pcount, cord = pord;
         bool more = false;
         if (!in_tail) {
             if (lin + stride < lin_end) {
                 lin += stride;
                 more = true;
-            } else if (has_unit) {
+            } else if (g_run < g_end) {
                 in_tail = true;
                 more = true;
             }
+        } else {
+            more = g_run < g_end;
         }
         if (more) {
             set_item(in_tail, lin);
@@ -602,15 +644,30 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
         // the staging as whole rows); the last block of the tile to arrive runs the epilogue and
         // adds the other partials there
         bool epilogue = true;
-        int others = 0;                 // first unit of my tile, when summing partials
         // Partial layout: row-major int32 quads; with bf16 output (where a lane of the epilogue
         // reads quads 2c and 2c + 1 of a row) a wave's row slice holds its even quads, then its odd
         // ones, so each load instruction there reads whole lines.
         constexpr int kQuadsPerRow = WN / 4;
         auto quad_pos = [](int c) { return kYKind == 1 ? (c & 1) * (kQuadsPerRow / 2) + (c >> 1) : c; };
-        if (ctail) {
+        // Stream-K tiles have two pieces: the tile's head, the last piece of its run, and the tail,
+        // the first piece of the next run, which is nearly always done first.  The tail stores its
+        // partial and adds 1.  The head first adds 2: if the tail's 1 is there, the head finishes
+        // the tile without storing its own partial; otherwise it stores it and adds 4, and whoever
+        // then sees both the other's publication (1 or 4) finishes the tile.  Exactly one does,
+        // after both partials it reads are stored.
+        bool publish = ctail;
+        const bool sk = sp.split == 0;
+        const bool head = sk && cord == 0;
+        if (ctail && head) {
+            __syncthreads();
+            if (tid == 0) s_flag[0] = static_cast<int>(split_arrive(sp.counters + ctile, sp.epoch, 2u));
+            __syncthreads();
+            publish = (static_cast<unsigned int>(s_flag[0]) & 1u) == 0u;
+        }
+        if (publish) {
             const __amdgpu_buffer_rsrc_t rsm = __builtin_amdgcn_make_buffer_rsrc(
-                sp.partials + static_cast<size_t>(unit) * (BM * BN / 4), (short)0, BM * BN * 4, kBufferWord3);
+                sp.partials + static_cast<size_t>(piece_slot(cfirst, cord)) * (BM * BN / 4), (short)0, BM * BN * 4,
+                kBufferWord3);
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
                 stage_block(i);
@@ -629,16 +686,16 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
             // there, and the last block reads the partials with loads that bypass its own L1.
             RTQ_WAIT_ALL_VMEM();
             __syncthreads();
-            if (tid == 0)
-                s_flag[0] = split_arrive(sp.counters + (unit / sp.split), sp.epoch) ==
-                            static_cast<unsigned int>(sp.split - 1);
+            if (tid == 0) {
+                const unsigned int v = split_arrive(sp.counters + ctile, sp.epoch, sk ? (head ? 4u : 1u) : 1u);
+                s_flag[0] = sk ? (v & (head ? 1u : 4u)) != 0u : v == static_cast<unsigned int>(ccount - 1);
+            }
             __syncthreads();
             epilogue = s_flag[0] != 0;
-            others = unit - unit % sp.split;
         }
         // int32 quad (4 consecutive columns) at (row, col) of the tile: mine plus the other K ranges'
         const __amdgpu_buffer_rsrc_t rsp = __builtin_amdgcn_make_buffer_rsrc(
-            sp.partials + static_cast<size_t>(others) * (BM * BN / 4), (short)0, sp.split * BM * BN * 4, kBufferWord3);
+            sp.partials, (short)0, static_cast<int>(2 * gridDim.x * (BM * BN * 4)), kBufferWord3);
         // The other ranges' loads are issued back to back, so their latencies overlap (the branches
         // are uniform: the split and the block's own range).
         auto add_others = [&](v4i v, int row, int col) -> v4i {
@@ -647,9 +704,10 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
 #pragma unroll
                 for (int o = 0; o < kMaxSplit; ++o) {
                     part[o] = v4i{0, 0, 0, 0};
-                    if (o < sp.split && others + o != unit)
+                    if (o < ccount && o != cord)
                         part[o] = __builtin_amdgcn_raw_buffer_load_b128(
-                            rsp, (o * BM * BN + row * BN + wn * WN + 4 * quad_pos((col - wn * WN) >> 2)) * 4, 0, kLoadL2);
+                            rsp, (piece_slot(cfirst, o) * BM * BN + row * BN + wn * WN + 4 * quad_pos((col - wn * WN) >> 2)) * 4,
+                            0, kLoadL2);
                 }
 #pragma unroll
                 for (int o = 0; o < kMaxSplit; ++o) v += part[o];
@@ -815,27 +873,38 @@ hipError_t launch_config(const GemmI8Args& g, hipStream_t stream) {
     const int64_t slots = std::max<int64_t>(kXcds, cus / kXcds * kXcds);
     int64_t grid = std::min<int64_t>(slots, (total + kXcds - 1) / kXcds * kXcds);
     SplitArgs sp{static_cast<int>(total), 1, nullptr, nullptr, 0u};
-    // With a workspace, the tiles of a last round that would leave at least 3/4 of the slots idle
-    // are split along K over them: `rem` tiles, each in min(slots / rem, K stages / 16, kMaxSplit)
-    // ranges.  (Measured: a range shorter than 16 stages, or a last round that already fills half
-    // the slots, loses more to the partial tiles' traffic and the lower clock of a full chip than
-    // the split gains.)
+    // With a workspace, a partial last round is shared along K (tiles of at least 16 stages):
+    //  * after at least one full round: stream-K over the last full round and the remainder, so
+    //    every block runs the same number of K stages (measured 3% faster than leaving half the
+    //    blocks idle in a last half round, 9-10% at 1.125 rounds);
+    //  * with no full round, when the tiles would leave at least 3/4 of the slots idle: each of the
+    //    `rem` tiles in min(slots / rem, K stages / 16, kMaxSplit) equal ranges.
     if (g.workspace != nullptr && g.ws_bytes >= gemm_i8_workspace_bytes()) {
         const int64_t whole = total / slots * slots;
         const int64_t rem = total - whole;
-        int64_t split = rem > 0 && 4 * rem <= slots
-                            ? std::min<int64_t>(std::min<int64_t>(slots / rem, g.d / (16 * BK)),
-                                                std::min<int64_t>(slots / kXcds, kMaxSplit))
-                            : 0;
-        // a power of two: the blocks per XCD are a multiple of it, so a tile's pieces share an XCD
-        while (split & (split - 1)) split &= split - 1;
-        if ((slots / kXcds) % std::max<int64_t>(split, 1) != 0) split = 1;
-        if (split >= 2) {
+        const int64_t nk = g.d / BK;
+        int64_t dp = total, split = 1;
+        if (rem > 0 && nk >= 16) {
+            if (whole >= slots) {
+                dp = whole - slots;
+                split = 0;
+            } else if (4 * rem <= slots) {
+                split = std::min<int64_t>(std::min<int64_t>(slots / rem, nk / 16),
+                                          std::min<int64_t>(slots / kXcds, kMaxSplit));
+                // a power of two: the blocks per XCD are a multiple of it, so a tile's ranges share an XCD
+                while (split & (split - 1)) split &= split - 1;
+                if ((slots / kXcds) % split != 0) split = 1;
+                dp = split >= 2 ? whole : total;
+            }
+        }
+        if (dp < total) {
             unsigned int e = ++g_split_epoch;
             if (e == 0) e = ++g_split_epoch;
             unsigned char* ws = static_cast<unsigned char*>(g.workspace);
-            sp = SplitArgs{static_cast<int>(whole), static_cast<int>(split), reinterpret_cast<v4i*>(ws),
-                           reinterpret_cast<unsigned long long*>(ws + static_cast<size_t>(slots) * BM * BN * 4), e};
+            sp = SplitArgs{static_cast<int>(dp), static_cast<int>(split), reinterpret_cast<v4i*>(ws),
+                           reinterpret_cast<unsigned long long*>(
+                               ws + static_cast<size_t>(partial_slots_cap(slots)) * BM * BN * 4),
+                           e};
             grid = slots;
         }
     }
@@ -852,8 +921,9 @@ hipError_t launch_config(const GemmI8Args& g, hipStream_t stream) {
 size_t gemm_i8_workspace_bytes() {
     const int cus = device_cu_count();
     const int64_t slots = std::max<int64_t>(kXcds, cus / kXcds * kXcds);
-    // partial tiles (int32) and counters, one each per slot
-    return static_cast<size_t>(slots) * (static_cast<size_t>(BM) * BN * 4 + sizeof(unsigned long long));
+    // partial tiles (int32) and one counter per shared tile
+    return static_cast<size_t>(partial_slots_cap(slots)) * BM * BN * 4 +
+           static_cast<size_t>(shared_tiles_cap(slots)) * sizeof(unsigned long long);
 }
 
 hipError_t launch_gemm_i8(const GemmI8Args& g, hipStream_t stream) {

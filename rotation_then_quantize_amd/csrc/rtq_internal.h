@@ -77,8 +77,8 @@ struct GemmI8Args {
     const int32_t* a_sum = nullptr;
     const int32_t* w_zero = nullptr;
     const int32_t* w_sum = nullptr;
-    // optional workspace (gemm_i8_workspace_bytes()): lets the last, partial round of tiles be
-    // split along K over the otherwise idle CUs
+    // optional workspace (gemm_i8_workspace_bytes()): lets a partial last round of tiles be shared
+    // along K (stream-K runs, or equal K ranges per tile)
     void* workspace = nullptr;
     size_t ws_bytes = 0;
 };

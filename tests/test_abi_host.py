@@ -153,7 +153,9 @@ def test_qgemm_and_qlinear_validation():
     # workspace sizing and checks of the fused call
     ws = lib.rtq_rotated_qlinear_workspace
     split = lib.rtq_qgemm_workspace()
-    assert split % 16 == 0 and split >= 8 * (256 * 256 * 4 + 8)
+    # two int32 256 x 256 partial tiles and two counters per block slot (a multiple of 8 XCDs)
+    per_slot = 2 * (256 * 256 * 4 + 8)
+    assert split % 16 == 0 and split % per_slot == 0 and (split // per_slot) % 8 == 0 and split >= 8 * per_slot
     split256 = (split + 255) // 256 * 256
     assert ws(4608, 4096, rtq.RTQ_INT8, 8) == 4608 * 4096 + 4608 * 4 + (256 - (4608 * 4) % 256) % 256 + split256
     assert ws(4608, 4096, rtq.RTQ_CODEBOOK_I8, 4) == 4608 * 4096 + 18432 + split256

@@ -91,6 +91,28 @@ def test_qgemm_asym_accumulators_bit_exact(T, N, d):
     assert rel_fro(y.cpu().numpy().astype(np.float64), want) <= 1e-5
 
 
+def test_qgemm_asym_stream_k_sampled():
+    # 288 tiles at d = 1024: stream-K runs of 18 stages cross tile edges, and the zero-point terms
+    # are applied once, after the two partial sums are added
+    T, N, d = 4608, 4096, 1024
+    rng = np.random.default_rng(41)
+    qa = rng.integers(-128, 128, size=(T, d)).astype(np.int8)
+    qw = rng.integers(-128, 128, size=(N, d)).astype(np.int8)
+    za = rng.integers(-128, 128, size=T).astype(np.int32)
+    zw = rng.integers(-128, 128, size=N).astype(np.int32)
+    sa = qa.astype(np.int64).sum(1).astype(np.int32)
+    sw = qw.astype(np.int64).sum(1).astype(np.int32)
+    rows = np.concatenate([np.sort(rng.choice(T, 40, replace=False)), [0, T - 1]])
+    ref = oracle.gemm_int8_asym(qa[rows], za[rows], qw, zw)
+    ws = torch.empty(rtq.qgemm_workspace(), dtype=torch.uint8, device="cuda")
+    acc = torch.empty((T, N), dtype=torch.int32, device="cuda")
+    ones_t, ones_n = to_dev(np.ones(T, np.float32)), to_dev(np.ones(N, np.float32))
+    rtq.qgemm_asym(to_dev(qa), ones_t, to_dev(za), to_dev(sa), to_dev(qw), ones_n, to_dev(zw), to_dev(sw), acc, d,
+                   workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy()[rows].astype(np.int64), ref)
+
+
 @pytest.mark.parametrize("T,N,d", [(200, 256, 4096), (70, 130, 256), (33, 96, 16384)])
 def test_asym_layer_small(T, N, d):
     xf = workloads.small_case(1800 + d, T, d, "t3")

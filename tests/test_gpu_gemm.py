@@ -100,33 +100,42 @@ def test_codebook_gemm_matches_oracle(bits_w, yt):
 
 
 def test_int8_full_shape_sampled():
-    # W8A8 DiT shape in the launch configuration the benchmark times: 4608 x 4096 -> 16384.
+    # W8A8 DiT shape, 4608 x 4096 -> 16384 (1152 tiles: 4.5 rounds), launched whole and in the
+    # configuration the benchmark times (with the workspace: 3 whole rounds, then stream-K runs of
+    # 1.5 tiles over the last 384).
     T, N, d = 4608, 16384, 4096
     a = _codes(21, T, d)
     w = _codes(22, N, d)
-    acc = torch.empty((T, N), dtype=torch.int32, device="cuda")
-    rtq.qgemm(to_dev(a), to_dev(np.ones(T, np.float32)), to_dev(w), to_dev(np.ones(N, np.float32)), acc, d)
-    torch.cuda.synchronize()
     rng = np.random.default_rng(23)
     rows = np.sort(rng.choice(T, 48, replace=False))
     cols = np.sort(rng.choice(N, 48, replace=False))
     rows = np.concatenate([rows, [0, T - 1]])
     cols = np.concatenate([cols, [0, N - 1]])
     ref = oracle.gemm_int8(a[rows], w[cols])
-    got = acc.cpu().numpy()[np.ix_(rows, cols)].astype(np.int64)
-    assert np.array_equal(got, ref)
+    ws = torch.empty(rtq.qgemm_workspace(), dtype=torch.uint8, device="cuda")
+    for workspace in (None, ws):
+        acc = torch.empty((T, N), dtype=torch.int32, device="cuda")
+        rtq.qgemm(to_dev(a), to_dev(np.ones(T, np.float32)), to_dev(w), to_dev(np.ones(N, np.float32)), acc, d,
+                  workspace=workspace)
+        torch.cuda.synchronize()
+        got = acc.cpu().numpy()[np.ix_(rows, cols)].astype(np.int64)
+        assert np.array_equal(got, ref)
 
 
 # ---------------------------------------------------------------- K-split of the last round
 
 @pytest.mark.parametrize("T,N,d", [(130, 200, 256), (257, 129, 128), (64, 384, 4096), (33, 70, 16384),
-                                   (300, 700, 2048), (4608, 4096, 8192), (3328, 5376, 4096)])
+                                   (300, 700, 2048), (4608, 4096, 8192), (3328, 5376, 4096), (4608, 4096, 1024),
+                                   (2304, 8448, 2048), (4608, 8192, 4096)])
 def test_int8_ksplit_accumulators_bit_exact(T, N, d):
-    # with a workspace the tiles of a last round that leaves most compute units idle are split
-    # along d; the pieces add exactly in int32.  On 256 CUs: d < 2048 never splits; one tile at
-    # d = 4096 / 16384 splits 4 / 8 ways; 300 x 700 x 2048 is 6 tiles split 2 ways; 4608 x 4096 is
-    # 288 tiles: one whole round, then 32 tiles split 8 ways; 3328 x 5376 is 273 tiles: 17 split
-    # 4 ways, dealt unevenly over the 8 XCDs (3 on the first, 2 on each other).
+    # with a workspace a last round that leaves most compute units idle is shared along d; the
+    # pieces add exactly in int32.  On 256 CUs: d < 1024 never shares; with no full round, one
+    # tile at d = 4096 / 16384 splits 4 / 8 ways and 300 x 700 x 2048 is 6 tiles split 2 ways.
+    # After a full round, stream-K: every block runs an equal run of K stages across tile edges,
+    # a tile meeting at most two runs.  4608 x 4096 x 8192 is 288 tiles (runs of 1.125 tiles);
+    # 3328 x 5376 is 273 tiles, dealt unevenly over the 8 XCDs (35 on the first, 34 on the
+    # others); 4608 x 4096 x 1024 has runs of 18 stages; 2304 x 8448 is 297 tiles; 4608 x 8192 is
+    # 576 tiles: one whole round, then 320 tiles shared.
     a = _codes(11 + T, T, d)
     w = _codes(12 + N, N, d)
     ws = torch.full((rtq.qgemm_workspace(),), 0x5A, dtype=torch.uint8, device="cuda")   # arbitrary contents
@@ -146,7 +155,7 @@ def test_int8_ksplit_accumulators_bit_exact(T, N, d):
 @pytest.mark.parametrize("T,N,d", [(300, 700, 2048), (3328, 5376, 4096)])
 def test_ksplit_outputs_equal_unsplit(yt, T, N, d):
     # exact int32 sums, then the same epilogue: split and unsplit products agree bit for bit
-    # (6 tiles split 2 ways; 17 of 273 tiles split 4 ways)
+    # (6 tiles split 2 ways; 273 tiles shared by stream-K runs)
     a = _codes(21, T, d)
     w = _codes(22, N, d)
     rng = np.random.default_rng(23)

@@ -112,8 +112,9 @@ def test_lowbit_gemm_integer_part_and_bound(bits_w, bits_a, T, N, d):
 
 
 def test_three_bit_weights_with_k_split_bit_exact_integer_part():
-    # 288 tiles of 256 x 256 with d = 8192: the last round is split along d; the decode of 24-byte
-    # rows at each range's start must match the unsplit product exactly (same int32 sums)
+    # 288 tiles of 256 x 256 with d = 8192: the tiles are shared along d by stream-K runs; the
+    # decode of 24-byte rows at each range's start must match the unsplit product exactly (same
+    # int32 sums)
     T, N, d = 4608, 4096, 8192
     rng = np.random.default_rng(5)
     qa = rng.integers(0, 8, size=(T, d)).astype(np.uint8)
@@ -208,7 +209,7 @@ def test_split_workspace_shared_across_weight_widths():
     # One workspace reused by products of different weight widths (different kernel variants):
     # the split counters' launch tags come from one sequence, so a counter left by one variant is
     # never read as the current launch's arrivals.  Each split product must equal the unsplit one.
-    T, N, d = 4608, 4096, 4096          # 288 tiles: the last round is split along d
+    T, N, d = 4608, 4096, 4096          # 288 tiles: shared along d by stream-K runs
     rng = np.random.default_rng(17)
     ws = torch.empty(rtq.qgemm_workspace(), dtype=torch.uint8, device="cuda")
     s_a = to_dev(np.ones(T, np.float32))
