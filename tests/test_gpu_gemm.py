@@ -126,7 +126,7 @@ def test_int8_full_shape_sampled():
 
 @pytest.mark.parametrize("T,N,d", [(130, 200, 256), (257, 129, 128), (64, 384, 4096), (33, 70, 16384),
                                    (300, 700, 2048), (4608, 4096, 8192), (3328, 5376, 4096), (4608, 4096, 1024),
-                                   (2304, 8448, 2048), (4608, 8192, 4096)])
+                                   (2304, 8448, 2048), (4608, 8192, 4096), (4100, 4100, 1024)])
 def test_int8_ksplit_accumulators_bit_exact(T, N, d):
     # with a workspace a last round that leaves most compute units idle is shared along d; the
     # pieces add exactly in int32.  On 256 CUs: d < 1024 never shares; with no full round, one
@@ -135,7 +135,8 @@ def test_int8_ksplit_accumulators_bit_exact(T, N, d):
     # a tile meeting at most two runs.  4608 x 4096 x 8192 is 288 tiles (runs of 1.125 tiles);
     # 3328 x 5376 is 273 tiles, dealt unevenly over the 8 XCDs (35 on the first, 34 on the
     # others); 4608 x 4096 x 1024 has runs of 18 stages; 2304 x 8448 is 297 tiles; 4608 x 8192 is
-    # 576 tiles: one whole round, then 320 tiles shared.
+    # 576 tiles: one whole round, then 320 tiles shared; 4100 x 4100 is 289 tiles with ragged
+    # last rows and columns (N % 8 != 0: per-element stores).
     a = _codes(11 + T, T, d)
     w = _codes(12 + N, N, d)
     ws = torch.full((rtq.qgemm_workspace(),), 0x5A, dtype=torch.uint8, device="cuda")   # arbitrary contents
@@ -152,10 +153,11 @@ def test_int8_ksplit_accumulators_bit_exact(T, N, d):
 
 
 @pytest.mark.parametrize("yt", ["f32", "bf16"])
-@pytest.mark.parametrize("T,N,d", [(300, 700, 2048), (3328, 5376, 4096)])
+@pytest.mark.parametrize("T,N,d", [(300, 700, 2048), (3328, 5376, 4096), (4100, 4100, 1024)])
 def test_ksplit_outputs_equal_unsplit(yt, T, N, d):
     # exact int32 sums, then the same epilogue: split and unsplit products agree bit for bit
-    # (6 tiles split 2 ways; 273 tiles shared by stream-K runs)
+    # (6 tiles split 2 ways; 273 and 289 tiles shared by stream-K runs, the latter with ragged
+    # edges and N % 8 != 0)
     a = _codes(21, T, d)
     w = _codes(22, N, d)
     rng = np.random.default_rng(23)
