@@ -506,12 +506,12 @@ __device__ __forceinline__ void quantize_block(double (&acc)[kH], const unsigned
             }
             // (the wave's LDS accesses execute in order: its reads below see these writes)
             const uint2* rt = ctab + (cc.lane_base / row_lanes) * kCells;
-            const float ka = 8.0f * cc.grid_k / dn;       // table bytes per unit of x'
-            constexpr float kMid = 4.0f * kCells, kTop = 8.0f * kCells - 1.0f;
+            const float ka = cc.grid_k / dn;              // cells per unit of x'
+            constexpr float kMid = 0.5f * kCells, kTop = kCells - 0.125f;
 #pragma unroll
             for (int b = 0; b < kH; ++b) {
                 const int a = static_cast<int>(__builtin_amdgcn_fmed3f(fmaf(xr[b], ka, kMid), 0.0f, kTop));
-                const uint2 e = rt[a >> 3];
+                const uint2 e = rt[a];
                 const bool ge = xr[b] >= __uint_as_float(e.x);
                 if constexpr (kLut)
                     put_bits(b, (e.y >> (ge ? 16 : 8)) & 0xffu);
