@@ -773,6 +773,15 @@ rpbh_quant_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int 
 //      writes), transforms, quantises and stores, while its next unit's loads are in flight.
 constexpr int kUnit = 4096;
 constexpr int kWaveBuf = 64 * kBlockPitch;
+
+// LDS addresses as 32-bit integers: a store through an LDS-space pointer formed from the integer
+// takes a constant addend into the instruction's offset field.
+typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
+typedef __attribute__((address_space(3))) unsigned char lds_u8_t;
+__device__ __forceinline__ uint32_t lds_address(unsigned char* p) {
+    return static_cast<uint32_t>(reinterpret_cast<size_t>((lds_u8_t*)p));
+}
+__device__ __forceinline__ void lds_store_u16(uint32_t addr, uint16_t v) { *(lds_u16_t*)(size_t)addr = v; }
 constexpr int kWaveMaxD = 4096;
 
 template <int kOut>
@@ -782,20 +791,25 @@ rpbh_wave_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int l
                       void* __restrict__ scale_out, int scale_bf16, const float* __restrict__ bounds, float eps,
                       const float* __restrict__ cent, RowExtra ex) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    // LDS: [scatter offset of each source column, u32[d]][its sign mask, u16[d]][one buffer per wave]
-    uint32_t* tab_off = reinterpret_cast<uint32_t*>(smem);
-    uint16_t* tab_sgn = reinterpret_cast<uint16_t*>(smem + 4 * d);
+    // LDS: [one buffer per wave][scatter offset of each source column, u32[d]][its sign mask,
+    // u16[d]][code tables].  The wave buffers come first, at offsets known when compiling, so the
+    // d = 4096 staging below folds a wave's buffer base into each store's offset field.
+    constexpr int kWaves = kThreads / 64;
+    uint32_t* tab_off = reinterpret_cast<uint32_t*>(smem + kWaves * kWaveBuf);
+    uint16_t* tab_sgn = reinterpret_cast<uint16_t*>(smem + kWaves * kWaveBuf + 4 * d);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    unsigned char* buf = smem + 6 * d + wave * kWaveBuf;
-    uint2* ctab0 = reinterpret_cast<uint2*>(smem + 6 * d + (kThreads / 64) * kWaveBuf);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    unsigned char* buf = smem + wave * kWaveBuf;
+    uint2* ctab0 = reinterpret_cast<uint2*>(smem + kWaves * kWaveBuf + 6 * d);
     uint2* ctab = ctab0 + wave * (CodeCtx<kOut>::kTabBytes / 8);
     const int log2nb = log2d - 6;
     const uint32_t dmask = static_cast<uint32_t>(d - 1);
 
     // Destination position j (block j / 64, slot j % 64) takes source column perm[j] with sign
-    // signs[j]: the table entry of that column holds j's LDS offset and sign bit.
+    // signs[j]: the table entry of that column holds j's LDS address within wave 0's buffer (the
+    // LDS address of smem plus its offset there) and sign bit.
+    const uint32_t lds0 = lds_address(smem);
     for (int j = 4 * tid; j < d; j += 4 * kThreads) {
         const int4 pv = *reinterpret_cast<const int4*>(perm + j);
         const uint32_t sv = *reinterpret_cast<const uint32_t*>(signs + j);
@@ -804,7 +818,7 @@ rpbh_wave_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int l
         for (int e = 0; e < 4; ++e) {
             const uint32_t c = static_cast<uint32_t>(pj[e]) & dmask;
             const uint32_t jj = static_cast<uint32_t>(j + e);
-            tab_off[c] = (jj >> 6) * kBlockPitch + (jj & 63u) * 2u;
+            tab_off[c] = lds0 + (jj >> 6) * kBlockPitch + (jj & 63u) * 2u;
             tab_sgn[c] = (sv >> (8 * e + 7)) & 1u ? 0x8000u : 0u;
         }
     }
@@ -841,22 +855,39 @@ rpbh_wave_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int l
     BlockOut res;
     int64_t res_row = -1;
     const int blk = lane & ((1 << log2nb) - 1);
+    // ---- stage: signs, then scatter each element to its rotated block slot (chunk i of the
+    // unit lies in row pos >> log2d of the unit, whose blocks start at rb)
+    auto stage_chunk = [&](int i, uint32_t rb, uint32_t col) {
+        const uint4 m = *reinterpret_cast<const uint4*>(tab_sgn + col);
+        const uint4 o0 = *reinterpret_cast<const uint4*>(tab_off + col);
+        const uint4 o1 = *reinterpret_cast<const uint4*>(tab_off + col + 4);
+        const uint32_t w[4] = {pre[i].x ^ m.x, pre[i].y ^ m.y, pre[i].z ^ m.z, pre[i].w ^ m.w};
+        const uint32_t off[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            lds_store_u16(off[k] + rb, static_cast<uint16_t>((k & 1) ? (w[k >> 1] >> 16) : (w[k >> 1] & 0xffffu)));
+    };
+    // d = 4096: one row per unit, the wave's buffer at a constant distance from wave 0's, which the
+    // compiler folds into each store's offset field
+    auto stage_row = [&](uint32_t rb) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) stage_chunk(i, rb, 512u * i + 8u * lane);
+    };
     for (; u < units; u += nwaves) {
-        // ---- stage: signs, then scatter each element to its rotated block slot
+        if (d == kUnit) {
+            static_assert(kWaves == 4, "one staging case per wave");
+            switch (wave) {
+                case 0: stage_row(0u * kWaveBuf); break;
+                case 1: stage_row(1u * kWaveBuf); break;
+                case 2: stage_row(2u * kWaveBuf); break;
+                default: stage_row(3u * kWaveBuf); break;
+            }
+        } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t pos = 512u * i + 8u * lane;
-            const uint32_t col = pos & dmask;
-            unsigned char* rb = buf + (pos >> log2d) * row_bytes;
-            const uint4 m = *reinterpret_cast<const uint4*>(tab_sgn + col);
-            const uint4 o0 = *reinterpret_cast<const uint4*>(tab_off + col);
-            const uint4 o1 = *reinterpret_cast<const uint4*>(tab_off + col + 4);
-            const uint32_t w[4] = {pre[i].x ^ m.x, pre[i].y ^ m.y, pre[i].z ^ m.z, pre[i].w ^ m.w};
-            const uint32_t off[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-                *reinterpret_cast<uint16_t*>(rb + off[k]) =
-                    static_cast<uint16_t>((k & 1) ? (w[k >> 1] >> 16) : (w[k >> 1] & 0xffffu));
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t pos = 512u * i + 8u * lane;
+                stage_chunk(i, static_cast<uint32_t>(wave) * kWaveBuf + (pos >> log2d) * row_bytes, pos & dmask);
+            }
         }
         if (res_row >= 0 && res_row < rows) store_block<kOut>(res, out, scale_out, scale_bf16, ex, res_row, blk, d);
         if (u + nwaves < units) load_unit(u + nwaves);
