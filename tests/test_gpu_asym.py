@@ -113,6 +113,32 @@ def test_qgemm_asym_stream_k_sampled():
     assert np.array_equal(acc.cpu().numpy()[rows].astype(np.int64), ref)
 
 
+@pytest.mark.parametrize("yt", ["f32", "bf16"])
+def test_qgemm_asym_stream_k_equals_whole(yt):
+    # 289 tiles with ragged edges and N % 8 != 0: the stream-K product (partials added before
+    # the zero-point terms and the scales) equals the product launched whole, bit for bit
+    T, N, d = 4100, 4100, 1024
+    rng = np.random.default_rng(43)
+    qa = rng.integers(-128, 128, size=(T, d)).astype(np.int8)
+    qw = rng.integers(-128, 128, size=(N, d)).astype(np.int8)
+    za = rng.integers(-128, 128, size=T).astype(np.int32)
+    zw = rng.integers(-128, 128, size=N).astype(np.int32)
+    sa = qa.astype(np.int64).sum(1).astype(np.int32)
+    sw = qw.astype(np.int64).sum(1).astype(np.int32)
+    s_a = to_dev((rng.random(T) * 0.1 + 0.01).astype(np.float32))
+    r_w = to_dev(oracle.to_bf16_bits(rng.random(N) * 0.1 + 0.01), "bf16")
+    dt = torch.float32 if yt == "f32" else torch.bfloat16
+    args = (to_dev(qa), s_a, to_dev(za), to_dev(sa), to_dev(qw), r_w, to_dev(zw), to_dev(sw))
+    y0 = torch.empty((T, N), dtype=dt, device="cuda")
+    y1 = torch.empty((T, N), dtype=dt, device="cuda")
+    rtq.qgemm_asym(*args, y0, d)
+    ws = torch.empty(rtq.qgemm_workspace(), dtype=torch.uint8, device="cuda")
+    rtq.qgemm_asym(*args, y1, d, workspace=ws)
+    torch.cuda.synchronize()
+    iv = torch.int32 if yt == "f32" else torch.int16
+    assert torch.equal(y0.view(iv), y1.view(iv))
+
+
 @pytest.mark.parametrize("T,N,d", [(200, 256, 4096), (70, 130, 256), (33, 96, 16384)])
 def test_asym_layer_small(T, N, d):
     xf = workloads.small_case(1800 + d, T, d, "t3")
