@@ -503,7 +503,7 @@ def main():
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU: the rotated linear is measured at "
-                                   "its single-GPU shape; multi-GPU sharding is not part of this build",
+                                   "its single-GPU shape; multi-GPU sharding is not implemented",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
