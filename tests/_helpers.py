@@ -27,7 +27,7 @@ def dense_pi(seed: int, d: int):
 
 
 def int8_mismatches_allowed(q_gpu, q_orc, pre_orc):
-    """North-star allowance for INT8 codes: equal, or one step apart where the oracle's fp32
+    """Allowance for INT8 codes: equal, or one step apart where the oracle's fp32
     pre-rounding value lies within 1e-6 relative of the rounding boundary k + 1/2."""
     diff = q_gpu.astype(np.int32) - q_orc.astype(np.int32)
     bad = diff != 0

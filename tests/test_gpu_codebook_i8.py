@@ -6,7 +6,7 @@ header states).  So the tests check two things separately:
   * the integer part is exact: activation values are the table entries of the oracle's codes
     (same boundary allowance as the packed codes), and the product equals the int64 product of
     the tables, rescaled by a_scale * w_scale / (S_a S_w), to fp32/bf16 rounding;
-  * the whole layer stays within the benchmark spec's bound (2e-2 relative Frobenius, bf16 output) of
+  * the whole layer stays within the layer's bound (2e-2 relative Frobenius, bf16 output) of
     the oracle's exact-centroid product.
 The table is computed here from the oracle's centroids with numpy fp32 arithmetic (the rule in
 include/rtq.h), independently of the library."""

@@ -1,7 +1,7 @@
 """GPU parity of the quantised products (INT8 MFMA and codebook-LUT MFMA) against the oracle.
 
 INT8 accumulators must be bit-exact; rescaled outputs within the stated relative Frobenius bounds
-(1e-4 fp32 output; 2e-2 bf16 output, spec tolerance) and, where both sides round the same
+(1e-4 fp32 output; 2e-2 bf16 output, the layer's tolerance) and, where both sides round the same
 fp32/fp64 value to bf16, within one bf16 ulp elementwise."""
 import numpy as np
 import pytest
