@@ -875,8 +875,8 @@ hipError_t launch_config(const GemmI8Args& g, hipStream_t stream) {
     SplitArgs sp{static_cast<int>(total), 1, nullptr, nullptr, 0u};
     // With a workspace, a partial last round is shared along K (tiles of at least 16 stages):
     //  * after at least one full round: stream-K over the last full round and the remainder, so
-    //    every block runs the same number of K stages (measured 3% faster than leaving half the
-    //    blocks idle in a last half round, 9-10% at 1.125 rounds);
+    //    every block runs the same number of K stages (measured up to 3% faster than leaving half
+    //    the blocks idle in a last half round, 8-11% at 1.125 rounds);
     //  * with no full round, when the tiles would leave at least 3/4 of the slots idle: each of the
     //    `rem` tiles in min(slots / rem, K stages / 16, kMaxSplit) equal ranges.
     if (g.workspace != nullptr && g.ws_bytes >= gemm_i8_workspace_bytes()) {

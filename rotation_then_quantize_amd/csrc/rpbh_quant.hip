@@ -1,8 +1,9 @@
 // rpbh_quant.hip -- the hot RPBH rotate + quantise kernel for bf16 rows on gfx950.
 //
-// Same arithmetic as rpbh_rows.hip (x' = Pi_d x via exact fp64 butterflies, OrbitQuant article
-// 2.3; INT8 s = max|x'|/127, q = rne(x'/s), cloud.baidu.com/article/9432521 4; Lloyd-Max codes of
-// x'/(||x'|| + eps), OrbitQuant article 2.1-2.2), organised for HBM throughput:
+// Same arithmetic as rpbh_rows.hip (x' = Pi_d x via fp64 butterflies, exact while a block's
+// magnitudes span at most 2^39, OrbitQuant article 2.3; INT8 s = max|x'|/127, q = rne(x'/s),
+// cloud.baidu.com/article/9432521 4; Lloyd-Max codes of x'/(||x'|| + eps), OrbitQuant article
+// 2.1-2.2), organised for HBM throughput:
 //
 //  * Scatter on staging.  Each lane loads 16-byte chunks of bf16 inputs and writes each element
 //    straight to the LDS slot of the rotated block it feeds (the inverse permutation, as LDS
