@@ -76,7 +76,9 @@ def _source_sha256(*names):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = {"gemm_i8_kernel": ("gemm_i8.hip",), "rpbh_wave_bf16_kernel": ("rpbh_quant.hip",)}
+# each kernel's source and the headers it includes: counters taken before any of them changed are stale
+KERNEL_SOURCES = {"gemm_i8_kernel": ("gemm_i8.hip", "codebook_int8.h", "rtq_internal.h"),
+                  "rpbh_wave_bf16_kernel": ("rpbh_quant.hip", "codebook_int8.h", "rtq_internal.h")}
 
 
 def _traffic(kernel):
