@@ -49,7 +49,7 @@ typedef enum {
 typedef enum {
     RTQ_F32 = 0,  /* IEEE binary32                                               */
     RTQ_BF16 = 1, /* bfloat16 bit patterns (uint16), rounded to nearest-even      */
-    RTQ_I32 = 2   /* int32 accumulators: rtq_qgemm output in INT8 mode only      */
+    RTQ_I32 = 2   /* int32 accumulators: rtq_qgemm output (INT8, CODEBOOK_I8)   */
 } rtq_dtype;
 
 typedef enum {
@@ -139,15 +139,19 @@ rtq_status rtq_quantize_rows(const void* x, rtq_dtype xt, int64_t rows, int32_t 
  *   token norm); w_codes [N][d] or [N][d*bits_w/8], w_scale [N] of w_scale_t (F32 or BF16).
  *   INT8:      acc[t][n] = sum_j a[t][j] w[n][j] exactly in int32 (|acc| <= 127^2 d);
  *              y = acc * a_scale[t] * w_scale[n] (fp32 arithmetic), stored as yt (F32 or BF16);
- *              yt == RTQ_I32 stores acc itself.  cb_a and cb_w must be NULL.
+ *              yt == RTQ_I32 stores acc itself.  cb_a and cb_w must be NULL.  N <= 2^22 for BF16
+ *              output, N <= 2^21 for F32 and I32 (else RTQ_ERR_UNSUPPORTED).
  *   CODEBOOK:  y = w_scale[n] * a_scale[t] * sum_j cb_w->centroids[qw] * cb_a->centroids[qa],
- *              accumulated in fp32 from fp16 copies of the centroids; yt F32 or BF16.
+ *              accumulated in fp32 from fp16 copies of the centroids; yt must be BF16.
  *              cb_a->bits must be 4; cb_w->bits 2 or 4.
  *   CODEBOOK_I8: a_codes int8[T][d] holds the activations' int8 codebook values (rtq_quantize_rows
  *              in this mode), w_codes packed codes [N][d*bits_w/8]; acc = sum_j a[t][j] v_w[qw]
- *              exactly in int32, y = acc * a_scale[t] * w_scale[n] / (S_a S_w) in fp32; yt F32 or
- *              BF16.  cb_a (centroids, bits 2, 3, 4 or 6) gives S_a; cb_w (centroids, bits 2, 3 or
- *              4) the weight values.  N <= 2^22, d a multiple of 64.
+ *              exactly in int32, y = acc * a_scale[t] * w_scale[n] / (S_a S_w) in fp32; yt BF16,
+ *              or RTQ_I32 for acc itself.  cb_a (centroids, bits 2, 3, 4 or 6) gives S_a; cb_w
+ *              (centroids, bits 2, 3 or 4) the weight values.  N <= 2^22 (BF16), 2^21 (I32).
+ *   The codebook modes give bf16 output (yt == RTQ_F32 returns RTQ_ERR_UNSUPPORTED): their
+ *   centroid rounding (fp16 copies, or int8 values) is sized for the bf16 output bound, not for
+ *   an fp32 one.
  * T == 0 is a no-op. */
 rtq_status rtq_qgemm(const void* a_codes, const float* a_scale, int64_t T, const void* w_codes,
                      const void* w_scale, rtq_dtype w_scale_t, int64_t N, int32_t d, rtq_qmode mode,
@@ -161,9 +165,10 @@ rtq_status rtq_qgemm(const void* a_codes, const float* a_scale, int64_t T, const
  * in the workspace, and the last piece of the tile to finish adds the others (exact int32 sums, so
  * results equal rtq_qgemm's bit for bit).
  *   workspace: device memory of at least rtq_qgemm_workspace() bytes, 16-byte aligned, any
- *   contents (per-tile arrival counters carry a launch tag, so no clearing is needed).  Launches
- *   that share a workspace must not run concurrently.  A smaller or NULL workspace, or the
- *   RTQ_CODEBOOK mode, gives exactly rtq_qgemm. */
+ *   contents: when the split is used, the call first zeroes the per-tile arrival counters with a
+ *   small fill kernel on `stream` (no memset node, so the call may be captured in a graph).
+ *   Launches that share a workspace must not run concurrently.  A smaller or NULL workspace, or
+ *   the RTQ_CODEBOOK mode, gives exactly rtq_qgemm. */
 rtq_status rtq_qgemm_ws(const void* a_codes, const float* a_scale, int64_t T, const void* w_codes,
                         const void* w_scale, rtq_dtype w_scale_t, int64_t N, int32_t d, rtq_qmode mode,
                         const rtq_codebook* cb_a, const rtq_codebook* cb_w, void* y, rtq_dtype yt,
@@ -177,7 +182,9 @@ size_t rtq_qgemm_workspace(void);
  * followed by rtq_qgemm on the same stream (OrbitQuant article, section 2.2, steps 1-5 and the
  * cancellation).  Weights come from rtq_quantize_rows with the SAME descriptor R.
  *   workspace: device memory of at least rtq_rotated_qlinear_workspace(T, R->d, mode, bits_a) bytes,
- *   16-byte aligned; on return it starts with the activation codes and scales. */
+ *   16-byte aligned, any contents (the quantiser launch zeroes the product's split counters); on
+ *   return it starts with the activation codes and scales.  Calls sharing a workspace must not
+ *   overlap.  yt: F32 or BF16 for RTQ_INT8, BF16 for the codebook modes. */
 rtq_status rtq_rotated_qlinear(const void* x, rtq_dtype xt, int64_t T, const rtq_rpbh* R, const void* w_codes,
                                const void* w_scale, rtq_dtype w_scale_t, int64_t N, rtq_qmode mode,
                                const rtq_codebook* cb_a, const rtq_codebook* cb_w, void* y, rtq_dtype yt,

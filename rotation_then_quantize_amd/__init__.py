@@ -133,6 +133,16 @@ def _ptr(t) -> int:
     return 0 if t is None else int(t.data_ptr())
 
 
+def _stream_local_workspace(torch, nbytes: int, device, stream):
+    """A temporary workspace for one call.  torch's caching allocator may hand its memory to other
+    work once it is freed; recording the launch stream makes that wait for the call's kernels when
+    they run on a stream other than the current one."""
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if stream is not None:
+        ws.record_stream(stream)
+    return ws
+
+
 def _stream(stream) -> int:
     torch = _torch()
     if stream is None:
@@ -249,7 +259,7 @@ def rotated_qlinear(x, R: Rpbh, w_codes, w_scale, y, mode: int = RTQ_INT8, cb_a:
     bits_a = cb_a.bits if (mode in (RTQ_CODEBOOK, RTQ_CODEBOOK_I8) and cb_a is not None) else 8
     need = rotated_qlinear_workspace(T, R.d, mode, bits_a)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+        workspace = _stream_local_workspace(torch, max(need, 16), x.device, stream)
     _check(load_library().rtq_rotated_qlinear(_ptr(x), _dtype_code(x), T, R.c, _ptr(w_codes), _ptr(w_scale),
                                               _dtype_code(w_scale), w_codes.shape[0], mode, _cb(cb_a), _cb(cb_w),
                                               _ptr(y), _dtype_code(y), _ptr(workspace), workspace.numel(),
@@ -288,7 +298,7 @@ def rotated_qlinear_asym(x, R: Rpbh, w_codes, w_scale, w_zero, w_sum, y, workspa
     torch = _torch()
     T = x.shape[0]
     if workspace is None:
-        workspace = torch.empty(max(rotated_qlinear_asym_workspace(T, R.d), 16), dtype=torch.uint8, device=x.device)
+        workspace = _stream_local_workspace(torch, max(rotated_qlinear_asym_workspace(T, R.d), 16), x.device, stream)
     _check(load_library().rtq_rotated_qlinear_asym(_ptr(x), _dtype_code(x), T, R.c, _ptr(w_codes), _ptr(w_scale),
                                                    _dtype_code(w_scale), _ptr(w_zero), _ptr(w_sum), w_codes.shape[0],
                                                    _ptr(y), _dtype_code(y), _ptr(workspace), workspace.numel(),

@@ -173,16 +173,16 @@ __device__ __forceinline__ void decode3(const uint32_t (&lut)[4], const uint32_t
 // run meets a tile only in part stores its int32 partial tile and arrives on the tile's counter;
 // the last to arrive adds the others' partials and runs the epilogue (no block ever waits for
 // another; a stream-K tile's second piece to finish skips its own store, see the epilogue).
-// Counters hold (epoch << 32) | arrivals; a counter from an earlier launch (other epoch) counts
-// as zero, so the workspace needs no clearing.
+// The counters are zero when the launch starts: a fill kernel (or the quantiser launch that
+// precedes the product on the same stream) clears them, so arrivals are counted from a known
+// state whatever the workspace held before.
 constexpr int kMaxSplit = 8;
 
 struct SplitArgs {
     int dp_tiles;
     int split;                      // 1: no shared tiles; >= 2: equal K ranges per tile; 0: stream-K
     v4i* partials;                  // [block][2][BM * BN / 4] int32 quads (below)
-    unsigned long long* counters;   // [shared tile]
-    unsigned int epoch;
+    unsigned long long* counters;   // [shared tile], zero at launch
 };
 
 // Workspace per block slot (one block per compute unit): two partial tiles, since a run meets at
@@ -191,18 +191,15 @@ struct SplitArgs {
 constexpr int64_t partial_slots_cap(int64_t slots) { return 2 * slots; }
 constexpr int64_t shared_tiles_cap(int64_t slots) { return 2 * slots; }
 
-// Add `add` to a shared tile's counter; returns its low word before, as this launch left it
-// (0 if the counter still holds an earlier launch's tag).
-__device__ unsigned int split_arrive(unsigned long long* c, unsigned int epoch, unsigned int add) {
-    unsigned long long cur = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (int i = 0; i < (1 << 20); ++i) {   // lock-free: each failed exchange means another block's succeeded
-        const bool same = static_cast<unsigned int>(cur >> 32) == epoch;
-        const unsigned long long next = same ? cur + add : ((static_cast<unsigned long long>(epoch) << 32) | add);
-        const unsigned long long seen = atomicCAS(c, cur, next);
-        if (seen == cur) return same ? static_cast<unsigned int>(cur) : 0u;
-        cur = seen;
-    }
-    return 0xffffffffu;
+// Add `add` to a shared tile's counter (an atomic at the L2 of the XCD that runs every piece of
+// the tile); returns the arrivals before this one.
+__device__ __forceinline__ unsigned int split_arrive(unsigned long long* c, unsigned int add) {
+    return static_cast<unsigned int>(
+        __hip_atomic_fetch_add(c, static_cast<unsigned long long>(add), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+__global__ void __launch_bounds__(256) split_clear_kernel(unsigned long long* __restrict__ c, int n) {
+    for (int i = static_cast<int>(threadIdx.x); i < n; i += 256) c[i] = 0ull;
 }
 
 // Tile index within the XCD-ordered sequence -> (tile_m, tile_n), in bands of 8 N-tiles.
@@ -244,7 +241,6 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
     constexpr bool kCoded = kWBits < 8;
     constexpr int kRawStage = raw_stage_bytes(kWBits);
     constexpr int kCodeLoads = kWBits == 4 ? 1 : (kWBits == 3 ? 3 : 2);   // LDS-writing loads per thread per code stage
-    static_assert(!kCoded || kYKind != 2, "raw accumulators only for int8 weights");
     constexpr int kThreads = 64 * kWaves;
     constexpr int WN = BN / kWavesN;                           // columns per wave
     constexpr int TM = WM / 32, TN = WN / 32;                  // MFMA tiles per wave
@@ -660,7 +656,7 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
         const bool head = sk && cord == 0;
         if (ctail && head) {
             __syncthreads();
-            if (tid == 0) s_flag[0] = static_cast<int>(split_arrive(sp.counters + ctile, sp.epoch, 2u));
+            if (tid == 0) s_flag[0] = static_cast<int>(split_arrive(sp.counters + ctile, 2u));
             __syncthreads();
             publish = (static_cast<unsigned int>(s_flag[0]) & 1u) == 0u;
         }
@@ -687,7 +683,7 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
             RTQ_WAIT_ALL_VMEM();
             __syncthreads();
             if (tid == 0) {
-                const unsigned int v = split_arrive(sp.counters + ctile, sp.epoch, sk ? (head ? 4u : 1u) : 1u);
+                const unsigned int v = split_arrive(sp.counters + ctile, sk ? (head ? 4u : 1u) : 1u);
                 s_flag[0] = sk ? (v & (head ? 1u : 4u)) != 0u : v == static_cast<unsigned int>(ccount - 1);
             }
             __syncthreads();
@@ -827,16 +823,11 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
     }
 }
 
-// The launch tag of the split counters.  One sequence for every kernel variant: a workspace may
-// pass between products of different weight widths (or be recycled by an allocator), and a tag
-// reused from another variant's sequence would read that launch's arrivals as this one's.
-std::atomic<unsigned int> g_split_epoch{0};
-
 template <int kWavesN, int kWBits, bool kAsym>
 hipError_t launch_config(const GemmI8Args& g, hipStream_t stream) {
     using KernelFn = void (*)(const int8_t*, const float*, const int8_t*, const void*, int64_t, int64_t, int,
                               void*, int, int, const float*, int, const float*, SplitArgs, AsymArgs);
-    constexpr int kYKinds = kWBits == 8 ? 3 : 2;   // raw int32 output only for int8 weights
+    constexpr int kYKinds = 3;   // fp32, bf16, raw int32 accumulators
     constexpr int kLdsBytes = lds_bytes(kWBits) + (kAsym ? kAsymBytes : 0);
     static_assert(kLdsBytes <= 160 * 1024, "LDS");
     // [w_scale bf16][N % 8 == 0][y kind]
@@ -872,7 +863,7 @@ hipError_t launch_config(const GemmI8Args& g, hipStream_t stream) {
     if (cus <= 0) return hipErrorInvalidDevice;
     const int64_t slots = std::max<int64_t>(kXcds, cus / kXcds * kXcds);
     int64_t grid = std::min<int64_t>(slots, (total + kXcds - 1) / kXcds * kXcds);
-    SplitArgs sp{static_cast<int>(total), 1, nullptr, nullptr, 0u};
+    SplitArgs sp{static_cast<int>(total), 1, nullptr, nullptr};
     // With a workspace, a partial last round is shared along K (tiles of at least 16 stages):
     //  * after at least one full round: stream-K over the last full round and the remainder, so
     //    every block runs the same number of K stages (measured up to 3% faster than leaving half
@@ -898,14 +889,17 @@ hipError_t launch_config(const GemmI8Args& g, hipStream_t stream) {
             }
         }
         if (dp < total) {
-            unsigned int e = ++g_split_epoch;
-            if (e == 0) e = ++g_split_epoch;
             unsigned char* ws = static_cast<unsigned char*>(g.workspace);
             sp = SplitArgs{static_cast<int>(dp), static_cast<int>(split), reinterpret_cast<v4i*>(ws),
                            reinterpret_cast<unsigned long long*>(
-                               ws + static_cast<size_t>(partial_slots_cap(slots)) * BM * BN * 4),
-                           e};
+                               ws + static_cast<size_t>(partial_slots_cap(slots)) * BM * BN * 4)};
             grid = slots;
+            if (!g.counters_zeroed) {
+                hipLaunchKernelGGL(split_clear_kernel, dim3(1), dim3(256), 0, stream, sp.counters,
+                                   static_cast<int>(shared_tiles_cap(slots)));
+                const hipError_t ce = hipGetLastError();
+                if (ce != hipSuccess) return ce;
+            }
         }
     }
     const KernelFn k = kernels[g.w_scale_bf16 ? 1 : 0][(g.N % 8) == 0 ? 1 : 0][g.y_kind];
@@ -926,10 +920,30 @@ size_t gemm_i8_workspace_bytes() {
            static_cast<size_t>(shared_tiles_cap(slots)) * sizeof(unsigned long long);
 }
 
+unsigned long long* gemm_i8_split_counters(void* workspace, size_t ws_bytes, int* n) {
+    *n = 0;
+    if (workspace == nullptr || ws_bytes < gemm_i8_workspace_bytes()) return nullptr;
+    const int cus = device_cu_count();
+    const int64_t slots = std::max<int64_t>(kXcds, cus / kXcds * kXcds);
+    *n = static_cast<int>(shared_tiles_cap(slots));
+    return reinterpret_cast<unsigned long long*>(static_cast<unsigned char*>(workspace) +
+                                                 static_cast<size_t>(partial_slots_cap(slots)) * BM * BN * 4);
+}
+
+hipError_t launch_split_clear(unsigned long long* counters, int n, hipStream_t stream) {
+    if (counters == nullptr || n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(split_clear_kernel, dim3(1), dim3(256), 0, stream, counters, n);
+    return hipGetLastError();
+}
+
+int64_t gemm_i8_max_n(int y_kind) { return y_kind == 1 ? (int64_t(1) << 22) : (int64_t(1) << 21); }
+
 hipError_t launch_gemm_i8(const GemmI8Args& g, hipStream_t stream) {
     if (g.T <= 0 || g.N <= 0) return hipSuccess;
     if (g.d % BK != 0 || g.d > 16384) return hipErrorInvalidValue;
-    if (g.N > (int64_t(1) << 22)) return hipErrorInvalidValue;   // 32-bit store offsets within a row block
+    // the epilogue's store descriptor spans one 256-row block of Y (at most 2^31 bytes, so its
+    // byte offsets and the out-of-range sentinel 2^31 fit its 32-bit range)
+    if (g.N > gemm_i8_max_n(g.y_kind)) return hipErrorInvalidValue;
     const bool asym = g.a_zero != nullptr;
     if (asym != (g.a_sum != nullptr) || asym != (g.w_zero != nullptr) || asym != (g.w_sum != nullptr))
         return hipErrorInvalidValue;

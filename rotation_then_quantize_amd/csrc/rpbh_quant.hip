@@ -301,7 +301,15 @@ struct BlockOut {
 struct RowExtra {
     int32_t* zero;
     int32_t* sum;
+    unsigned long long* clear;   // words the first workgroup zeroes (the next product's split counters)
+    int nclear;
 };
+
+// The first workgroup zeroes the words the launch was asked to clear.
+__device__ __forceinline__ void clear_words(const RowExtra& ex) {
+    if (blockIdx.x == 0)
+        for (int i = static_cast<int>(threadIdx.x); i < ex.nclear; i += static_cast<int>(blockDim.x)) ex.clear[i] = 0ull;
+}
 
 // Bytes per output element (8 codes per 64 bits for 4-bit codes etc., in bits).
 template <int kOut>
@@ -605,6 +613,7 @@ rpbh_quant_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int 
                        void* __restrict__ scale_out, int scale_bf16, const float* __restrict__ bounds, float eps,
                        const float* __restrict__ cent, RowExtra ex) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    clear_words(ex);
     // LDS: [row buffer(s) | prologue scratch overlaid][sign masks, d x u16 (kNC >= 4)][reduction]
     // d <= 4096: two row buffers, so staging group g+1 never waits for readers of group g
     // (one barrier per group).  d >= 8192: one buffer plus the persistent sign-mask table.
@@ -792,6 +801,7 @@ rpbh_wave_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int l
                       void* __restrict__ scale_out, int scale_bf16, const float* __restrict__ bounds, float eps,
                       const float* __restrict__ cent, RowExtra ex) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    clear_words(ex);
     // LDS: [one buffer per wave][scatter offset of each source column, u32[d]][its sign mask,
     // u16[d]][code tables].  The wave buffers come first, at offsets known when compiling, so the
     // d = 4096 staging below folds a wave's buffer base into each store's offset field.
@@ -916,7 +926,7 @@ hipError_t launch_wave(const RowArgs& a, int log2d, hipStream_t stream) {
     const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(cap, (units + kThreads / 64 - 1) / (kThreads / 64)));
     hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), lds, stream,
                        static_cast<const uint16_t*>(a.x), a.rows, a.d, log2d, a.perm, a.signs, a.out, a.scale,
-                       a.scale_bf16 ? 1 : 0, a.bounds, a.eps, a.centroids, RowExtra{a.zero, a.sum});
+                       a.scale_bf16 ? 1 : 0, a.bounds, a.eps, a.centroids, RowExtra{a.zero, a.sum, a.clear, a.nclear});
     return hipGetLastError();
 }
 
@@ -939,7 +949,7 @@ hipError_t launch_t(const RowArgs& a, int log2d, hipStream_t stream) {
     const int grid = static_cast<int>((ngroups + per_wg - 1) / per_wg);
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), lds, stream, static_cast<const uint16_t*>(a.x), a.rows,
                        a.d, log2d, log2nb, a.perm, a.signs, a.out, a.scale, a.scale_bf16 ? 1 : 0, a.bounds, a.eps,
-                       a.centroids, RowExtra{a.zero, a.sum});
+                       a.centroids, RowExtra{a.zero, a.sum, a.clear, a.nclear});
     return hipGetLastError();
 }
 

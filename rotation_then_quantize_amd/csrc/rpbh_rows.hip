@@ -452,10 +452,12 @@ hipError_t launch_rows_kind(const RowArgs& a, hipStream_t stream) {
 
 hipError_t launch_rpbh_rows(const RowArgs& a, hipStream_t stream) {
     if (a.rows <= 0) return hipSuccess;
-    if (rpbh_quant_bf16_supported(a)) return launch_rpbh_quant_bf16(a, stream);
+    if (rpbh_quant_bf16_supported(a)) return launch_rpbh_quant_bf16(a, stream);   // it zeroes a.clear itself
     const bool rot = a.perm != nullptr;
-    if (a.x_bf16) return rot ? launch_rows_kind<true, true>(a, stream) : launch_rows_kind<true, false>(a, stream);
-    return rot ? launch_rows_kind<false, true>(a, stream) : launch_rows_kind<false, false>(a, stream);
+    const hipError_t e = a.x_bf16 ? (rot ? launch_rows_kind<true, true>(a, stream) : launch_rows_kind<true, false>(a, stream))
+                                  : (rot ? launch_rows_kind<false, true>(a, stream) : launch_rows_kind<false, false>(a, stream));
+    if (e != hipSuccess) return e;
+    return launch_split_clear(a.clear, a.nclear, stream);
 }
 
 hipError_t launch_rpbh_inverse(const void* y, bool y_bf16, void* x, bool x_bf16, int64_t rows, int d,

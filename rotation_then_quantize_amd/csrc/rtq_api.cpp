@@ -164,6 +164,10 @@ rtq_status plan_gemm(const void* a_codes, const float* a_scale, int64_t T, const
     if (mode == RTQ_INT8) {
         if (cb_a != nullptr || cb_w != nullptr) return fail(RTQ_ERR_INVALID_ARG, "codebooks must be NULL for RTQ_INT8");
         if (yt != RTQ_F32 && yt != RTQ_BF16 && yt != RTQ_I32) return fail(RTQ_ERR_UNSUPPORTED, "bad yt");
+        const int y_kind = yt == RTQ_F32 ? 0 : (yt == RTQ_BF16 ? 1 : 2);
+        if (N > rtq::gemm_i8_max_n(y_kind))
+            return fail(RTQ_ERR_UNSUPPORTED, "N too large for this output type (max %lld)",
+                        static_cast<long long>(rtq::gemm_i8_max_n(y_kind)));
         p.lut = false;
         p.i8 = rtq::GemmI8Args{static_cast<const int8_t*>(a_codes), a_scale, static_cast<const int8_t*>(w_codes),
                                w_scale, w_scale_t == RTQ_BF16, T, N, d, y,
@@ -174,7 +178,7 @@ rtq_status plan_gemm(const void* a_codes, const float* a_scale, int64_t T, const
         if (cb_a->bits != 4) return fail(RTQ_ERR_UNSUPPORTED, "activation codes must be 4-bit (got %d)", cb_a->bits);
         if (cb_w->bits != 2 && cb_w->bits != 4)
             return fail(RTQ_ERR_UNSUPPORTED, "RTQ_CODEBOOK weight codes must be 2- or 4-bit (got %d)", cb_w->bits);
-        if (yt != RTQ_F32 && yt != RTQ_BF16) return fail(RTQ_ERR_UNSUPPORTED, "yt must be RTQ_F32 or RTQ_BF16");
+        if (yt != RTQ_BF16) return fail(RTQ_ERR_UNSUPPORTED, "codebook products give bf16 output (yt must be RTQ_BF16)");
         p.lut = true;
         p.cb = rtq::GemmLutArgs{static_cast<const uint8_t*>(a_codes), a_scale, static_cast<const uint8_t*>(w_codes),
                                 w_scale, w_scale_t == RTQ_BF16, cb_a->centroids, cb_w->centroids, cb_a->bits,
@@ -183,11 +187,16 @@ rtq_status plan_gemm(const void* a_codes, const float* a_scale, int64_t T, const
         RTQ_TRY(check_codebook(cb_a, "cb_a", true, false));
         RTQ_TRY(check_codebook(cb_w, "cb_w", true, false));
         if (cb_w->bits == 6) return fail(RTQ_ERR_UNSUPPORTED, "weight codes must be 2-, 3- or 4-bit (got 6)");
-        if (yt != RTQ_F32 && yt != RTQ_BF16) return fail(RTQ_ERR_UNSUPPORTED, "yt must be RTQ_F32 or RTQ_BF16");
-        if (N > (int64_t(1) << 22)) return fail(RTQ_ERR_UNSUPPORTED, "N too large (max %d)", 1 << 22);
+        if (yt != RTQ_BF16 && yt != RTQ_I32)
+            return fail(RTQ_ERR_UNSUPPORTED, "codebook products give bf16 output (yt must be RTQ_BF16, or RTQ_I32 "
+                                             "for the raw int8-value accumulators)");
+        const int y_kind = yt == RTQ_BF16 ? 1 : 2;
+        if (N > rtq::gemm_i8_max_n(y_kind))
+            return fail(RTQ_ERR_UNSUPPORTED, "N too large for this output type (max %lld)",
+                        static_cast<long long>(rtq::gemm_i8_max_n(y_kind)));
         p.lut = false;
         p.i8 = rtq::GemmI8Args{static_cast<const int8_t*>(a_codes), a_scale, static_cast<const int8_t*>(w_codes),
-                               w_scale, w_scale_t == RTQ_BF16, T, N, d, y, yt == RTQ_F32 ? 0 : 1};
+                               w_scale, w_scale_t == RTQ_BF16, T, N, d, y, y_kind};
         p.i8.w_bits = cb_w->bits;
         p.i8.cent_a = cb_a->centroids;
         p.i8.a_bits = cb_a->bits;
@@ -363,11 +372,16 @@ rtq_status rtq_rotated_qlinear(const void* x, rtq_dtype xt, int64_t T, const rtq
     RTQ_TRY(plan_gemm(a_codes, a_scale, T, w_codes, w_scale, w_scale_t, N, d, mode, cb_a, cb_w, y, yt, &gp));
     if (T == 0) return ok();
     hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t split_off = align256(code_bytes) + align256(static_cast<size_t>(T) * sizeof(float));
+    if (!gp.lut) {
+        // the quantiser launch zeroes the product's split counters (when the workspace has them)
+        gp.i8.workspace = ws + split_off;
+        gp.i8.ws_bytes = ws_bytes - split_off;
+        qa.clear = rtq::gemm_i8_split_counters(gp.i8.workspace, gp.i8.ws_bytes, &qa.nclear);
+        gp.i8.counters_zeroed = true;
+    }
     RTQ_TRY(hip_status(rtq::launch_rpbh_rows(qa, s), "rpbh_rows launch"));
     if (gp.lut) return hip_status(rtq::launch_gemm_lut(gp.cb, s), "gemm_lut launch");
-    const size_t split_off = align256(code_bytes) + align256(static_cast<size_t>(T) * sizeof(float));
-    gp.i8.workspace = ws + split_off;
-    gp.i8.ws_bytes = ws_bytes - split_off;
     return hip_status(rtq::launch_gemm_i8(gp.i8, s), "gemm_i8 launch");
 }
 
@@ -441,9 +455,11 @@ rtq_status rtq_rotated_qlinear_asym(const void* x, rtq_dtype xt, int64_t T, cons
                            &gp));
     if (T == 0) return ok();
     hipStream_t s = static_cast<hipStream_t>(stream);
-    RTQ_TRY(hip_status(rtq::launch_rpbh_rows(qa, s), "rpbh_rows launch"));
     gp.i8.workspace = ws + off;
     gp.i8.ws_bytes = ws_bytes - off;
+    qa.clear = rtq::gemm_i8_split_counters(gp.i8.workspace, gp.i8.ws_bytes, &qa.nclear);
+    gp.i8.counters_zeroed = true;
+    RTQ_TRY(hip_status(rtq::launch_rpbh_rows(qa, s), "rpbh_rows launch"));
     return hip_status(rtq::launch_gemm_i8(gp.i8, s), "gemm_i8 launch");
 }
 

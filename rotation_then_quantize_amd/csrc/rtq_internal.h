@@ -38,6 +38,9 @@ struct RowArgs {
     const float* centroids = nullptr;   // codebook centroids (device), 2^bits entries (kRowLut*)
     int32_t* zero = nullptr;            // kRowInt8Asym: per-row zero point
     int32_t* sum = nullptr;             // kRowInt8Asym: per-row sum of the codes
+    // words zeroed by the launch (the K-split counters of the product that follows on the stream)
+    unsigned long long* clear = nullptr;
+    int nclear = 0;
 };
 
 hipError_t launch_rpbh_rows(const RowArgs& a, hipStream_t stream);
@@ -81,12 +84,21 @@ struct GemmI8Args {
     // along K (stream-K runs, or equal K ranges per tile)
     void* workspace = nullptr;
     size_t ws_bytes = 0;
+    // the workspace's split counters were zeroed earlier on this stream (by the quantiser launch):
+    // no fill kernel is needed before the product
+    bool counters_zeroed = false;
 };
 
 hipError_t launch_gemm_i8(const GemmI8Args& g, hipStream_t stream);
-// Workspace bytes for the K-split of launch_gemm_i8 on the current device (partial int32 tiles
-// for up to one per CU, plus one counter per CU).
+// Workspace bytes for the K-split of launch_gemm_i8 on the current device (two partial int32
+// tiles and two counters per CU slot).
 size_t gemm_i8_workspace_bytes();
+// The split counters inside a workspace of ws_bytes (nullptr and *n = 0 if it has no split region).
+unsigned long long* gemm_i8_split_counters(void* workspace, size_t ws_bytes, int* n);
+// Zero n counter words on the stream (a fill kernel: safe under graph capture).
+hipError_t launch_split_clear(unsigned long long* counters, int n, hipStream_t stream);
+// Largest N the INT8-core product takes for an output kind (0 fp32, 1 bf16, 2 int32).
+int64_t gemm_i8_max_n(int y_kind);
 
 struct GemmLutArgs {
     const uint8_t* a;         // [T][d*bits_a/8] packed codes

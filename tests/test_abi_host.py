@@ -150,6 +150,19 @@ def test_qgemm_and_qlinear_validation():
     assert call({8: rtq.RTQ_CODEBOOK_I8, 9: ctypes.byref(cb4), 10: ctypes.byref(cb6)}) == rtq.RTQ_ERR_UNSUPPORTED
     assert call({8: rtq.RTQ_CODEBOOK_I8, 9: ctypes.byref(cb6), 10: ctypes.byref(cb3), 2: 0}) == rtq.RTQ_OK
     assert call({2: 0}) == rtq.RTQ_OK                                    # T = 0 is a no-op
+    # codebook products give bf16 output only: fp32 output is refused in both codebook modes
+    assert call({8: rtq.RTQ_CODEBOOK, 9: ctypes.byref(cb4), 10: ctypes.byref(cb4), 12: rtq.RTQ_F32, 2: 0}) == \
+        rtq.RTQ_ERR_UNSUPPORTED
+    assert "bf16" in rtq.last_error()
+    assert call({8: rtq.RTQ_CODEBOOK_I8, 9: ctypes.byref(cb4), 10: ctypes.byref(cb4), 12: rtq.RTQ_F32, 2: 0}) == \
+        rtq.RTQ_ERR_UNSUPPORTED
+    assert call({8: rtq.RTQ_CODEBOOK_I8, 9: ctypes.byref(cb4), 10: ctypes.byref(cb4), 2: 0}) == rtq.RTQ_OK
+    # output-row limits of the INT8-core product: one 256-row block of y spans at most 2^31 bytes
+    assert call({6: (1 << 21) + 8, 12: rtq.RTQ_F32, 2: 0}) == rtq.RTQ_ERR_UNSUPPORTED
+    assert call({6: (1 << 21) + 8, 12: rtq.RTQ_I32, 2: 0}) == rtq.RTQ_ERR_UNSUPPORTED
+    assert call({6: 1 << 21, 12: rtq.RTQ_F32, 2: 0}) == rtq.RTQ_OK
+    assert call({6: (1 << 21) + 8, 12: rtq.RTQ_BF16, 2: 0}) == rtq.RTQ_OK
+    assert call({6: (1 << 22) + 8, 12: rtq.RTQ_BF16, 2: 0}) == rtq.RTQ_ERR_UNSUPPORTED
     # workspace sizing and checks of the fused call
     ws = lib.rtq_rotated_qlinear_workspace
     split = lib.rtq_qgemm_workspace()
@@ -174,6 +187,10 @@ def test_qgemm_and_qlinear_validation():
     assert ql(*a) == rtq.RTQ_ERR_UNSUPPORTED
     a = list(args); a[2] = 0
     assert ql(*a) == rtq.RTQ_OK
+    # codebook layers: bf16 output only
+    a = list(args); a[8] = rtq.RTQ_CODEBOOK_I8; a[9] = ctypes.byref(cb4); a[10] = ctypes.byref(cb4)
+    a[12] = rtq.RTQ_F32; a[2] = 0
+    assert ql(*a) == rtq.RTQ_ERR_UNSUPPORTED
 
 
 def test_rotate_validation():

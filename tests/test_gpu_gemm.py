@@ -76,8 +76,7 @@ def test_int8_rescale_epilogue(yt):
 
 
 @pytest.mark.parametrize("bits_w", [4, 2])
-@pytest.mark.parametrize("yt", ["f32", "bf16"])
-def test_codebook_gemm_matches_oracle(bits_w, yt):
+def test_codebook_gemm_matches_oracle(bits_w):
     T, N, d = 140, 260, 1024
     rng = np.random.default_rng(10 + bits_w)
     qa = rng.integers(0, 16, size=(T, d)).astype(np.uint8)
@@ -89,14 +88,15 @@ def test_codebook_gemm_matches_oracle(bits_w, yt):
     s_a = (rng.random(T) * 10 + 1).astype(np.float32)
     r_wb = oracle.to_bf16_bits(rng.random(N) + 0.5)
     r_w = oracle.bf16_bits_to_f32(r_wb)
-    y = torch.empty((T, N), dtype=torch.float32 if yt == "f32" else torch.bfloat16, device="cuda")
+    y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
     rtq.qgemm(to_dev(oracle.pack(qa, 4)), to_dev(s_a), to_dev(oracle.pack(qw, bits_w)), to_dev(r_wb, "bf16"), y, d,
               rtq.RTQ_CODEBOOK, cb_a, cb_w)
     ref = oracle.gemm_codebook(qa, qw, ca, cw, s_a, r_w)
-    got = y.cpu().numpy().astype(np.float64) if yt == "f32" else oracle.bf16_bits_to_f32(bf16_host(y))
+    got = oracle.bf16_bits_to_f32(bf16_host(y))
     err = rel_fro(got, ref)
-    # fp16 copies of the centroids (2^-11 relative rounding) bound the error well below this
-    assert err <= (1e-3 if yt == "f32" else 2e-2), err
+    # fp16 copies of the centroids (2^-11 relative rounding), fp32 sums and the bf16 output
+    assert err <= 2e-2, err
+    assert np.max(np.abs(got - ref)) <= 1e-2 * np.abs(ref).max()
 
 
 def test_int8_full_shape_sampled():
@@ -145,7 +145,7 @@ def test_int8_ksplit_accumulators_bit_exact(T, N, d):
     da, dw = to_dev(a), to_dev(w)
     rows = np.arange(T) if T * N <= 1 << 17 else np.sort(np.random.default_rng(3).choice(T, 40, replace=False))
     ref = oracle.gemm_int8(a[rows], w)
-    for _ in range(3):   # the same workspace again: per-launch counter tags
+    for _ in range(3):   # the same workspace again: counters cleared before each launch
         acc.fill_(0)
         rtq.qgemm(da, ones_t, dw, ones_n, acc, d, workspace=ws)
         torch.cuda.synchronize()
@@ -172,3 +172,28 @@ def test_ksplit_outputs_equal_unsplit(yt, T, N, d):
     torch.cuda.synchronize()
     assert torch.equal(y0.view(torch.int16) if yt == "bf16" else y0.view(torch.int32),
                        y1.view(torch.int16) if yt == "bf16" else y1.view(torch.int32))
+
+
+def test_split_counters_cleared_whatever_the_workspace_held():
+    # The split counters are zeroed by a fill kernel before each split launch, so stale words in
+    # the workspace never count as arrivals: here every counter word starts with small values a
+    # previous launch could have left (1, 2, 4 and their sums are the stream-K publication bits)
+    # and the rest of the workspace holds int32 partial-tile-like data.  Split and unsplit
+    # products must agree bit for bit on two launches in a row.
+    T, N, d = 4608, 4096, 4096                    # 288 tiles: all shared by stream-K runs
+    a = to_dev(_codes(31, T, d))
+    w = to_dev(_codes(32, N, d))
+    ones_t, ones_n = to_dev(np.ones(T, np.float32)), to_dev(np.ones(N, np.float32))
+    acc0 = torch.empty((T, N), dtype=torch.int32, device="cuda")
+    rtq.qgemm(a, ones_t, w, ones_n, acc0, d)
+    nbytes = rtq.qgemm_workspace()
+    ws = torch.randint(-1000, 1000, (nbytes // 4,), dtype=torch.int32, device="cuda")
+    slots = nbytes // (2 * (256 * 256 * 4 + 8))
+    counters = ws.view(torch.int64)[-2 * slots:]
+    counters.copy_(torch.arange(2 * slots, device="cuda", dtype=torch.int64) % 8)
+    for _ in range(2):
+        acc1 = torch.full((T, N), -1, dtype=torch.int32, device="cuda")
+        rtq.qgemm(a, ones_t, w, ones_n, acc1, d, workspace=ws.view(torch.uint8))
+        torch.cuda.synchronize()
+        assert torch.equal(acc0, acc1)
+        counters.copy_(torch.full_like(counters, 5))

@@ -12,6 +12,8 @@ import pytest
 import oracle
 import rotation_then_quantize_amd as rtq
 import workloads
+import _dit_cases as dit_cases
+from _dit_cases import bf16_within_one_ulp
 from _helpers import bf16_host, codebook_mismatches_allowed, codes_of, dense_pi, int8_table, rel_fro, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -98,15 +100,18 @@ def test_lowbit_gemm_integer_part_and_bound(bits_w, bits_a, T, N, d):
     s_a = (rng.random(T) * 10 + 1).astype(np.float32)
     r_wb = oracle.to_bf16_bits(rng.random(N) + 0.5)
     r_w = oracle.bf16_bits_to_f32(r_wb)
-    for yt in ("f32", "bf16"):
-        y = torch.empty((T, N), dtype=torch.float32 if yt == "f32" else torch.bfloat16, device="cuda")
+    acc = ta[qa].astype(np.int64) @ tw[qw].astype(np.int64).T
+    for yt in ("i32", "bf16"):
+        y = torch.empty((T, N), dtype=torch.int32 if yt == "i32" else torch.bfloat16, device="cuda")
         rtq.qgemm(to_dev(ta[qa]), to_dev(s_a), to_dev(oracle.pack(qw, bits_w)), to_dev(r_wb, "bf16"), y, d,
                   rtq.RTQ_CODEBOOK_I8, rtq.Codebook.for_dim(d, bits_a), rtq.Codebook.for_dim(d, bits_w))
         torch.cuda.synchronize()
-        got = y.cpu().numpy().astype(np.float64) if yt == "f32" else oracle.bf16_bits_to_f32(bf16_host(y))
-        acc = ta[qa].astype(np.int64) @ tw[qw].astype(np.int64).T
+        if yt == "i32":   # raw accumulators: the int64 product of the tables, bit for bit
+            assert np.array_equal(y.cpu().numpy().astype(np.int64), acc)
+            continue
+        got = oracle.bf16_bits_to_f32(bf16_host(y))
         y_int = acc * s_a.astype(np.float64)[:, None] * r_w.astype(np.float64)[None, :] / (float(sa_i) * float(sw_i))
-        assert rel_fro(got, y_int) <= (1e-5 if yt == "f32" else 4e-3)
+        assert np.all(bf16_within_one_ulp(got, y_int))
         ref = oracle.gemm_codebook(qa, qw, ocb_a["centroids"], ocb_w["centroids"], s_a, r_w)
         assert rel_fro(got, ref) <= 2e-2
 
@@ -125,19 +130,16 @@ def test_three_bit_weights_with_k_split_bit_exact_integer_part():
     w = to_dev(oracle.pack(qw, 3))
     s_a = to_dev(np.ones(T, np.float32))
     s_w = to_dev(np.ones(N, np.float32))
-    y0 = torch.empty((T, N), dtype=torch.float32, device="cuda")
-    y1 = torch.empty((T, N), dtype=torch.float32, device="cuda")
+    y0 = torch.empty((T, N), dtype=torch.int32, device="cuda")
+    y1 = torch.empty((T, N), dtype=torch.int32, device="cuda")
     rtq.qgemm(a, s_a, w, s_w, y0, d, rtq.RTQ_CODEBOOK_I8, cb, cb)
     ws = torch.empty(rtq.qgemm_workspace(), dtype=torch.uint8, device="cuda")
     rtq.qgemm(a, s_a, w, s_w, y1, d, rtq.RTQ_CODEBOOK_I8, cb, cb, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(y0, y1)
     rows = np.array([0, 1000, 4607])
-    _, tw = int8_table(oracle.lloyd_max(3, d)["centroids"])
-    sa_i = int8_table(oracle.lloyd_max(3, d)["centroids"])[0]
-    acc = ta[qa[rows]].astype(np.int64) @ tw[qw].astype(np.int64).T
-    ref = acc / (float(sa_i) * float(sa_i))
-    assert rel_fro(y1.cpu().numpy()[rows].astype(np.float64), ref) <= 1e-6
+    acc = ta[qa[rows]].astype(np.int64) @ ta[qw].astype(np.int64).T
+    assert np.array_equal(y1.cpu().numpy()[rows].astype(np.int64), acc)
 
 
 @pytest.mark.parametrize("bits_w,bits_a,T,N,d", [(3, 3, 200, 256, 4096), (4, 6, 130, 200, 4096), (3, 3, 70, 96, 256),
@@ -173,13 +175,13 @@ def test_lowbit_layer_small(bits_w, bits_a, T, N, d):
 
 @pytest.mark.parametrize("variant", ["w3a3", "w4a6"])
 def test_lowbit_dit_shape_sampled(variant):
-    # the benchmark's layers at the attention-output shape (4608 x 4096 -> 4096), full launches
-    d, N = workloads.DIT_HIDDEN, workloads.DIT_HIDDEN
-    bits_w, bits_a = (3, 3) if variant == "w3a3" else (4, 6)
+    # the benchmark's layers at the attention-output shape (4608 x 4096 -> 4096), full launches;
+    # 64 tokens x 256 channels covering every output tile
+    ref = dit_cases.codebook_sample(variant)
+    d, N, bits_w, bits_a = ref["d"], ref["N"], ref["bits_w"], ref["bits_a"]
     xh, wh = workloads.dit_activations_bf16(d), workloads.w4a4_weight_bf16()
     T = xh.shape[0]
-    seed = workloads.RPBH_SEED[d]
-    R = rtq.Rpbh.from_seed(seed, d)
+    R = rtq.Rpbh.from_seed(workloads.RPBH_SEED[d], d)
     cb_a, cb_w = rtq.Codebook.for_dim(d, bits_a), rtq.Codebook.for_dim(d, bits_w)
     wcodes = torch.empty((N, d * bits_w // 8), dtype=torch.uint8, device="cuda")
     wnorm = torch.empty(N, dtype=torch.bfloat16, device="cuda")
@@ -189,26 +191,23 @@ def test_lowbit_dit_shape_sampled(variant):
                        device="cuda")
     rtq.rotated_qlinear(to_dev(xh, "bf16"), R, wcodes, wnorm, y, rtq.RTQ_CODEBOOK_I8, cb_a, cb_w, workspace=work)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(98)
-    rows = np.concatenate([[T - 1], np.sort(rng.choice(np.arange(0, T - 1), 7, replace=False))])
-    cols = np.concatenate([[N - 1], np.sort(rng.choice(np.arange(0, N - 1), 23, replace=False))])
-    pi = dense_pi(seed, d)
-    ocb_a, ocb_w = oracle.lloyd_max(bits_a, d), oracle.lloyd_max(bits_w, d)
-    wo = oracle.weights_codebook(workloads.bf16_bits_to_f32(wh[cols]), pi, ocb_w, bits_w)
-    ao = oracle.activations_codebook(workloads.bf16_bits_to_f32(xh[rows]), pi, ocb_a, bits_a)
-    _, ta = int8_table(ocb_a["centroids"])
-    a_codes = codes_of(work[:T * d].view(T, d).cpu().numpy().view(np.int8)[rows], ta)
+    rows, cols, wo, ao = ref["rows"], ref["cols"], ref["wo"], ref["ao"]
+    ocb_a, ocb_w = ref["ocb_a"], ref["ocb_w"]
+    w_codes = oracle.unpack(wcodes.cpu().numpy()[cols], d, bits_w)
+    assert codebook_mismatches_allowed(w_codes, wo["codes"], wo["u"], ocb_w["boundaries"], d)[1] == 0
+    a_codes = codes_of(work[:T * d].view(T, d).cpu().numpy().view(np.int8)[rows], ref["ta"])
     assert codebook_mismatches_allowed(a_codes, ao["codes"], ao["u"], ocb_a["boundaries"], d)[1] == 0
-    ref = oracle.gemm_codebook(ao["codes"], wo["codes"], ocb_a["centroids"], ocb_w["centroids"], ao["norm"],
-                               wo["norm"])
     got = workloads.bf16_bits_to_f32(bf16_host(y))[np.ix_(rows, cols)]
-    assert rel_fro(got, ref) <= 2e-2
+    assert rel_fro(got, ref["y"]) <= 2e-2
+    same = np.all(a_codes == ao["codes"], axis=1)[:, None] & np.all(w_codes == wo["codes"], axis=1)[None, :]
+    assert same.mean() > 0.9
+    assert np.all(bf16_within_one_ulp(got, ref["y_int8"])[same])
 
 
 def test_split_workspace_shared_across_weight_widths():
     # One workspace reused by products of different weight widths (different kernel variants):
-    # the split counters' launch tags come from one sequence, so a counter left by one variant is
-    # never read as the current launch's arrivals.  Each split product must equal the unsplit one.
+    # the split counters are zeroed before every split launch, so arrivals left by one variant are
+    # never read as the current launch's.  Each split product must equal the unsplit one.
     T, N, d = 4608, 4096, 4096          # 288 tiles: shared along d by stream-K runs
     rng = np.random.default_rng(17)
     ws = torch.empty(rtq.qgemm_workspace(), dtype=torch.uint8, device="cuda")
@@ -220,8 +219,8 @@ def test_split_workspace_shared_across_weight_widths():
         qa = to_dev(rng.integers(-127, 128, size=(T, d)).astype(np.int8))
         qw = to_dev(oracle.pack(rng.integers(0, 1 << bits_w, size=(N, d)).astype(np.uint8), bits_w))
         cb_w = rtq.Codebook.for_dim(d, bits_w)
-        y0 = torch.empty((T, N), dtype=torch.float32, device="cuda")
-        y1 = torch.full((T, N), float("nan"), dtype=torch.float32, device="cuda")
+        y0 = torch.empty((T, N), dtype=torch.int32, device="cuda")
+        y1 = torch.full((T, N), -1, dtype=torch.int32, device="cuda")
         rtq.qgemm(qa, s_a, qw, s_w, y0, d, rtq.RTQ_CODEBOOK_I8, cb4, cb_w)
         rtq.qgemm(qa, s_a, qw, s_w, y1, d, rtq.RTQ_CODEBOOK_I8, cb4, cb_w, workspace=ws)
         torch.cuda.synchronize()

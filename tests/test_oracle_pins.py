@@ -422,6 +422,29 @@ def test_int8_gemm_matches_integer_matmul():
     assert oracle.gemm_int8(full, -full)[0, 0] == -127 * 127 * 16384
 
 
+def test_int8_rescale_is_the_dequantised_product():
+    # y = (s_a q_a) . (s_w q_w) = s_a s_w sum_j q_a q_w ([CR2] section 4: W ~ s q).  With power-of-two
+    # scales every product and sum below is exact in fp64, so the oracle's rescale of the integer
+    # product must equal the product of the dequantised operands bit for bit; T != N and distinct
+    # scales per row and column catch a transposed or swapped scale.
+    rng = np.random.default_rng(12)
+    T, N, d = 5, 9, 128
+    qa = rng.integers(-127, 128, size=(T, d)).astype(np.int8)
+    qw = rng.integers(-127, 128, size=(N, d)).astype(np.int8)
+    sa = np.ldexp(1.0, rng.integers(-12, -2, size=T)).astype(np.float32)
+    sw = np.ldexp(1.0, rng.integers(-20, -8, size=N)).astype(np.float32)
+    y = oracle.rescale_int8(oracle.gemm_int8(qa, qw), sa, sw)
+    deq_a = qa.astype(np.float64) * sa.astype(np.float64)[:, None]
+    deq_w = qw.astype(np.float64) * sw.astype(np.float64)[:, None]
+    assert y.shape == (T, N)
+    assert np.array_equal(y, deq_a @ deq_w.T)
+    # a row of zero codes gives zero outputs; a zero scale gives zero outputs
+    qa[1] = 0
+    sw[3] = 0.0
+    y = oracle.rescale_int8(oracle.gemm_int8(qa, qw), sa, sw)
+    assert np.all(y[1] == 0.0) and np.all(y[:, 3] == 0.0)
+
+
 def test_codebook_gemm_matches_float_matmul():
     rng = np.random.default_rng(4)
     cb_a = oracle.lloyd_max(4, 256)["centroids"]
