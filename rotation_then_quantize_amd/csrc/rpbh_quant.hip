@@ -472,7 +472,15 @@ __device__ __forceinline__ void quantize_block(double (&acc)[kH], const unsigned
         }
         double ss = row_sum((ss4[0] + ss4[1]) + (ss4[2] + ss4[3]), log2nb, red);
         const float s = static_cast<float>(sqrt(ss));
-        const float den = (eps == 0.0f) ? s : s + eps;
+        float den = (eps == 0.0f) ? s : s + eps;
+        // A row with a tiny norm (a weight row, eps = 0) is scaled by 2^64, x' and den alike: exact
+        // (|x'| <= den), and fl32(x'/den) is unchanged, while the thresholds t_k * den and the
+        // grid's cells per unit of x' (grid_k / den) stay in the normal fp32 range.
+        if (den != 0.0f && den < 0x1p-60f) {
+            den *= 0x1p64f;
+#pragma unroll
+            for (int b = 0; b < kH; ++b) xr[b] *= 0x1p64f;
+        }
         // codes as one LSB-first bit stream of kSlot-bit fields: packed codes (2, 3, 4 bits), or one
         // byte per code (kRowLut*: its int8 value; the grid table holds the values, the other paths
         // look codes up afterwards, or as they are found for 6-bit codes)
