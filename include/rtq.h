@@ -197,6 +197,23 @@ rtq_status rtq_rotated_qlinear(const void* x, rtq_dtype xt, int64_t T, const rtq
  * bits_a is ignored for RTQ_INT8.  Returns 0 for invalid arguments. */
 size_t rtq_rotated_qlinear_workspace(int64_t T, int32_t d, rtq_qmode mode, int32_t bits_a);
 
+/* The online layer with no workspace and no allocation, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * rtq_rotated_qlinear with the activation codes and fp32 token scales held in a static device
+ * array of RTQ_NOALLOC_SCRATCH_BYTES bytes inside the library (one per GPU, kept until the
+ * process ends) instead of a caller's workspace.  Arguments and results as rtq_rotated_qlinear;
+ * the product runs without the K-split of a partial last round (it has no split region).
+ * Limit: rtq_rotated_qlinear_workspace's codes and scales, i.e. align256(T*d) + align256(4*T)
+ * bytes (T*d*bits_a/8 codes for RTQ_CODEBOOK), at most RTQ_NOALLOC_SCRATCH_BYTES; larger inputs
+ * return RTQ_ERR_INVALID_ARG before anything is enqueued.  Calls and graph replays on one GPU
+ * share the array: calls that overlap on a GPU (other streams, other threads) race, so order
+ * them on one stream.  The first call on a device looks up its copy with hipGetSymbolAddress. */
+#define RTQ_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+rtq_status rtq_rotated_qlinear_noalloc(const void* x, rtq_dtype xt, int64_t T, const rtq_rpbh* R,
+                                       const void* w_codes, const void* w_scale, rtq_dtype w_scale_t, int64_t N,
+                                       rtq_qmode mode, const rtq_codebook* cb_a, const rtq_codebook* cb_w,
+                                       void* y, rtq_dtype yt, void* stream);
+
 /* ---- Asymmetric INT8: a scale and a zero point per row (the scale-and-zero-point INT8 the pages
  * name: "INT8旋转量化是什么" section 3 lists per-channel scales and zero points; the int8
  * image-model page computes a scale and a zero-point offset).  With the range widened to contain 0,

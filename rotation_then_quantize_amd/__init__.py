@@ -25,7 +25,9 @@ RTQ_INT8, RTQ_CODEBOOK, RTQ_CODEBOOK_I8 = 0, 1, 2
 EXPORTS = ("rtq_rpbh_make", "rtq_lloyd_max", "rtq_rpbh_rotate", "rtq_quantize_rows", "rtq_qgemm",
            "rtq_qgemm_ws", "rtq_qgemm_workspace", "rtq_rotated_qlinear", "rtq_rotated_qlinear_workspace",
            "rtq_quantize_rows_asym", "rtq_qgemm_asym", "rtq_rotated_qlinear_asym",
-           "rtq_rotated_qlinear_asym_workspace", "rtq_last_error")
+           "rtq_rotated_qlinear_asym_workspace", "rtq_rotated_qlinear_noalloc", "rtq_last_error")
+
+NOALLOC_SCRATCH_BYTES = 96 << 20   # RTQ_NOALLOC_SCRATCH_BYTES
 
 
 class RtqError(RuntimeError):
@@ -67,6 +69,7 @@ def load_library():
     lib.rtq_qgemm_workspace.argtypes = []
     lib.rtq_qgemm_workspace.restype = sz
     lib.rtq_rotated_qlinear.argtypes = [vp, i32, i64, R, vp, vp, i32, i64, i32, C, C, vp, i32, vp, sz, vp]
+    lib.rtq_rotated_qlinear_noalloc.argtypes = [vp, i32, i64, R, vp, vp, i32, i64, i32, C, C, vp, i32, vp]
     lib.rtq_rotated_qlinear_workspace.argtypes = [i64, i32, i32, i32]
     lib.rtq_rotated_qlinear_workspace.restype = sz
     lib.rtq_quantize_rows_asym.argtypes = [vp, i32, i64, i32, R, vp, vp, i32, vp, vp, vp]
@@ -78,7 +81,7 @@ def load_library():
     lib.rtq_last_error.restype = ctypes.c_char_p
     for name in ("rtq_rpbh_make", "rtq_lloyd_max", "rtq_rpbh_rotate", "rtq_quantize_rows", "rtq_qgemm",
                  "rtq_qgemm_ws", "rtq_rotated_qlinear", "rtq_quantize_rows_asym", "rtq_qgemm_asym",
-                 "rtq_rotated_qlinear_asym"):
+                 "rtq_rotated_qlinear_asym", "rtq_rotated_qlinear_noalloc"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -264,6 +267,17 @@ def rotated_qlinear(x, R: Rpbh, w_codes, w_scale, y, mode: int = RTQ_INT8, cb_a:
                                               _dtype_code(w_scale), w_codes.shape[0], mode, _cb(cb_a), _cb(cb_w),
                                               _ptr(y), _dtype_code(y), _ptr(workspace), workspace.numel(),
                                               _stream(stream)))
+    return y
+
+
+def rotated_qlinear_noalloc(x, R: Rpbh, w_codes, w_scale, y, mode: int = RTQ_INT8, cb_a: Codebook | None = None,
+                            cb_w: Codebook | None = None, stream=None):
+    """The online layer with no workspace: the activation codes and scales go to the library's
+    static device scratch (NOALLOC_SCRATCH_BYTES per GPU; calls on one GPU must not overlap)."""
+    T = x.shape[0]
+    _check(load_library().rtq_rotated_qlinear_noalloc(_ptr(x), _dtype_code(x), T, R.c, _ptr(w_codes), _ptr(w_scale),
+                                                      _dtype_code(w_scale), w_codes.shape[0], mode, _cb(cb_a),
+                                                      _cb(cb_w), _ptr(y), _dtype_code(y), _stream(stream)))
     return y
 
 

@@ -7,6 +7,8 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <map>
+#include <mutex>
 #include <string>
 
 #include "../../include/rtq.h"
@@ -250,6 +252,90 @@ size_t asym_workspace_bytes(int64_t T, int32_t d, bool with_split) {
            (with_split ? align256(rtq::gemm_i8_workspace_bytes()) : 0);
 }
 
+// Bytes of activation codes and scales the online layer needs (the workspace's required part).
+rtq_status qlinear_need(const rtq_rpbh* R, int64_t T, rtq_qmode mode, const rtq_codebook* cb_a, size_t* need) {
+    if (R == nullptr) return fail(RTQ_ERR_INVALID_ARG, "rpbh descriptor is NULL");
+    RTQ_TRY(check_d(R->d));
+    const bool cbook = mode == RTQ_CODEBOOK || mode == RTQ_CODEBOOK_I8;
+    if (cbook && cb_a == nullptr) return fail(RTQ_ERR_INVALID_ARG, "cb_a is NULL");
+    const int32_t bits_a = cbook ? cb_a->bits : 8;
+    if (mode == RTQ_CODEBOOK && bits_a != 4)
+        return fail(RTQ_ERR_UNSUPPORTED, "activation codes must be 4-bit (got %d)", bits_a);
+    *need = workspace_bytes(T < 0 ? 0 : T, R->d, mode, bits_a, false);
+    if (*need == 0 && T > 0) return fail(RTQ_ERR_INVALID_ARG, "unsupported mode or activation bits");
+    return RTQ_OK;
+}
+
+// The online layer on a caller's workspace: rotate-quantise into its head, then the product.
+rtq_status rotated_qlinear_ws(const void* x, rtq_dtype xt, int64_t T, const rtq_rpbh* R, const void* w_codes,
+                              const void* w_scale, rtq_dtype w_scale_t, int64_t N, rtq_qmode mode,
+                              const rtq_codebook* cb_a, const rtq_codebook* cb_w, void* y, rtq_dtype yt,
+                              void* workspace, size_t ws_bytes, void* stream) {
+    size_t need = 0;
+    RTQ_TRY(qlinear_need(R, T, mode, cb_a, &need));
+    const int32_t d = R->d;
+    if (yt == RTQ_I32) return fail(RTQ_ERR_UNSUPPORTED, "rtq_rotated_qlinear produces F32 or BF16 output");
+    const bool cbook = mode == RTQ_CODEBOOK || mode == RTQ_CODEBOOK_I8;
+    const int32_t bits_a = cbook ? cb_a->bits : 8;
+    // (need covers the codes and scales; a larger workspace also carries the product's K-split)
+    if (workspace == nullptr) return fail(RTQ_ERR_INVALID_ARG, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return fail(RTQ_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+    if (ws_bytes < need) return fail(RTQ_ERR_INVALID_ARG, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    const size_t code_bytes = mode == RTQ_CODEBOOK ? static_cast<size_t>(T < 0 ? 0 : T) * d * bits_a / 8
+                                                   : static_cast<size_t>(T < 0 ? 0 : T) * d;
+    void* a_codes = ws;
+    float* a_scale = reinterpret_cast<float*>(ws + align256(code_bytes));
+    rtq::RowArgs qa{};
+    RTQ_TRY(plan_quantize(x, xt, T, d, R, mode, cbook ? cb_a : nullptr, cbook ? 1e-8f : 0.0f, a_codes, a_scale,
+                          RTQ_F32, &qa));
+    GemmPlan gp{};
+    RTQ_TRY(plan_gemm(a_codes, a_scale, T, w_codes, w_scale, w_scale_t, N, d, mode, cb_a, cb_w, y, yt, &gp));
+    if (T == 0) return ok();
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t split_off = align256(code_bytes) + align256(static_cast<size_t>(T) * sizeof(float));
+    if (!gp.lut) {
+        // the quantiser launch zeroes the product's split counters (when the workspace has them)
+        gp.i8.workspace = ws + split_off;
+        gp.i8.ws_bytes = ws_bytes - split_off;
+        qa.clear = rtq::gemm_i8_split_counters(gp.i8.workspace, gp.i8.ws_bytes, &qa.nclear);
+        gp.i8.counters_zeroed = true;
+    }
+    RTQ_TRY(hip_status(rtq::launch_rpbh_rows(qa, s), "rpbh_rows launch"));
+    if (gp.lut) return hip_status(rtq::launch_gemm_lut(gp.cb, s), "gemm_lut launch");
+    return hip_status(rtq::launch_gemm_i8(gp.i8, s), "gemm_i8 launch");
+}
+
+// Device scratch of rtq_rotated_qlinear_noalloc: the activation codes, then the fp32 token scales
+// (the head of rtq_rotated_qlinear's workspace, without the product's K-split region).  Each GPU
+// the library runs on holds its own copy until the process ends; host code reaches it only
+// through the address hipGetSymbolAddress returns on that device (the array's name is a host-side
+// stand-in, not a device address).
+constexpr size_t kScratchBytes = RTQ_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_addr;   // device -> address of its copy of `scratch`
+
+// The current device's copy of `scratch`, looked up once per device (with that device current).
+rtq_status scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    auto it = g_scratch_addr.find(dev);
+    if (it == g_scratch_addr.end()) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+        if (p == nullptr || reinterpret_cast<uintptr_t>(p) % 256 != 0)
+            return fail(RTQ_ERR_HIP, "hipGetSymbolAddress(scratch) returned an unaligned address");
+        it = g_scratch_addr.emplace(dev, p).first;
+    }
+    *out = it->second;
+    return RTQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -345,44 +431,24 @@ rtq_status rtq_rotated_qlinear(const void* x, rtq_dtype xt, int64_t T, const rtq
                                const void* w_scale, rtq_dtype w_scale_t, int64_t N, rtq_qmode mode,
                                const rtq_codebook* cb_a, const rtq_codebook* cb_w, void* y, rtq_dtype yt,
                                void* workspace, size_t ws_bytes, void* stream) {
-    if (R == nullptr) return fail(RTQ_ERR_INVALID_ARG, "rpbh descriptor is NULL");
-    const int32_t d = R->d;
-    RTQ_TRY(check_d(d));
-    if (yt == RTQ_I32) return fail(RTQ_ERR_UNSUPPORTED, "rtq_rotated_qlinear produces F32 or BF16 output");
-    const bool cbook = mode == RTQ_CODEBOOK || mode == RTQ_CODEBOOK_I8;
-    if (cbook && cb_a == nullptr) return fail(RTQ_ERR_INVALID_ARG, "cb_a is NULL");
-    const int32_t bits_a = cbook ? cb_a->bits : 8;
-    const size_t need = workspace_bytes(T < 0 ? 0 : T, d, mode, bits_a, false);
-    if (mode == RTQ_CODEBOOK && bits_a != 4)
-        return fail(RTQ_ERR_UNSUPPORTED, "activation codes must be 4-bit (got %d)", bits_a);
-    if (need == 0 && T > 0) return fail(RTQ_ERR_INVALID_ARG, "unsupported mode or activation bits");
-    // (need covers the codes and scales; a larger workspace also carries the product's K-split)
-    if (workspace == nullptr) return fail(RTQ_ERR_INVALID_ARG, "workspace is NULL");
-    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return fail(RTQ_ERR_MISALIGNED, "workspace is not 16-byte aligned");
-    if (ws_bytes < need) return fail(RTQ_ERR_INVALID_ARG, "workspace too small: %zu < %zu bytes", ws_bytes, need);
-    unsigned char* ws = static_cast<unsigned char*>(workspace);
-    const size_t code_bytes = mode == RTQ_CODEBOOK ? static_cast<size_t>(T < 0 ? 0 : T) * d * bits_a / 8
-                                                   : static_cast<size_t>(T < 0 ? 0 : T) * d;
-    void* a_codes = ws;
-    float* a_scale = reinterpret_cast<float*>(ws + align256(code_bytes));
-    rtq::RowArgs qa{};
-    RTQ_TRY(plan_quantize(x, xt, T, d, R, mode, cbook ? cb_a : nullptr, cbook ? 1e-8f : 0.0f, a_codes, a_scale,
-                          RTQ_F32, &qa));
-    GemmPlan gp{};
-    RTQ_TRY(plan_gemm(a_codes, a_scale, T, w_codes, w_scale, w_scale_t, N, d, mode, cb_a, cb_w, y, yt, &gp));
-    if (T == 0) return ok();
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const size_t split_off = align256(code_bytes) + align256(static_cast<size_t>(T) * sizeof(float));
-    if (!gp.lut) {
-        // the quantiser launch zeroes the product's split counters (when the workspace has them)
-        gp.i8.workspace = ws + split_off;
-        gp.i8.ws_bytes = ws_bytes - split_off;
-        qa.clear = rtq::gemm_i8_split_counters(gp.i8.workspace, gp.i8.ws_bytes, &qa.nclear);
-        gp.i8.counters_zeroed = true;
-    }
-    RTQ_TRY(hip_status(rtq::launch_rpbh_rows(qa, s), "rpbh_rows launch"));
-    if (gp.lut) return hip_status(rtq::launch_gemm_lut(gp.cb, s), "gemm_lut launch");
-    return hip_status(rtq::launch_gemm_i8(gp.i8, s), "gemm_i8 launch");
+    return rotated_qlinear_ws(x, xt, T, R, w_codes, w_scale, w_scale_t, N, mode, cb_a, cb_w, y, yt, workspace,
+                              ws_bytes, stream);
+}
+
+rtq_status rtq_rotated_qlinear_noalloc(const void* x, rtq_dtype xt, int64_t T, const rtq_rpbh* R, const void* w_codes,
+                                       const void* w_scale, rtq_dtype w_scale_t, int64_t N, rtq_qmode mode,
+                                       const rtq_codebook* cb_a, const rtq_codebook* cb_w, void* y, rtq_dtype yt,
+                                       void* stream) {
+    size_t need = 0;
+    RTQ_TRY(qlinear_need(R, T, mode, cb_a, &need));
+    if (need > kScratchBytes)
+        return fail(RTQ_ERR_INVALID_ARG,
+                    "rtq_rotated_qlinear_noalloc: the activation codes and scales need %zu bytes, more than its "
+                    "static scratch of %zu bytes (use rtq_rotated_qlinear with a workspace)", need, kScratchBytes);
+    void* ws = nullptr;
+    RTQ_TRY(scratch_address(&ws));
+    return rotated_qlinear_ws(x, xt, T, R, w_codes, w_scale, w_scale_t, N, mode, cb_a, cb_w, y, yt, ws, need,
+                              stream);
 }
 
 // ---- asymmetric INT8 (scale + zero point per row)

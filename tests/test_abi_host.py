@@ -193,6 +193,28 @@ def test_qgemm_and_qlinear_validation():
     assert ql(*a) == rtq.RTQ_ERR_UNSUPPORTED
 
 
+def test_noalloc_layer_rejects_inputs_beyond_its_scratch():
+    # the allocation-free layer checks its size limit on the host, before any HIP call
+    lib = rtq.load_library()
+    cb4 = _C(4, A, A)
+    R = _R(4096, 64, A, A)
+    f = lib.rtq_rotated_qlinear_noalloc
+    args = [A, rtq.RTQ_BF16, 0, ctypes.byref(R), A, A, rtq.RTQ_BF16, 32, rtq.RTQ_INT8, None, None, A, rtq.RTQ_BF16,
+            None]
+    limit = rtq.NOALLOC_SCRATCH_BYTES
+    # INT8 codes: T * 4096 bytes plus 4 T bytes of scales (each 256-aligned)
+    t_max = max(t for t in range(limit // 4096 - 64, limit // 4096 + 1)
+                if ((t * 4096 + 255) // 256 + (4 * t + 255) // 256) * 256 <= limit)
+    a = list(args); a[2] = t_max + 1
+    assert f(*a) == rtq.RTQ_ERR_INVALID_ARG and "static scratch" in rtq.last_error()
+    # packed 4-bit codes take half the bytes per token (no call that passes the checks is made
+    # here: its fake pointers would reach a kernel)
+    a = list(args); a[2] = 2 * t_max + 64; a[8] = rtq.RTQ_CODEBOOK; a[9] = ctypes.byref(cb4); a[10] = ctypes.byref(cb4)
+    assert f(*a) == rtq.RTQ_ERR_INVALID_ARG and "static scratch" in rtq.last_error()
+    a = list(args); a[3] = None
+    assert f(*a) == rtq.RTQ_ERR_INVALID_ARG
+
+
 def test_rotate_validation():
     lib = rtq.load_library()
     R = _R(256, 64, A, A)
