@@ -4,7 +4,8 @@
 Headline workload: the online W8A8 rotated linear at DiT image shape -- 4608 tokens (4096 latent
 patches + 512 text tokens) x d_in 4096 -> d_out 16384 (the MLP-up linear of a 7B, 32-layer
 single-stream DiT), bf16 activations in, bf16 out, INT8 weights rotated and quantised offline with
-the same RPBH descriptor.  One step = one call of rtq_rotated_qlinear, one pass of the online path
+the same RPBH descriptor, both operands' codes in the product's tiled layout (RTQ_INT8_TILED; the
+row-major format is timed beside it).  One step = one call of rtq_rotated_qlinear, one pass of the online path
 over one batch:
     rotate-quantise (gather + sign + FWHT-64 + per-token INT8)   [HBM-bound]
     product         (INT8 MFMA product + scale epilogue)          [MFMA-bound]
@@ -124,37 +125,41 @@ def _burst_ms(n, launch, torch):
     return e0.elapsed_time(e1) / n
 
 
-def bench_w8a8(args, torch, rtq, workloads):
+def bench_w8a8(args, torch, rtq, workloads, mode=None):
+    """The headline step.  mode RTQ_INT8_TILED (default): weight and activation codes in the
+    product's tiled layout; RTQ_INT8: row-major codes (reported beside it)."""
+    mode = rtq.RTQ_INT8_TILED if mode is None else mode
     d, N = workloads.DIT_HIDDEN, workloads.DIT_MLP
     xh = workloads.dit_activations_bf16(d)
     T = xh.shape[0]
     wh = workloads.dit_weight_bf16("mlp_up")
     R = rtq.Rpbh.from_seed(workloads.RPBH_SEED[d], d)
+    tiled = mode == rtq.RTQ_INT8_TILED
     w = _bf16_dev(wh, torch)
-    wq = torch.empty((N, d), dtype=torch.int8, device="cuda")
+    wq = torch.empty(((rtq.tiled_rows(N) if tiled else N), d), dtype=torch.int8, device="cuda")
     ws = torch.empty(N, dtype=torch.bfloat16, device="cuda")
-    rtq.quantize_rows(w, wq, ws, R, rtq.RTQ_INT8)           # offline, not timed here
+    rtq.quantize_rows(w, wq, ws, R, mode)                   # offline, not timed here
     del w
     xs = _copies(_bf16_dev(xh, torch), 512 << 20, torch)
-    codes = torch.empty((T, d), dtype=torch.int8, device="cuda")
+    codes = torch.empty(((rtq.tiled_rows(T) if tiled else T), d), dtype=torch.int8, device="cuda")
     scale = torch.empty(T, dtype=torch.float32, device="cuda")
     y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
 
     def quant(i):
-        rtq.quantize_rows(xs[i % len(xs)], codes, scale, R, rtq.RTQ_INT8)
+        rtq.quantize_rows(xs[i % len(xs)], codes, scale, R, mode)
 
     split_ws = torch.empty(rtq.qgemm_workspace(), dtype=torch.uint8, device="cuda")
 
     def gemm(i):
-        rtq.qgemm(codes, scale, wq, ws, y, d, workspace=split_ws)
+        rtq.qgemm(codes, scale, wq, ws, y, d, mode, workspace=split_ws, n_tokens=T, n_out=N)
 
     # The timed steps: the layer's entry point (rotate-quantise, then the product, on one stream),
     # K launches bracketed by synchronisation only.
-    ws_bytes = rtq.rotated_qlinear_workspace(T, d)
+    ws_bytes = rtq.rotated_qlinear_workspace(T, d, mode)
     work = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
 
     def step(i):
-        rtq.rotated_qlinear(xs[i % len(xs)], R, wq, ws, y, workspace=work)
+        rtq.rotated_qlinear(xs[i % len(xs)], R, wq, ws, y, mode, workspace=work)
 
     prewarm = _prewarm(step, torch)
     for i in range(args.warmup):
@@ -538,6 +543,8 @@ def main():
     r = bench_w8a8(args, torch, rtq, workloads)
     extra = {}
     if args.only == "all":
+        rm = bench_w8a8(args, torch, rtq, workloads, rtq.RTQ_INT8)
+        extra["w8a8_row_major_codes"] = {k: rm[k] for k in ("step_ms", "quant_ms", "gemm_ms", "quant_burst_ms")}
         extra["offline_weight_rotate_quantize"] = bench_offline(args, torch, rtq, workloads)
         extra["w4a4_dit_attn_out_4608x4096x4096"] = bench_codebook(args, torch, rtq, workloads, "w4a4")
         extra["w2a4_dit_mlp_down_4608x16384x4096"] = bench_codebook(args, torch, rtq, workloads, "w2a4")
@@ -572,6 +579,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "w8a8_dit_mlp_up_4608x4096x16384_bf16", "tokens": r["T"], "d_in": r["d"],
                    "d_out": r["N"], "io": "bf16", "weights": "int8 per-row, bf16 scales",
+                   "codes_layout": "tiled (RTQ_INT8_TILED: 256-row x 64-byte blocks)",
                    "activations": "int8 per-token, fp32 scales", "rotation": "RPBH h=64"},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
                      "frac": round(gemm_tops / PEAK_INT8_TOPS, 4), "traffic": _traffic("gemm_i8_kernel"),

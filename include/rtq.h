@@ -55,7 +55,7 @@ typedef enum {
 typedef enum {
     RTQ_INT8 = 0,     /* symmetric INT8, scale = max|v|/127, codes in [-127, 127]       */
     RTQ_CODEBOOK = 1, /* L2 norm + Lloyd-Max direction codes of `bits` bits, packed     */
-    RTQ_CODEBOOK_I8 = 2 /* the same Lloyd-Max codes, multiplied on the INT8 matrix cores:
+    RTQ_CODEBOOK_I8 = 2, /* the same Lloyd-Max codes, multiplied on the INT8 matrix cores:
                          * each codebook enters the product as v_k = rint(c_k * S),
                          * S = 127 / max_k |c_k| (largest centroid -> +-127), and y is
                          * rescaled by 1/(S_a S_w).  Activations are then stored as their
@@ -63,6 +63,16 @@ typedef enum {
                          * stay packed codes.  Relative Frobenius error of y against the
                          * exact-centroid product: ~0.9% (W4A4) / ~0.5% (W2A4) on the DiT
                          * synthetic shapes, inside the 2e-2 bound for bf16 outputs.    */
+    RTQ_INT8_TILED = 3 /* RTQ_INT8 codes and scales, with the codes stored in the product's tiled
+                         * layout: rows in tiles of 256 (padded to a multiple of 256; padding rows
+                         * are neither written nor read as results), K in slices of 64 bytes;
+                         * block (tile, slice) is 16 KB contiguous at
+                         * ((row / 256) * (d / 64) + j / 64) * 16384, holding [256 rows][64 bytes],
+                         * and within a row's 64 bytes the 16-byte chunk c (bytes j = 16c .. of
+                         * the slice) sits at chunk c ^ ((row >> 2) & 3).  It is the image of one
+                         * LDS stage of the INT8 product, whose operand loads then read whole 1 KB
+                         * runs (about 7% faster products at the DiT shapes than row-major codes).
+                         * A codes buffer holds ceil(rows / 256) * 256 * d bytes.            */
 } rtq_qmode;
 
 /* RPBH descriptor (OrbitQuant article, section 2.3).  perm (int32[d]) and signs (int8[d], +-1)
@@ -115,6 +125,7 @@ rtq_status rtq_rpbh_rotate(const void* x, rtq_dtype xt, void* y, rtq_dtype yt, i
  *   INT8:      s = max_j |x'_j| / 127 in fp32, stored as scale_t (F32 or BF16); the STORED value
  *              divides: q_j = round-half-even(x'_j / s), clamped to [-127, 127]; s == 0 gives q = 0.
  *              codes: int8[rows][d].  cb must be NULL.  eps is ignored.
+ *   INT8_TILED: the same codes and scales, codes written in the tiled layout (RTQ_INT8_TILED).
  *   CODEBOOK:  s = ||x'||_2 (summed in double, rounded to fp32); u_j = x'_j / (s + eps) in fp32
  *              (0 when s + eps == 0); code_j = #{k : boundaries[k] < u_j}.  The norm s is stored as
  *              scale_t: BF16 for weights (eps = 0), F32 for activations (eps > 0, e.g. 1e-8).
@@ -137,7 +148,8 @@ rtq_status rtq_quantize_rows(const void* x, rtq_dtype xt, int64_t rows, int32_t 
  * W'x' = W Pi^T Pi x).
  *   a_codes [T][d] (INT8) or [T][d*bits_a/8] packed (CODEBOOK), a_scale fp32[T] (INT8 scale or
  *   token norm); w_codes [N][d] or [N][d*bits_w/8], w_scale [N] of w_scale_t (F32 or BF16).
- *   INT8:      acc[t][n] = sum_j a[t][j] w[n][j] exactly in int32 (|acc| <= 127^2 d);
+ *   INT8, INT8_TILED (both operands' codes in the tiled layout):
+ *              acc[t][n] = sum_j a[t][j] w[n][j] exactly in int32 (|acc| <= 127^2 d);
  *              y = acc * a_scale[t] * w_scale[n] (fp32 arithmetic), stored as yt (F32 or BF16);
  *              yt == RTQ_I32 stores acc itself.  cb_a and cb_w must be NULL.  N <= 2^22 for BF16
  *              output, N <= 2^21 for F32 and I32 (else RTQ_ERR_UNSUPPORTED).
@@ -180,7 +192,8 @@ size_t rtq_qgemm_workspace(void);
 
 /* The online layer: rtq_quantize_rows(x, R, mode, cb_a, eps = 1e-8 (CODEBOOK) ...) into `workspace`
  * followed by rtq_qgemm on the same stream (OrbitQuant article, section 2.2, steps 1-5 and the
- * cancellation).  Weights come from rtq_quantize_rows with the SAME descriptor R.
+ * cancellation).  Weights come from rtq_quantize_rows with the SAME descriptor R (RTQ_INT8_TILED:
+ * weight codes written in that mode, and the activation codes go to the workspace tiled too).
  *   workspace: device memory of at least rtq_rotated_qlinear_workspace(T, R->d, mode, bits_a) bytes,
  *   16-byte aligned, any contents (the quantiser launch zeroes the product's split counters); on
  *   return it starts with the activation codes and scales.  Calls sharing a workspace must not
@@ -191,7 +204,8 @@ rtq_status rtq_rotated_qlinear(const void* x, rtq_dtype xt, int64_t T, const rtq
                                void* workspace, size_t ws_bytes, void* stream);
 
 /* Bytes of workspace rtq_rotated_qlinear uses: the codes and fp32 scales (each 256-byte aligned;
- * the codes take T*d bytes for RTQ_INT8 and RTQ_CODEBOOK_I8, T*d*bits_a/8 for RTQ_CODEBOOK), then,
+ * the codes take T*d bytes for RTQ_INT8 and RTQ_CODEBOOK_I8, ceil(T/256)*256*d for RTQ_INT8_TILED,
+ * T*d*bits_a/8 for RTQ_CODEBOOK), then,
  * for the INT8-core modes, rtq_qgemm_workspace() bytes for the product's K-split.  A workspace
  * that holds only the codes and scales is accepted (the product then runs without the split).
  * bits_a is ignored for RTQ_INT8.  Returns 0 for invalid arguments. */

@@ -20,7 +20,13 @@ LIB_PATH = os.path.join(_PKG, "librtq.so")
 
 RTQ_OK, RTQ_ERR_INVALID_ARG, RTQ_ERR_UNSUPPORTED, RTQ_ERR_MISALIGNED, RTQ_ERR_HIP = 0, -1, -2, -3, -4
 RTQ_F32, RTQ_BF16, RTQ_I32 = 0, 1, 2
-RTQ_INT8, RTQ_CODEBOOK, RTQ_CODEBOOK_I8 = 0, 1, 2
+RTQ_INT8, RTQ_CODEBOOK, RTQ_CODEBOOK_I8, RTQ_INT8_TILED = 0, 1, 2, 3
+TILE_ROWS, TILE_K = 256, 64   # the tiled INT8 layout: 256-row tiles, 64-byte K slices
+
+
+def tiled_rows(rows: int) -> int:
+    """Rows a codes buffer in the tiled INT8 layout holds (rows padded to a multiple of 256)."""
+    return -(-rows // TILE_ROWS) * TILE_ROWS
 
 EXPORTS = ("rtq_rpbh_make", "rtq_lloyd_max", "rtq_rpbh_rotate", "rtq_quantize_rows", "rtq_qgemm",
            "rtq_qgemm_ws", "rtq_qgemm_workspace", "rtq_rotated_qlinear", "rtq_rotated_qlinear_workspace",
@@ -221,6 +227,8 @@ def quantize_rows(x, codes, scale, R: Rpbh | None = None, mode: int = RTQ_INT8, 
                   eps: float = 0.0, stream=None):
     """Rotate (if R) and quantise each row of x into codes + per-row scale/norm."""
     rows, d = x.shape
+    if mode == RTQ_INT8_TILED and codes.numel() * codes.element_size() < tiled_rows(rows) * d:
+        raise ValueError(f"tiled codes need {tiled_rows(rows) * d} bytes (rows padded to a multiple of 256)")
     _check(load_library().rtq_quantize_rows(_ptr(x), _dtype_code(x), rows, d, None if R is None else R.c, mode,
                                             _cb(cb), ctypes.c_float(eps), _ptr(codes), _ptr(scale),
                                             _dtype_code(scale), _stream(stream)))
@@ -228,12 +236,15 @@ def quantize_rows(x, codes, scale, R: Rpbh | None = None, mode: int = RTQ_INT8, 
 
 
 def qgemm(a_codes, a_scale, w_codes, w_scale, y, d: int, mode: int = RTQ_INT8, cb_a: Codebook | None = None,
-          cb_w: Codebook | None = None, stream=None, workspace=None):
+          cb_w: Codebook | None = None, stream=None, workspace=None, n_tokens: int | None = None,
+          n_out: int | None = None):
     """y = dequantised product of activation and weight codes (rotation already cancelled).
     With a workspace (qgemm_workspace() bytes) this is rtq_qgemm_ws: a partial last round of tiles
-    is shared along d (stream-K runs after a full round, equal K ranges otherwise)."""
-    T = a_codes.shape[0]
-    N = w_codes.shape[0]
+    is shared along d (stream-K runs after a full round, equal K ranges otherwise).
+    T and N default to the codes' first dimensions; pass n_tokens / n_out for tiled codes (whose
+    buffers hold rows padded to a multiple of 256), or take them from y."""
+    T = a_codes.shape[0] if n_tokens is None else n_tokens
+    N = w_codes.shape[0] if n_out is None else n_out
     lib = load_library()
     if workspace is None:
         _check(lib.rtq_qgemm(_ptr(a_codes), _ptr(a_scale), T, _ptr(w_codes), _ptr(w_scale), _dtype_code(w_scale), N,
@@ -260,11 +271,12 @@ def rotated_qlinear(x, R: Rpbh, w_codes, w_scale, y, mode: int = RTQ_INT8, cb_a:
     torch = _torch()
     T = x.shape[0]
     bits_a = cb_a.bits if (mode in (RTQ_CODEBOOK, RTQ_CODEBOOK_I8) and cb_a is not None) else 8
+    N = y.shape[1]
     need = rotated_qlinear_workspace(T, R.d, mode, bits_a)
     if workspace is None:
         workspace = _stream_local_workspace(torch, max(need, 16), x.device, stream)
     _check(load_library().rtq_rotated_qlinear(_ptr(x), _dtype_code(x), T, R.c, _ptr(w_codes), _ptr(w_scale),
-                                              _dtype_code(w_scale), w_codes.shape[0], mode, _cb(cb_a), _cb(cb_w),
+                                              _dtype_code(w_scale), N, mode, _cb(cb_a), _cb(cb_w),
                                               _ptr(y), _dtype_code(y), _ptr(workspace), workspace.numel(),
                                               _stream(stream)))
     return y
@@ -276,7 +288,7 @@ def rotated_qlinear_noalloc(x, R: Rpbh, w_codes, w_scale, y, mode: int = RTQ_INT
     static device scratch (NOALLOC_SCRATCH_BYTES per GPU; calls on one GPU must not overlap)."""
     T = x.shape[0]
     _check(load_library().rtq_rotated_qlinear_noalloc(_ptr(x), _dtype_code(x), T, R.c, _ptr(w_codes), _ptr(w_scale),
-                                                      _dtype_code(w_scale), w_codes.shape[0], mode, _cb(cb_a),
+                                                      _dtype_code(w_scale), y.shape[1], mode, _cb(cb_a),
                                                       _cb(cb_w), _ptr(y), _dtype_code(y), _stream(stream)))
     return y
 

@@ -229,7 +229,7 @@ struct AsymArgs {
     const int32_t* w_sum;    // [N]  sum_j qw[n][j]
 };
 
-template <int kWavesN, int kYKind, bool kWScaleBF16, bool kVec, int kWBits, bool kAsym>
+template <int kWavesN, int kYKind, bool kWScaleBF16, bool kVec, int kWBits, bool kAsym, bool kTiled>
 __global__ void __launch_bounds__(64 * kWavesM * kWavesN, 1)
 gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, const int8_t* __restrict__ W,
                const void* __restrict__ w_scale, int64_t T, int64_t N, int d, void* __restrict__ Y,
@@ -304,14 +304,18 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
     };
 
     // Load geometry: instruction q of wave w fills rows 16 * (q * kWaves + w) .. +16 of an operand
-    // block; lane L takes row 16 * (q * kWaves + w) + L / 4 and LDS slot L % 4, which holds the
-    // row's chunk (L % 4) ^ ((row >> 2) & 3) = (L % 4) ^ ((L >> 4) & 3).
+    // block, 1 KB of LDS; lane L writes its 16 bytes at LDS offset 16 L of that KB, which holds row
+    // 16 * (q * kWaves + w) + L / 4, chunk (L % 4) ^ ((row >> 2) & 3) = (L % 4) ^ ((L >> 4) & 3).
+    // Row-major operands: each lane fetches that chunk of that row (16 rows x 64 bytes per
+    // instruction).  kTiled: the operands are stored as the stage blocks themselves (the tiled
+    // layout), so a lane fetches bytes 16 L of the KB and each instruction reads 1 KB contiguous.
     uint32_t load_off[kLoadsPerOp];
 #pragma unroll
     for (int q = 0; q < kLoadsPerOp; ++q) {
         const int row = 16 * (q * kWaves + wave) + (lane >> 2);
         const int chunk = (lane & 3) ^ ((lane >> 4) & 3);
-        load_off[q] = static_cast<uint32_t>(row * d + chunk * 16);
+        load_off[q] = kTiled ? static_cast<uint32_t>((q * kWaves + wave) * 1024 + 16 * lane)
+                             : static_cast<uint32_t>(row * d + chunk * 16);
     }
     const uint32_t wave_lds = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave * 1024));
 
@@ -349,13 +353,14 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
         n0 = static_cast<int64_t>(tn) * BN;
         const int rows_a = static_cast<int>(min<int64_t>(BM, T - m0));
         const int rows_w = static_cast<int>(min<int64_t>(BN, N - n0));
-        rsa = make_rsrc(A + m0 * d, static_cast<uint32_t>(rows_a * d));
+        // (tiled operands: the tile's whole panel, padding rows included, is in the buffer)
+        rsa = make_rsrc(A + m0 * d, static_cast<uint32_t>((kTiled ? BM : rows_a) * d));
         const int wrow = d * kWBits / 8;                      // bytes per weight row
-        rsw = make_rsrc(W + n0 * wrow, static_cast<uint32_t>(rows_w * wrow));
+        rsw = make_rsrc(W + n0 * wrow, static_cast<uint32_t>((kTiled ? BN : rows_w) * wrow));
     };
     auto issue_stage = [&](int st) {
         const uint32_t sb = lds_base + static_cast<uint32_t>((st & (kStages - 1)) * kStageBytes) + wave_lds;
-        const uint32_t k0 = static_cast<uint32_t>((kbeg + st) * BK);
+        const uint32_t k0 = static_cast<uint32_t>((kbeg + st) * (kTiled ? BM * BK : BK));   // BM == BN
 #pragma unroll
         for (int q = 0; q < kLoadsPerOp; ++q) {
             load_to_lds(rsa, load_off[q] + k0, sb + q * kWaves * 1024);
@@ -823,8 +828,9 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
     }
 }
 
-template <int kWavesN, int kWBits, bool kAsym>
+template <int kWavesN, int kWBits, bool kAsym, bool kTiled = false>
 hipError_t launch_config(const GemmI8Args& g, hipStream_t stream) {
+    static_assert(!kTiled || (kWBits == 8 && !kAsym), "the tiled layout holds int8 codes");
     using KernelFn = void (*)(const int8_t*, const float*, const int8_t*, const void*, int64_t, int64_t, int,
                               void*, int, int, const float*, int, const float*, SplitArgs, AsymArgs);
     constexpr int kYKinds = 3;   // fp32, bf16, raw int32 accumulators
@@ -832,14 +838,14 @@ hipError_t launch_config(const GemmI8Args& g, hipStream_t stream) {
     static_assert(kLdsBytes <= 160 * 1024, "LDS");
     // [w_scale bf16][N % 8 == 0][y kind]
     static const KernelFn kernels[2][2][3] = {
-        {{gemm_i8_kernel<kWavesN, 0, false, false, kWBits, kAsym>, gemm_i8_kernel<kWavesN, 1, false, false, kWBits, kAsym>,
-          kYKinds > 2 ? gemm_i8_kernel<kWavesN, kYKinds - 1, false, false, kWBits, kAsym> : nullptr},
-         {gemm_i8_kernel<kWavesN, 0, false, true, kWBits, kAsym>, gemm_i8_kernel<kWavesN, 1, false, true, kWBits, kAsym>,
-          kYKinds > 2 ? gemm_i8_kernel<kWavesN, kYKinds - 1, false, true, kWBits, kAsym> : nullptr}},
-        {{gemm_i8_kernel<kWavesN, 0, true, false, kWBits, kAsym>, gemm_i8_kernel<kWavesN, 1, true, false, kWBits, kAsym>,
-          kYKinds > 2 ? gemm_i8_kernel<kWavesN, kYKinds - 1, true, false, kWBits, kAsym> : nullptr},
-         {gemm_i8_kernel<kWavesN, 0, true, true, kWBits, kAsym>, gemm_i8_kernel<kWavesN, 1, true, true, kWBits, kAsym>,
-          kYKinds > 2 ? gemm_i8_kernel<kWavesN, kYKinds - 1, true, true, kWBits, kAsym> : nullptr}}};
+        {{gemm_i8_kernel<kWavesN, 0, false, false, kWBits, kAsym, kTiled>, gemm_i8_kernel<kWavesN, 1, false, false, kWBits, kAsym, kTiled>,
+          kYKinds > 2 ? gemm_i8_kernel<kWavesN, kYKinds - 1, false, false, kWBits, kAsym, kTiled> : nullptr},
+         {gemm_i8_kernel<kWavesN, 0, false, true, kWBits, kAsym, kTiled>, gemm_i8_kernel<kWavesN, 1, false, true, kWBits, kAsym, kTiled>,
+          kYKinds > 2 ? gemm_i8_kernel<kWavesN, kYKinds - 1, false, true, kWBits, kAsym, kTiled> : nullptr}},
+        {{gemm_i8_kernel<kWavesN, 0, true, false, kWBits, kAsym, kTiled>, gemm_i8_kernel<kWavesN, 1, true, false, kWBits, kAsym, kTiled>,
+          kYKinds > 2 ? gemm_i8_kernel<kWavesN, kYKinds - 1, true, false, kWBits, kAsym, kTiled> : nullptr},
+         {gemm_i8_kernel<kWavesN, 0, true, true, kWBits, kAsym, kTiled>, gemm_i8_kernel<kWavesN, 1, true, true, kWBits, kAsym, kTiled>,
+          kYKinds > 2 ? gemm_i8_kernel<kWavesN, kYKinds - 1, true, true, kWBits, kAsym, kTiled> : nullptr}}};
     static const hipError_t attr_err = [] {
         hipError_t e = hipSuccess;
         for (auto& a : kernels)
@@ -947,7 +953,8 @@ hipError_t launch_gemm_i8(const GemmI8Args& g, hipStream_t stream) {
     const bool asym = g.a_zero != nullptr;
     if (asym != (g.a_sum != nullptr) || asym != (g.w_zero != nullptr) || asym != (g.w_sum != nullptr))
         return hipErrorInvalidValue;
-    if (asym) return g.w_bits == 8 ? launch_config<kDefaultWavesN, 8, true>(g, stream) : hipErrorInvalidValue;
+    if (asym) return g.w_bits == 8 && !g.tiled ? launch_config<kDefaultWavesN, 8, true>(g, stream) : hipErrorInvalidValue;
+    if (g.tiled) return g.w_bits == 8 ? launch_config<kDefaultWavesN, 8, false, true>(g, stream) : hipErrorInvalidValue;
     switch (g.w_bits) {
         case 8: return launch_config<kDefaultWavesN, 8, false>(g, stream);
         case 4:

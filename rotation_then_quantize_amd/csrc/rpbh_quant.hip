@@ -303,6 +303,7 @@ struct RowExtra {
     int32_t* sum;
     unsigned long long* clear;   // words the first workgroup zeroes (the next product's split counters)
     int nclear;
+    int tiled;                   // INT8 codes in the product's tiled layout
 };
 
 // The first workgroup zeroes the words the launch was asked to clear.
@@ -592,7 +593,13 @@ template <int kOut>
 __device__ __forceinline__ void store_block(const BlockOut& res, void* __restrict__ out, void* __restrict__ scale_out,
                                             int scale_bf16, RowExtra ex, int64_t row, int blk, int d) {
     constexpr int kWords = kH * out_bits<kOut>() / 32;
-    if constexpr (kWords % 4 == 0) {
+    if (kOut == kRowInt8 && ex.tiled) {   // the product's tiled layout: a 64-byte slot, chunks swizzled
+        int8_t* o = static_cast<int8_t*>(out) + tiled_slot_offset(row, blk, d);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<uint4*>(o + 16 * tiled_chunk(row, q)) =
+                make_uint4(res.w[4 * q], res.w[4 * q + 1], res.w[4 * q + 2], res.w[4 * q + 3]);
+    } else if constexpr (kWords % 4 == 0) {
         uint4* o = reinterpret_cast<uint4*>(static_cast<uint8_t*>(out) + (row * d + blk * kH) * out_bits<kOut>() / 8);
 #pragma unroll
         for (int q = 0; q < kWords / 4; ++q) o[q] = make_uint4(res.w[4 * q], res.w[4 * q + 1], res.w[4 * q + 2], res.w[4 * q + 3]);
@@ -934,7 +941,7 @@ hipError_t launch_wave(const RowArgs& a, int log2d, hipStream_t stream) {
     const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(cap, (units + kThreads / 64 - 1) / (kThreads / 64)));
     hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), lds, stream,
                        static_cast<const uint16_t*>(a.x), a.rows, a.d, log2d, a.perm, a.signs, a.out, a.scale,
-                       a.scale_bf16 ? 1 : 0, a.bounds, a.eps, a.centroids, RowExtra{a.zero, a.sum, a.clear, a.nclear});
+                       a.scale_bf16 ? 1 : 0, a.bounds, a.eps, a.centroids, RowExtra{a.zero, a.sum, a.clear, a.nclear, a.tiled ? 1 : 0});
     return hipGetLastError();
 }
 
@@ -957,7 +964,7 @@ hipError_t launch_t(const RowArgs& a, int log2d, hipStream_t stream) {
     const int grid = static_cast<int>((ngroups + per_wg - 1) / per_wg);
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), lds, stream, static_cast<const uint16_t*>(a.x), a.rows,
                        a.d, log2d, log2nb, a.perm, a.signs, a.out, a.scale, a.scale_bf16 ? 1 : 0, a.bounds, a.eps,
-                       a.centroids, RowExtra{a.zero, a.sum, a.clear, a.nclear});
+                       a.centroids, RowExtra{a.zero, a.sum, a.clear, a.nclear, a.tiled ? 1 : 0});
     return hipGetLastError();
 }
 

@@ -96,7 +96,7 @@ __global__ void __launch_bounds__(kThreads)
 rpbh_rows_kernel(const void* __restrict__ xin, int64_t rows, int d, int log2d, int log2nb,
                  const int32_t* __restrict__ perm, const int8_t* __restrict__ signs, void* __restrict__ out,
                  void* __restrict__ scale_out, int scale_bf16, const float* __restrict__ bounds, float eps,
-                 const float* __restrict__ cent) {
+                 const float* __restrict__ cent, int tiled) {
     constexpr int ES = kBF16In ? 2 : 4;
     // codebook outputs: kRowCode* pack the codes, kRowLut* write each code's int8 codebook value
     constexpr bool k4 = kOut == kRowCode4 || kOut == kRowLut4;
@@ -257,9 +257,17 @@ rpbh_rows_kernel(const void* __restrict__ xin, int64_t rows, int d, int log2d, i
                 }
             }
             if (valid) {
-                uint4* o = reinterpret_cast<uint4*>(static_cast<int8_t*>(out) + row * d + blk * kH);
+                if (tiled) {
+                    int8_t* o = static_cast<int8_t*>(out) + tiled_slot_offset(row, blk, d);
 #pragma unroll
-                for (int q = 0; q < kH / 16; ++q) o[q] = make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+                    for (int q = 0; q < kH / 16; ++q)
+                        *reinterpret_cast<uint4*>(o + 16 * tiled_chunk(row, q)) =
+                            make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+                } else {
+                    uint4* o = reinterpret_cast<uint4*>(static_cast<int8_t*>(out) + row * d + blk * kH);
+#pragma unroll
+                    for (int q = 0; q < kH / 16; ++q) o[q] = make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+                }
                 if (blk == 0) {
                     if (scale_bf16)
                         static_cast<uint16_t*>(scale_out)[row] = static_cast<uint16_t>(f32_to_bf16(s));
@@ -431,7 +439,7 @@ hipError_t launch_rows_t(const RowArgs& a, hipStream_t stream) {
     const size_t lds = static_cast<size_t>(kGroup) * ES + static_cast<size_t>(a.d) * ES + kRedBytes;
     return launch_persistent(rpbh_rows_kernel<kBF16In, kRotate, kOut>, lds, ngroups, stream, a.x, a.rows, a.d,
                              log2d, log2nb, a.perm, a.signs, a.out, a.scale, a.scale_bf16 ? 1 : 0, a.bounds, a.eps,
-                             a.centroids);
+                             a.centroids, a.tiled ? 1 : 0);
 }
 
 template <bool kBF16In, bool kRotate>

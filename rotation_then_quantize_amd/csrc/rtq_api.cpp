@@ -111,10 +111,11 @@ rtq_status plan_quantize(const void* x, rtq_dtype xt, int64_t rows, int32_t d, c
     a.scale = scale;
     a.scale_bf16 = scale_t == RTQ_BF16;
     a.eps = eps;
-    if (mode == RTQ_INT8) {
-        if (cb != nullptr) return fail(RTQ_ERR_INVALID_ARG, "cb must be NULL for RTQ_INT8");
+    if (mode == RTQ_INT8 || mode == RTQ_INT8_TILED) {
+        if (cb != nullptr) return fail(RTQ_ERR_INVALID_ARG, "cb must be NULL for RTQ_INT8 and RTQ_INT8_TILED");
         a.out_kind = rtq::kRowInt8;
         a.bounds = nullptr;
+        a.tiled = mode == RTQ_INT8_TILED;
     } else if (mode == RTQ_CODEBOOK) {
         RTQ_TRY(check_codebook(cb, "cb", false, true));
         if (!(eps >= 0.0f) || std::isinf(eps)) return fail(RTQ_ERR_INVALID_ARG, "eps must be finite and >= 0");
@@ -163,8 +164,9 @@ rtq_status plan_gemm(const void* a_codes, const float* a_scale, int64_t T, const
         return fail(RTQ_ERR_MISALIGNED, "w_scale is not 4-byte aligned");
     if ((T + 127) / 128 > 65535) return fail(RTQ_ERR_UNSUPPORTED, "T too large (max %d)", 65535 * 128);
     GemmPlan p{};
-    if (mode == RTQ_INT8) {
-        if (cb_a != nullptr || cb_w != nullptr) return fail(RTQ_ERR_INVALID_ARG, "codebooks must be NULL for RTQ_INT8");
+    if (mode == RTQ_INT8 || mode == RTQ_INT8_TILED) {
+        if (cb_a != nullptr || cb_w != nullptr)
+            return fail(RTQ_ERR_INVALID_ARG, "codebooks must be NULL for RTQ_INT8 and RTQ_INT8_TILED");
         if (yt != RTQ_F32 && yt != RTQ_BF16 && yt != RTQ_I32) return fail(RTQ_ERR_UNSUPPORTED, "bad yt");
         const int y_kind = yt == RTQ_F32 ? 0 : (yt == RTQ_BF16 ? 1 : 2);
         if (N > rtq::gemm_i8_max_n(y_kind))
@@ -174,6 +176,7 @@ rtq_status plan_gemm(const void* a_codes, const float* a_scale, int64_t T, const
         p.i8 = rtq::GemmI8Args{static_cast<const int8_t*>(a_codes), a_scale, static_cast<const int8_t*>(w_codes),
                                w_scale, w_scale_t == RTQ_BF16, T, N, d, y,
                                yt == RTQ_F32 ? 0 : (yt == RTQ_BF16 ? 1 : 2)};
+        p.i8.tiled = mode == RTQ_INT8_TILED;
     } else if (mode == RTQ_CODEBOOK) {
         RTQ_TRY(check_codebook(cb_a, "cb_a", true, false));
         RTQ_TRY(check_codebook(cb_w, "cb_w", true, false));
@@ -217,7 +220,9 @@ size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 size_t workspace_bytes(int64_t T, int32_t d, rtq_qmode mode, int32_t bits_a, bool with_split = true) {
     if (T < 0 || d <= 0) return 0;
     size_t code_bytes;
-    if (mode == RTQ_INT8 || (mode == RTQ_CODEBOOK_I8 && (bits_a == 2 || bits_a == 3 || bits_a == 4 || bits_a == 6)))
+    if (mode == RTQ_INT8_TILED)
+        code_bytes = static_cast<size_t>(rtq::tiled_rows(T)) * static_cast<size_t>(d);
+    else if (mode == RTQ_INT8 || (mode == RTQ_CODEBOOK_I8 && (bits_a == 2 || bits_a == 3 || bits_a == 4 || bits_a == 6)))
         code_bytes = static_cast<size_t>(T) * static_cast<size_t>(d);
     else if (mode == RTQ_CODEBOOK && (bits_a == 2 || bits_a == 4))
         code_bytes = static_cast<size_t>(T) * static_cast<size_t>(d) * static_cast<size_t>(bits_a) / 8;
@@ -282,8 +287,10 @@ rtq_status rotated_qlinear_ws(const void* x, rtq_dtype xt, int64_t T, const rtq_
     if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return fail(RTQ_ERR_MISALIGNED, "workspace is not 16-byte aligned");
     if (ws_bytes < need) return fail(RTQ_ERR_INVALID_ARG, "workspace too small: %zu < %zu bytes", ws_bytes, need);
     unsigned char* ws = static_cast<unsigned char*>(workspace);
-    const size_t code_bytes = mode == RTQ_CODEBOOK ? static_cast<size_t>(T < 0 ? 0 : T) * d * bits_a / 8
-                                                   : static_cast<size_t>(T < 0 ? 0 : T) * d;
+    const int64_t rows = T < 0 ? 0 : T;
+    const size_t code_bytes = mode == RTQ_CODEBOOK     ? static_cast<size_t>(rows) * d * bits_a / 8
+                              : mode == RTQ_INT8_TILED ? static_cast<size_t>(rtq::tiled_rows(rows)) * d
+                                                       : static_cast<size_t>(rows) * d;
     void* a_codes = ws;
     float* a_scale = reinterpret_cast<float*>(ws + align256(code_bytes));
     rtq::RowArgs qa{};

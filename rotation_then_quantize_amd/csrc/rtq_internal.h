@@ -22,6 +22,21 @@ enum RowOut : int {
     kRowInt8Asym = 10,  // asymmetric INT8 codes + per-row scale, zero point and code sum
 };
 
+// The tiled layout of INT8 operands (RTQ_INT8_TILED): rows are grouped in tiles of 256 and the K
+// dimension in slices of 64 bytes; block (tile, slice) is 16 KB, contiguous, [256 rows][64 bytes],
+// and within a row's 64 bytes the 16-byte chunk c sits at chunk c ^ ((row >> 2) & 3).  This is the
+// image of one LDS stage of the INT8 product, so its loads copy whole 1 KB runs.  Rows are padded
+// to a multiple of 256 (padding rows are neither written nor used).
+constexpr int kTileRows = 256;
+constexpr int kTileK = 64;
+__host__ __device__ constexpr int64_t tiled_rows(int64_t rows) { return (rows + kTileRows - 1) / kTileRows * kTileRows; }
+// Byte offset of the 64-byte slot of row `row`, K slice `blk` (bytes blk*64 .. +64 of the row).
+__host__ __device__ inline int64_t tiled_slot_offset(int64_t row, int blk, int d) {
+    return ((row / kTileRows) * (d / kTileK) + blk) * (kTileRows * kTileK) + (row % kTileRows) * kTileK;
+}
+// Position (in 16-byte chunks) of chunk c of a row inside its 64-byte slot.
+__host__ __device__ inline int tiled_chunk(int64_t row, int c) { return c ^ static_cast<int>((row >> 2) & 3); }
+
 struct RowArgs {
     const void* x;          // [rows][d] fp32 or bf16
     bool x_bf16;
@@ -38,6 +53,7 @@ struct RowArgs {
     const float* centroids = nullptr;   // codebook centroids (device), 2^bits entries (kRowLut*)
     int32_t* zero = nullptr;            // kRowInt8Asym: per-row zero point
     int32_t* sum = nullptr;             // kRowInt8Asym: per-row sum of the codes
+    bool tiled = false;                 // kRowInt8: codes in the tiled layout (see above)
     // words zeroed by the launch (the K-split counters of the product that follows on the stream)
     unsigned long long* clear = nullptr;
     int nclear = 0;
@@ -68,7 +84,8 @@ struct GemmI8Args {
     int64_t T, N;
     int d;
     void* y;                // [T][N]
-    int y_kind;             // 0 fp32, 1 bf16, 2 raw int32 (w_bits 8 only)
+    int y_kind;             // 0 fp32, 1 bf16, 2 raw int32
+    bool tiled = false;     // int8 weights and codes: both operands in the tiled layout
     // codebook operands on the INT8 matrix cores (w_bits 4 or 2): both codebooks are rounded to
     // int8 as v_k = rint(c_k * S), S = 127 / max_k |c_k|; the product is rescaled by 1/(S_a S_w)
     int w_bits = 8;

@@ -77,3 +77,35 @@ def codes_of(values, table):
     flat = np.array([lookup.get(int(v), -1) for v in values.ravel()], np.int64)
     assert (flat >= 0).all(), "value outside the codebook table"
     return flat.reshape(values.shape)
+
+
+def tile_codes(codes):
+    """Row-major int8 codes [rows][d] -> the tiled layout of RTQ_INT8_TILED (a flat int8 array of
+    ceil(rows/256)*256*d bytes; padding rows are zero): block (row // 256, j // 64) of 16 KB holds
+    [256 rows][64 bytes], chunk c of a row's 64 bytes at chunk c ^ ((row >> 2) & 3)."""
+    codes = np.asarray(codes, np.int8)
+    rows, d = codes.shape
+    rp = -(-rows // 256) * 256
+    full = np.zeros((rp, d), np.int8)
+    full[:rows] = codes
+    # [tile][256][slice][4 chunks][16] -> [tile][slice][256][4 chunks (swizzled)][16]
+    v = full.reshape(rp // 256, 256, d // 64, 4, 16)
+    r = np.arange(256)
+    perm = (np.arange(4)[None, :] ^ ((r[:, None] >> 2) & 3))           # [256][4]: chunk c -> slot
+    out = np.empty((rp // 256, d // 64, 256, 4, 16), np.int8)
+    for c in range(4):
+        out[:, :, r, perm[:, c], :] = v[:, :, :, c, :].transpose(0, 2, 1, 3)
+    return out.reshape(-1)
+
+
+def untile_codes(buf, rows, d):
+    """Inverse of tile_codes: the first `rows` rows as a row-major [rows][d] int8 array."""
+    buf = np.asarray(buf).view(np.int8).reshape(-1)
+    rp = -(-rows // 256) * 256
+    v = buf[:rp * d].reshape(rp // 256, d // 64, 256, 4, 16)
+    r = np.arange(256)
+    perm = (np.arange(4)[None, :] ^ ((r[:, None] >> 2) & 3))
+    full = np.empty((rp // 256, 256, d // 64, 4, 16), np.int8)
+    for c in range(4):
+        full[:, :, :, c, :] = v[:, :, r, perm[:, c], :].transpose(0, 2, 1, 3)
+    return full.reshape(rp, d)[:rows]

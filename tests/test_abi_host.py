@@ -172,6 +172,8 @@ def test_qgemm_and_qlinear_validation():
     split256 = (split + 255) // 256 * 256
     assert ws(4608, 4096, rtq.RTQ_INT8, 8) == 4608 * 4096 + 4608 * 4 + (256 - (4608 * 4) % 256) % 256 + split256
     assert ws(4608, 4096, rtq.RTQ_CODEBOOK_I8, 4) == 4608 * 4096 + 18432 + split256
+    assert ws(4608, 4096, rtq.RTQ_INT8_TILED, 8) == ws(4608, 4096, rtq.RTQ_INT8, 8)
+    assert ws(100, 256, rtq.RTQ_INT8_TILED, 8) == 256 * 256 + 512 + split256     # rows padded to 256
     assert ws(4608, 4096, rtq.RTQ_CODEBOOK, 4) == 4608 * 2048 + 18432
     assert ws(10, 4096, rtq.RTQ_CODEBOOK, 3) == 0
     assert ws(4608, 4096, rtq.RTQ_CODEBOOK_I8, 3) == ws(4608, 4096, rtq.RTQ_CODEBOOK_I8, 6) == \

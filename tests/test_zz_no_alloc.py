@@ -21,11 +21,11 @@ def _gpu():
     rtq.load_library()
 
 
-def _int8_weights(N, d, R, seed):
+def _int8_weights(N, d, R, seed, mode):
     wh = workloads.f32_to_bf16_bits(workloads.small_case(seed, N, d, "w"))
-    wq = torch.empty((N, d), dtype=torch.int8, device="cuda")
+    wq = torch.empty(((rtq.tiled_rows(N) if mode == rtq.RTQ_INT8_TILED else N), d), dtype=torch.int8, device="cuda")
     ws = torch.empty(N, dtype=torch.bfloat16, device="cuda")
-    rtq.quantize_rows(to_dev(wh, "bf16"), wq, ws, R, rtq.RTQ_INT8)
+    rtq.quantize_rows(to_dev(wh, "bf16"), wq, ws, R, mode)
     return wq, ws
 
 
@@ -33,18 +33,19 @@ def _same_bits(a, b):
     return torch.equal(a.view(torch.int16), b.view(torch.int16)) if a.dtype == torch.bfloat16 else torch.equal(a, b)
 
 
+@pytest.mark.parametrize("mode", [rtq.RTQ_INT8, rtq.RTQ_INT8_TILED])
 @pytest.mark.parametrize("d,N,tokens", [(4096, 16384, (4608, 1000)), (1024, 300, (517, 129)), (256, 512, (128, 33))])
-def test_noalloc_int8_matches_workspace_layer(d, N, tokens):
+def test_noalloc_int8_matches_workspace_layer(d, N, tokens, mode):
     R = rtq.Rpbh.from_seed(61, d)
-    wq, ws = _int8_weights(N, d, R, 7100 + d)
+    wq, ws = _int8_weights(N, d, R, 7100 + d, mode)
     for T in tokens:                       # the second call is smaller
-        print(f"noalloc int8 d={d} N={N} T={T}", flush=True)
+        print(f"noalloc int8 mode={mode} d={d} N={N} T={T}", flush=True)
         xh = workloads.f32_to_bf16_bits(workloads.small_case(7200 + T + d, T, d, "t3"))
         x = to_dev(xh, "bf16")
         y_ref = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
         y = torch.full((T, N), float("nan"), dtype=torch.bfloat16, device="cuda")
-        rtq.rotated_qlinear(x, R, wq, ws, y_ref)
-        rtq.rotated_qlinear_noalloc(x, R, wq, ws, y)
+        rtq.rotated_qlinear(x, R, wq, ws, y_ref, mode)
+        rtq.rotated_qlinear_noalloc(x, R, wq, ws, y, mode)
         torch.cuda.synchronize()
         assert _same_bits(y, y_ref)
 
