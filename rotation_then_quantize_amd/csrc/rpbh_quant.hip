@@ -656,16 +656,32 @@ rpbh_quant_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int 
     uint32_t addr[kTabAddr ? 1 : kNC * 8];
     uint4 msk[kMaskInLds ? 1 : kNC];
     if constexpr (kTabAddr) {
-        for (int j = 4 * tid; j < d; j += 4 * kThreads) {
-            const int4 pv = *reinterpret_cast<const int4*>(perm + j);
-            const uint32_t sv = *reinterpret_cast<const uint32_t*>(signs + j);
-            const int pj[4] = {pv.x, pv.y, pv.z, pv.w};
+        // batches of 8 loads per thread (16 at d = 16384), issued before their LDS stores
+        constexpr int kBatch = 8;
+        for (int j0 = 4 * tid; j0 < d; j0 += 4 * kThreads * kBatch) {
+            int4 pv[kBatch];
+            uint32_t sv[kBatch];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t c = static_cast<uint32_t>(pj[e]) & dmask;
-                const uint32_t jj = static_cast<uint32_t>(j + e);
-                sg[c] = static_cast<uint16_t>(((jj >> 6) * (kBlockPitch / 2) + (jj & 63u)) |
-                                              ((sv >> (8 * e + 7)) & 1u ? 0x8000u : 0u));
+            for (int i = 0; i < kBatch; ++i) {
+                const int j = j0 + i * 4 * kThreads;
+                if (j < d) {
+                    pv[i] = *reinterpret_cast<const int4*>(perm + j);
+                    sv[i] = *reinterpret_cast<const uint32_t*>(signs + j);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) {
+                const int j = j0 + i * 4 * kThreads;
+                if (j < d) {
+                    const int pj[4] = {pv[i].x, pv[i].y, pv[i].z, pv[i].w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t c = static_cast<uint32_t>(pj[e]) & dmask;
+                        const uint32_t jj = static_cast<uint32_t>(j + e);
+                        sg[c] = static_cast<uint16_t>(((jj >> 6) * (kBlockPitch / 2) + (jj & 63u)) |
+                                                      ((sv[i] >> (8 * e + 7)) & 1u ? 0x8000u : 0u));
+                    }
+                }
             }
         }
     } else {
@@ -836,16 +852,31 @@ rpbh_wave_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int d, int l
     // signs[j]: the table entry of that column holds j's LDS address within wave 0's buffer (the
     // LDS address of smem plus its offset there) and sign bit.
     const uint32_t lds0 = lds_address(smem);
-    for (int j = 4 * tid; j < d; j += 4 * kThreads) {
-        const int4 pv = *reinterpret_cast<const int4*>(perm + j);
-        const uint32_t sv = *reinterpret_cast<const uint32_t*>(signs + j);
-        const int pj[4] = {pv.x, pv.y, pv.z, pv.w};
+    // all of this thread's descriptor loads first (d <= 4096: at most 4 each), then the scatter, so
+    // their latencies overlap instead of adding up
+    constexpr int kTabIters = kWaveMaxD / (4 * kThreads);
+    int4 pv[kTabIters];
+    uint32_t sv[kTabIters];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t c = static_cast<uint32_t>(pj[e]) & dmask;
-            const uint32_t jj = static_cast<uint32_t>(j + e);
-            tab_off[c] = lds0 + (jj >> 6) * kBlockPitch + (jj & 63u) * 2u;
-            tab_sgn[c] = (sv >> (8 * e + 7)) & 1u ? 0x8000u : 0u;
+    for (int it = 0; it < kTabIters; ++it) {
+        const int j = 4 * tid + it * 4 * kThreads;
+        if (j < d) {
+            pv[it] = *reinterpret_cast<const int4*>(perm + j);
+            sv[it] = *reinterpret_cast<const uint32_t*>(signs + j);
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < kTabIters; ++it) {
+        const int j = 4 * tid + it * 4 * kThreads;
+        if (j < d) {
+            const int pj[4] = {pv[it].x, pv[it].y, pv[it].z, pv[it].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t c = static_cast<uint32_t>(pj[e]) & dmask;
+                const uint32_t jj = static_cast<uint32_t>(j + e);
+                tab_off[c] = lds0 + (jj >> 6) * kBlockPitch + (jj & 63u) * 2u;
+                tab_sgn[c] = (sv[it] >> (8 * e + 7)) & 1u ? 0x8000u : 0u;
+            }
         }
     }
     CodeCtx<kOut> cc;
