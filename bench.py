@@ -148,7 +148,7 @@ def bench_w8a8(args, torch, rtq, workloads, mode=None):
     def quant(i):
         rtq.quantize_rows(xs[i % len(xs)], codes, scale, R, mode)
 
-    split_ws = torch.empty(rtq.qgemm_workspace(), dtype=torch.uint8, device="cuda")
+    split_ws = rtq.new_qgemm_workspace()
 
     def gemm(i):
         rtq.qgemm(codes, scale, wq, ws, y, d, mode, workspace=split_ws, n_tokens=T, n_out=N)
@@ -191,20 +191,26 @@ def bench_w8a8(args, torch, rtq, workloads, mode=None):
 
 
 def bench_offline(args, torch, rtq, workloads):
-    """Offline rotate + INT8 quantise of one DiT block's four linears (bf16 in, int8 + bf16 scale out)."""
+    """Offline rotate + INT8 quantise of one DiT block's four linears (bf16 in; int8 codes in the
+    product's tiled layout + bf16 row scales out): the four launches back to back, and each linear
+    alone (a burst of its launch), for the per-kernel roofline."""
     mats = []
     total = 0
     for name, n_out, d_in in workloads.DIT_LINEARS:
         w = _bf16_dev(workloads.dit_weight_bf16(name), torch)
         R = rtq.Rpbh.from_seed(workloads.RPBH_SEED[d_in], d_in)
-        q = torch.empty((n_out, d_in), dtype=torch.int8, device="cuda")
+        q = torch.empty((rtq.tiled_rows(n_out), d_in), dtype=torch.int8, device="cuda")
         s = torch.empty(n_out, dtype=torch.bfloat16, device="cuda")
-        mats.append((w, R, q, s))
+        mats.append((name, w, R, q, s, n_out * d_in * 3 + n_out * 2))
         total += n_out * d_in * 3 + n_out * 2
 
+    def launch(m):
+        _, w, R, q, s, _ = m
+        rtq.quantize_rows(w, q, s, R, rtq.RTQ_INT8_TILED)
+
     def run():
-        for w, R, q, s in mats:
-            rtq.quantize_rows(w, q, s, R, rtq.RTQ_INT8)
+        for m in mats:
+            launch(m)
 
     for _ in range(max(1, args.warmup // 2)):
         run()
@@ -217,7 +223,14 @@ def bench_offline(args, torch, rtq, workloads):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
-    return {"bytes": total, "ms": ms, "GB/s": total / (ms * 1e-3) / 1e9}
+    per = {}
+    for m in mats:
+        t = _burst_ms(max(5, reps), lambda i, m=m: launch(m), torch)
+        per[m[0]] = {"ms": t, "bytes": m[5], "GB/s": m[5] / (t * 1e-3) / 1e9,
+                     "frac_hbm": m[5] / (t * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+    return {"bytes": total, "ms": ms, "GB/s": total / (ms * 1e-3) / 1e9,
+            "frac_hbm": total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, "per_linear": per,
+            "codes_layout": "tiled (RTQ_INT8_TILED)"}
 
 
 def bench_codebook(args, torch, rtq, workloads, variant, mode=None):
@@ -251,7 +264,7 @@ def bench_codebook(args, torch, rtq, workloads, variant, mode=None):
     def quant(i):
         rtq.quantize_rows(xs[i % len(xs)], codes, norm, R, mode, cb_a, 1e-8)
 
-    split_ws = torch.empty(rtq.qgemm_workspace(), dtype=torch.uint8, device="cuda")
+    split_ws = rtq.new_qgemm_workspace()
 
     def gemm(i):
         rtq.qgemm(codes, norm, wc, wn, y, d, mode, cb_a, cb_w, workspace=split_ws)
@@ -298,7 +311,7 @@ def bench_w8a8_asym(args, torch, rtq, workloads):
     zero = torch.empty(T, dtype=torch.int32, device="cuda")
     csum = torch.empty(T, dtype=torch.int32, device="cuda")
     y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
-    split_ws = torch.empty(rtq.qgemm_workspace(), dtype=torch.uint8, device="cuda")
+    split_ws = rtq.new_qgemm_workspace()
 
     def quant(i):
         rtq.quantize_rows_asym(xs[i % len(xs)], codes, scale, zero, csum, R)
@@ -496,7 +509,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
-    ap.add_argument("--only", choices=["w8a8", "codebook", "ablation", "asym", "all"], default="all",
+    ap.add_argument("--only", choices=["w8a8", "codebook", "ablation", "asym", "offline", "all"], default="all",
                     help="w8a8: time only the headline step (profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain streaming kernel of known size (bitwise_not over 256 MiB of int8, "
@@ -530,6 +543,9 @@ def main():
         del src, dst
     if args.only == "asym":
         print(json.dumps(bench_w8a8_asym(args, torch, rtq, workloads)))
+        return
+    if args.only == "offline":   # the offline weight rotate-quantise only (profiling runs)
+        print(json.dumps(bench_offline(args, torch, rtq, workloads)))
         return
     if args.only == "ablation":
         print(json.dumps(bench_ablation(args, torch, rtq, workloads)))

@@ -176,18 +176,20 @@ rtq_status rtq_qgemm(const void* a_codes, const float* a_scale, int64_t T, const
  * cut into equal K ranges.  A piece that holds only part of a tile stores an int32 partial tile
  * in the workspace, and the last piece of the tile to finish adds the others (exact int32 sums, so
  * results equal rtq_qgemm's bit for bit).
- *   workspace: device memory of at least rtq_qgemm_workspace() bytes, 16-byte aligned, any
- *   contents: when the split is used, the call first zeroes the per-tile arrival counters with a
- *   small fill kernel on `stream` (no memset node, so the call may be captured in a graph).
- *   Launches that share a workspace must not run concurrently.  A smaller or NULL workspace, or
- *   the RTQ_CODEBOOK mode, gives exactly rtq_qgemm. */
+ *   workspace: device memory of at least rtq_qgemm_workspace() bytes, 16-byte aligned, zero-filled
+ *   once before its first use: it ends with one 8-byte arrival counter per shared tile (the last
+ *   16 bytes per compute unit), which must start at zero; the block that finishes a shared tile
+ *   sets its counter back to zero, so every call that completes leaves the workspace reusable as
+ *   is (the partial tiles before the counters may hold anything).  Launches that share a
+ *   workspace must not run concurrently.  A smaller or NULL workspace, or the RTQ_CODEBOOK mode,
+ *   gives exactly rtq_qgemm. */
 rtq_status rtq_qgemm_ws(const void* a_codes, const float* a_scale, int64_t T, const void* w_codes,
                         const void* w_scale, rtq_dtype w_scale_t, int64_t N, int32_t d, rtq_qmode mode,
                         const rtq_codebook* cb_a, const rtq_codebook* cb_w, void* y, rtq_dtype yt,
                         void* workspace, size_t ws_bytes, void* stream);
 
-/* Bytes of workspace rtq_qgemm_ws uses on the current device: two 256 KB int32 partial tiles and
- * two 8-byte counters per compute unit (128 MB on a 256-CU MI355X). */
+/* Bytes of workspace rtq_qgemm_ws uses on the current device: two 256 KB int32 partial tiles per
+ * compute unit, then two 8-byte counters per compute unit (128 MB on a 256-CU MI355X). */
 size_t rtq_qgemm_workspace(void);
 
 /* The online layer: rtq_quantize_rows(x, R, mode, cb_a, eps = 1e-8 (CODEBOOK) ...) into `workspace`
@@ -246,7 +248,7 @@ rtq_status rtq_quantize_rows_asym(const void* x, rtq_dtype xt, int64_t rows, int
  * int32 (evaluated as acc' - zw sum(qa) - za (sum(qw) - d zw) from the int8 products acc'), then
  * y = acc * a_scale[t] * w_scale[n] in fp32, stored as yt (F32, BF16, or RTQ_I32 for acc itself).
  * a_codes int8[T][d], a_scale fp32[T], a_zero/a_sum int32[T]; w_codes int8[N][d], w_scale [N] of
- * w_scale_t, w_zero/w_sum int32[N]; workspace as for rtq_qgemm_ws (may be NULL). */
+ * w_scale_t, w_zero/w_sum int32[N]; workspace as for rtq_qgemm_ws (zero-filled once; may be NULL). */
 rtq_status rtq_qgemm_asym(const int8_t* a_codes, const float* a_scale, const int32_t* a_zero, const int32_t* a_sum,
                           int64_t T, const int8_t* w_codes, const void* w_scale, rtq_dtype w_scale_t,
                           const int32_t* w_zero, const int32_t* w_sum, int64_t N, int32_t d, void* y, rtq_dtype yt,

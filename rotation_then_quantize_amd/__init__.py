@@ -261,6 +261,12 @@ def qgemm_workspace() -> int:
     return int(load_library().rtq_qgemm_workspace())
 
 
+def new_qgemm_workspace(device="cuda"):
+    """A zero-filled workspace for qgemm(..., workspace=...): its arrival counters must start at
+    zero, and every product that completes leaves them zero again, so it can be reused as is."""
+    return _torch().zeros(qgemm_workspace(), dtype=_torch().uint8, device=device)
+
+
 def rotated_qlinear_workspace(T: int, d: int, mode: int = RTQ_INT8, bits_a: int = 8) -> int:
     return int(load_library().rtq_rotated_qlinear_workspace(T, d, mode, bits_a))
 

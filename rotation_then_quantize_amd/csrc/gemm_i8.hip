@@ -173,9 +173,10 @@ __device__ __forceinline__ void decode3(const uint32_t (&lut)[4], const uint32_t
 // run meets a tile only in part stores its int32 partial tile and arrives on the tile's counter;
 // the last to arrive adds the others' partials and runs the epilogue (no block ever waits for
 // another; a stream-K tile's second piece to finish skips its own store, see the epilogue).
-// The counters are zero when the launch starts: a fill kernel (or the quantiser launch that
-// precedes the product on the same stream) clears them, so arrivals are counted from a known
-// state whatever the workspace held before.
+// The counters are zero when the launch starts (the quantiser launch that precedes the product in
+// the layer clears them; a standalone product's workspace is zero-filled once by its owner), and
+// the block that finishes a shared tile sets its counter back to zero, so every complete launch
+// leaves them zero for the next.
 constexpr int kMaxSplit = 8;
 
 struct SplitArgs {
@@ -196,6 +197,12 @@ constexpr int64_t shared_tiles_cap(int64_t slots) { return 2 * slots; }
 __device__ __forceinline__ unsigned int split_arrive(unsigned long long* c, unsigned int add) {
     return static_cast<unsigned int>(
         __hip_atomic_fetch_add(c, static_cast<unsigned long long>(add), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// The block that finishes a shared tile leaves its counter at zero again, so a launch that completes
+// leaves every counter as it found it.
+__device__ __forceinline__ void split_reset(unsigned long long* c) {
+    __hip_atomic_store(c, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __global__ void __launch_bounds__(256) split_clear_kernel(unsigned long long* __restrict__ c, int n) {
@@ -661,7 +668,11 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
         const bool head = sk && cord == 0;
         if (ctail && head) {
             __syncthreads();
-            if (tid == 0) s_flag[0] = static_cast<int>(split_arrive(sp.counters + ctile, 2u));
+            if (tid == 0) {
+                const unsigned int v = split_arrive(sp.counters + ctile, 2u);
+                if (v & 1u) split_reset(sp.counters + ctile);   // the tail has arrived: this block finishes
+                s_flag[0] = static_cast<int>(v);
+            }
             __syncthreads();
             publish = (static_cast<unsigned int>(s_flag[0]) & 1u) == 0u;
         }
@@ -689,7 +700,9 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
             __syncthreads();
             if (tid == 0) {
                 const unsigned int v = split_arrive(sp.counters + ctile, sk ? (head ? 4u : 1u) : 1u);
-                s_flag[0] = sk ? (v & (head ? 1u : 4u)) != 0u : v == static_cast<unsigned int>(ccount - 1);
+                const bool last = sk ? (v & (head ? 1u : 4u)) != 0u : v == static_cast<unsigned int>(ccount - 1);
+                if (last) split_reset(sp.counters + ctile);    // nobody arrives on this tile again
+                s_flag[0] = last;
             }
             __syncthreads();
             epilogue = s_flag[0] != 0;
@@ -900,12 +913,6 @@ hipError_t launch_config(const GemmI8Args& g, hipStream_t stream) {
                            reinterpret_cast<unsigned long long*>(
                                ws + static_cast<size_t>(partial_slots_cap(slots)) * BM * BN * 4)};
             grid = slots;
-            if (!g.counters_zeroed) {
-                hipLaunchKernelGGL(split_clear_kernel, dim3(1), dim3(256), 0, stream, sp.counters,
-                                   static_cast<int>(shared_tiles_cap(slots)));
-                const hipError_t ce = hipGetLastError();
-                if (ce != hipSuccess) return ce;
-            }
         }
     }
     const KernelFn k = kernels[g.w_scale_bf16 ? 1 : 0][(g.N % 8) == 0 ? 1 : 0][g.y_kind];

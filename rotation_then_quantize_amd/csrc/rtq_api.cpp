@@ -306,7 +306,6 @@ rtq_status rotated_qlinear_ws(const void* x, rtq_dtype xt, int64_t T, const rtq_
         gp.i8.workspace = ws + split_off;
         gp.i8.ws_bytes = ws_bytes - split_off;
         qa.clear = rtq::gemm_i8_split_counters(gp.i8.workspace, gp.i8.ws_bytes, &qa.nclear);
-        gp.i8.counters_zeroed = true;
     }
     RTQ_TRY(hip_status(rtq::launch_rpbh_rows(qa, s), "rpbh_rows launch"));
     if (gp.lut) return hip_status(rtq::launch_gemm_lut(gp.cb, s), "gemm_lut launch");
@@ -531,7 +530,6 @@ rtq_status rtq_rotated_qlinear_asym(const void* x, rtq_dtype xt, int64_t T, cons
     gp.i8.workspace = ws + off;
     gp.i8.ws_bytes = ws_bytes - off;
     qa.clear = rtq::gemm_i8_split_counters(gp.i8.workspace, gp.i8.ws_bytes, &qa.nclear);
-    gp.i8.counters_zeroed = true;
     RTQ_TRY(hip_status(rtq::launch_rpbh_rows(qa, s), "rpbh_rows launch"));
     return hip_status(rtq::launch_gemm_i8(gp.i8, s), "gemm_i8 launch");
 }

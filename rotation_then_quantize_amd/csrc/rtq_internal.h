@@ -101,9 +101,6 @@ struct GemmI8Args {
     // along K (stream-K runs, or equal K ranges per tile)
     void* workspace = nullptr;
     size_t ws_bytes = 0;
-    // the workspace's split counters were zeroed earlier on this stream (by the quantiser launch):
-    // no fill kernel is needed before the product
-    bool counters_zeroed = false;
 };
 
 hipError_t launch_gemm_i8(const GemmI8Args& g, hipStream_t stream);

@@ -73,7 +73,7 @@ def test_qgemm_asym_accumulators_bit_exact(T, N, d):
     sw = qw.astype(np.int64).sum(1).astype(np.int32)
     ref = oracle.gemm_int8_asym(qa, za, qw, zw)
     ones_t, ones_n = to_dev(np.ones(T, np.float32)), to_dev(np.ones(N, np.float32))
-    ws = torch.empty(rtq.qgemm_workspace(), dtype=torch.uint8, device="cuda")
+    ws = rtq.new_qgemm_workspace()
     for workspace in (None, ws):
         acc = torch.empty((T, N), dtype=torch.int32, device="cuda")
         rtq.qgemm_asym(to_dev(qa), ones_t, to_dev(za), to_dev(sa), to_dev(qw), ones_n, to_dev(zw), to_dev(sw), acc, d,
@@ -104,7 +104,7 @@ def test_qgemm_asym_stream_k_sampled():
     sw = qw.astype(np.int64).sum(1).astype(np.int32)
     rows = np.concatenate([np.sort(rng.choice(T, 40, replace=False)), [0, T - 1]])
     ref = oracle.gemm_int8_asym(qa[rows], za[rows], qw, zw)
-    ws = torch.empty(rtq.qgemm_workspace(), dtype=torch.uint8, device="cuda")
+    ws = rtq.new_qgemm_workspace()
     acc = torch.empty((T, N), dtype=torch.int32, device="cuda")
     ones_t, ones_n = to_dev(np.ones(T, np.float32)), to_dev(np.ones(N, np.float32))
     rtq.qgemm_asym(to_dev(qa), ones_t, to_dev(za), to_dev(sa), to_dev(qw), ones_n, to_dev(zw), to_dev(sw), acc, d,
@@ -132,7 +132,7 @@ def test_qgemm_asym_stream_k_equals_whole(yt):
     y0 = torch.empty((T, N), dtype=dt, device="cuda")
     y1 = torch.empty((T, N), dtype=dt, device="cuda")
     rtq.qgemm_asym(*args, y0, d)
-    ws = torch.empty(rtq.qgemm_workspace(), dtype=torch.uint8, device="cuda")
+    ws = rtq.new_qgemm_workspace()
     rtq.qgemm_asym(*args, y1, d, workspace=ws)
     torch.cuda.synchronize()
     iv = torch.int32 if yt == "f32" else torch.int16

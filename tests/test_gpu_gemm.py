@@ -8,6 +8,7 @@ import pytest
 
 import oracle
 import rotation_then_quantize_amd as rtq
+import workloads
 from _helpers import bf16_host, rel_fro, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -112,7 +113,7 @@ def test_int8_full_shape_sampled():
     rows = np.concatenate([rows, [0, T - 1]])
     cols = np.concatenate([cols, [0, N - 1]])
     ref = oracle.gemm_int8(a[rows], w[cols])
-    ws = torch.empty(rtq.qgemm_workspace(), dtype=torch.uint8, device="cuda")
+    ws = rtq.new_qgemm_workspace()
     for workspace in (None, ws):
         acc = torch.empty((T, N), dtype=torch.int32, device="cuda")
         rtq.qgemm(to_dev(a), to_dev(np.ones(T, np.float32)), to_dev(w), to_dev(np.ones(N, np.float32)), acc, d,
@@ -139,17 +140,19 @@ def test_int8_ksplit_accumulators_bit_exact(T, N, d):
     # last rows and columns (N % 8 != 0: per-element stores).
     a = _codes(11 + T, T, d)
     w = _codes(12 + N, N, d)
-    ws = torch.full((rtq.qgemm_workspace(),), 0x5A, dtype=torch.uint8, device="cuda")   # arbitrary contents
+    ws = rtq.new_qgemm_workspace()
+    ws[:-_counter_bytes()] = 0x5A   # partial tiles: any contents; the counters start at zero
     acc = torch.empty((T, N), dtype=torch.int32, device="cuda")
     ones_t, ones_n = to_dev(np.ones(T, np.float32)), to_dev(np.ones(N, np.float32))
     da, dw = to_dev(a), to_dev(w)
     rows = np.arange(T) if T * N <= 1 << 17 else np.sort(np.random.default_rng(3).choice(T, 40, replace=False))
     ref = oracle.gemm_int8(a[rows], w)
-    for _ in range(3):   # the same workspace again: counters cleared before each launch
+    for _ in range(3):   # the same workspace again: each launch leaves its counters at zero
         acc.fill_(0)
         rtq.qgemm(da, ones_t, dw, ones_n, acc, d, workspace=ws)
         torch.cuda.synchronize()
         assert np.array_equal(acc.cpu().numpy()[rows].astype(np.int64), ref)
+        assert not ws[-_counter_bytes():].any()
 
 
 @pytest.mark.parametrize("yt", ["f32", "bf16"])
@@ -167,33 +170,56 @@ def test_ksplit_outputs_equal_unsplit(yt, T, N, d):
     y0 = torch.empty((T, N), dtype=dt, device="cuda")
     y1 = torch.empty((T, N), dtype=dt, device="cuda")
     rtq.qgemm(to_dev(a), a_s, to_dev(w), w_s, y0, d)
-    ws = torch.empty(rtq.qgemm_workspace(), dtype=torch.uint8, device="cuda")
+    ws = rtq.new_qgemm_workspace()
     rtq.qgemm(to_dev(a), a_s, to_dev(w), w_s, y1, d, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(y0.view(torch.int16) if yt == "bf16" else y0.view(torch.int32),
                        y1.view(torch.int16) if yt == "bf16" else y1.view(torch.int32))
 
 
-def test_split_counters_cleared_whatever_the_workspace_held():
-    # The split counters are zeroed by a fill kernel before each split launch, so stale words in
-    # the workspace never count as arrivals: here every counter word starts with small values a
-    # previous launch could have left (1, 2, 4 and their sums are the stream-K publication bits)
-    # and the rest of the workspace holds int32 partial-tile-like data.  Split and unsplit
-    # products must agree bit for bit on two launches in a row.
+def _counter_bytes():
+    # the split region ends with two 8-byte arrival counters per block slot
+    nbytes = rtq.qgemm_workspace()
+    return 16 * (nbytes // (2 * (256 * 256 * 4 + 8)))
+
+
+def test_split_counters_left_zero_and_layer_workspace_any_contents():
+    # rtq_qgemm_ws: a zero-filled workspace stays reusable, since the block that finishes a shared
+    # tile resets its counter; partial tiles may hold anything.  rtq_rotated_qlinear: its workspace
+    # may hold anything at all (the quantiser launch zeroes the product's counters), here int32
+    # partial-tile-like data with the counter words set to publication-like values (1, 2, 4, 5 ...).
     T, N, d = 4608, 4096, 4096                    # 288 tiles: all shared by stream-K runs
     a = to_dev(_codes(31, T, d))
     w = to_dev(_codes(32, N, d))
     ones_t, ones_n = to_dev(np.ones(T, np.float32)), to_dev(np.ones(N, np.float32))
     acc0 = torch.empty((T, N), dtype=torch.int32, device="cuda")
     rtq.qgemm(a, ones_t, w, ones_n, acc0, d)
-    nbytes = rtq.qgemm_workspace()
-    ws = torch.randint(-1000, 1000, (nbytes // 4,), dtype=torch.int32, device="cuda")
-    slots = nbytes // (2 * (256 * 256 * 4 + 8))
-    counters = ws.view(torch.int64)[-2 * slots:]
-    counters.copy_(torch.arange(2 * slots, device="cuda", dtype=torch.int64) % 8)
-    for _ in range(2):
+    ws = rtq.new_qgemm_workspace()
+    ws[:-_counter_bytes()].view(torch.int32).copy_(torch.randint(-1000, 1000, ((ws.numel() - _counter_bytes()) // 4,),
+                                                                 dtype=torch.int32, device="cuda"))
+    for _ in range(3):
         acc1 = torch.full((T, N), -1, dtype=torch.int32, device="cuda")
-        rtq.qgemm(a, ones_t, w, ones_n, acc1, d, workspace=ws.view(torch.uint8))
+        rtq.qgemm(a, ones_t, w, ones_n, acc1, d, workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(acc0, acc1)
-        counters.copy_(torch.full_like(counters, 5))
+        assert not ws[-_counter_bytes():].any()
+    # the layer: any workspace contents
+    R = rtq.Rpbh.from_seed(33, d)
+    xh = to_dev(workloads.f32_to_bf16_bits(workloads.small_case(3301, T, d, "t3")), "bf16")
+    wq = torch.empty((N, d), dtype=torch.int8, device="cuda")
+    wsc = torch.empty(N, dtype=torch.bfloat16, device="cuda")
+    rtq.quantize_rows(to_dev(workloads.f32_to_bf16_bits(workloads.small_case(3302, N, d, "w")), "bf16"), wq, wsc, R,
+                      rtq.RTQ_INT8)
+    need = rtq.rotated_qlinear_workspace(T, d)
+    y0 = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    rtq.rotated_qlinear(xh, R, wq, wsc, y0, workspace=torch.zeros(need, dtype=torch.uint8, device="cuda"))
+    junk = torch.randint(-1000, 1000, ((need + 3) // 4,), dtype=torch.int32, device="cuda")
+    junk_ws = junk.view(torch.uint8)[:need]
+    cw = junk_ws[-_counter_bytes():].view(torch.int64)
+    cw.copy_(torch.arange(cw.numel(), device="cuda", dtype=torch.int64) % 8)
+    for _ in range(2):
+        y1 = torch.full((T, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+        rtq.rotated_qlinear(xh, R, wq, wsc, y1, workspace=junk_ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+        cw.fill_(5)

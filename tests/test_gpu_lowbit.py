@@ -133,7 +133,7 @@ def test_three_bit_weights_with_k_split_bit_exact_integer_part():
     y0 = torch.empty((T, N), dtype=torch.int32, device="cuda")
     y1 = torch.empty((T, N), dtype=torch.int32, device="cuda")
     rtq.qgemm(a, s_a, w, s_w, y0, d, rtq.RTQ_CODEBOOK_I8, cb, cb)
-    ws = torch.empty(rtq.qgemm_workspace(), dtype=torch.uint8, device="cuda")
+    ws = rtq.new_qgemm_workspace()
     rtq.qgemm(a, s_a, w, s_w, y1, d, rtq.RTQ_CODEBOOK_I8, cb, cb, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(y0, y1)
@@ -210,7 +210,7 @@ def test_split_workspace_shared_across_weight_widths():
     # never read as the current launch's.  Each split product must equal the unsplit one.
     T, N, d = 4608, 4096, 4096          # 288 tiles: shared along d by stream-K runs
     rng = np.random.default_rng(17)
-    ws = torch.empty(rtq.qgemm_workspace(), dtype=torch.uint8, device="cuda")
+    ws = rtq.new_qgemm_workspace()
     s_a = to_dev(np.ones(T, np.float32))
     s_w = to_dev(np.ones(N, np.float32))
     cb4 = rtq.Codebook.for_dim(d, 4)

@@ -65,7 +65,7 @@ def test_tiled_product_accumulators_bit_exact(T, N, d, ws):
     rows = np.arange(T) if T * N <= 1 << 18 else np.sort(rng.choice(T, 48, replace=False))
     ref = oracle.gemm_int8(a[rows], w)
     acc = torch.empty((T, N), dtype=torch.int32, device="cuda")
-    work = torch.empty(rtq.qgemm_workspace(), dtype=torch.uint8, device="cuda") if ws else None
+    work = rtq.new_qgemm_workspace() if ws else None
     rtq.qgemm(to_dev(tile_codes(a)), to_dev(np.ones(T, np.float32)), to_dev(tile_codes(w)),
               to_dev(np.ones(N, np.float32)), acc, d, rtq.RTQ_INT8_TILED, workspace=work, n_tokens=T, n_out=N)
     torch.cuda.synchronize()
