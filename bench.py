@@ -234,11 +234,13 @@ def bench_offline(args, torch, rtq, workloads):
 
 
 def bench_codebook(args, torch, rtq, workloads, variant, mode=None):
-    """One online codebook layer (quantise + product).  mode RTQ_CODEBOOK_I8 (default): codes on
-    the INT8 matrix cores (int8 codebook values, 1 byte per activation element); RTQ_CODEBOOK:
-    fp16 LUT product."""
-    mode = rtq.RTQ_CODEBOOK_I8 if mode is None else mode
-    i8 = mode == rtq.RTQ_CODEBOOK_I8
+    """One online codebook layer (quantise + product).  mode RTQ_CODEBOOK_I8_TILED (default): codes
+    on the INT8 matrix cores (int8 codebook values, 1 byte per activation element), both operands
+    in the tiled layouts; RTQ_CODEBOOK_I8: the same with row-major operands; RTQ_CODEBOOK: fp16 LUT
+    product."""
+    mode = rtq.RTQ_CODEBOOK_I8_TILED if mode is None else mode
+    tiled = mode == rtq.RTQ_CODEBOOK_I8_TILED
+    i8 = mode in (rtq.RTQ_CODEBOOK_I8, rtq.RTQ_CODEBOOK_I8_TILED)
     bits_a = 4
     if variant in ("w4a4", "w3a3", "w4a6"):     # the attention-output shape
         d, N = workloads.DIT_HIDDEN, workloads.DIT_HIDDEN
@@ -252,12 +254,14 @@ def bench_codebook(args, torch, rtq, workloads, variant, mode=None):
     R = rtq.Rpbh.from_seed(workloads.RPBH_SEED[d], d)
     cb_a, cb_w = rtq.Codebook.for_dim(d, bits_a), rtq.Codebook.for_dim(d, bits_w)
     w = _bf16_dev(wh, torch)
-    wc = torch.empty((N, d * bits_w // 8), dtype=torch.uint8, device="cuda")
+    wmode = rtq.RTQ_CODEBOOK_TILED if tiled else rtq.RTQ_CODEBOOK
+    wc = torch.empty(rtq.tiled_code_bytes(N, d, wmode, bits_w) or N * d * bits_w // 8, dtype=torch.uint8, device="cuda")
     wn = torch.empty(N, dtype=torch.bfloat16, device="cuda")
-    rtq.quantize_rows(w, wc, wn, R, rtq.RTQ_CODEBOOK, cb_w, 0.0)
+    rtq.quantize_rows(w, wc, wn, R, wmode, cb_w, 0.0)
     del w
     xs = _copies(_bf16_dev(xh, torch), 512 << 20, torch)
-    codes = torch.empty((T, d if i8 else d * bits_a // 8), dtype=torch.int8 if i8 else torch.uint8, device="cuda")
+    codes = torch.empty(rtq.tiled_rows(T) * d if tiled else T * (d if i8 else d * bits_a // 8),
+                        dtype=torch.int8 if i8 else torch.uint8, device="cuda")
     norm = torch.empty(T, dtype=torch.float32, device="cuda")
     y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
 
@@ -267,7 +271,7 @@ def bench_codebook(args, torch, rtq, workloads, variant, mode=None):
     split_ws = rtq.new_qgemm_workspace()
 
     def gemm(i):
-        rtq.qgemm(codes, norm, wc, wn, y, d, mode, cb_a, cb_w, workspace=split_ws)
+        rtq.qgemm(codes, norm, wc, wn, y, d, mode, cb_a, cb_w, workspace=split_ws, n_tokens=T, n_out=N)
 
     _prewarm(lambda i: (quant(i), gemm(i)), torch, 0.25)
     for i in range(args.warmup):
@@ -280,7 +284,9 @@ def bench_codebook(args, torch, rtq, workloads, variant, mode=None):
     q_bytes = T * (2 * d + (d if i8 else d * bits_a // 8) + 4)
     gemm_tflops = flops / (tg.mean() * 1e-3) / 1e12
     peak = PEAK_INT8_TOPS if i8 else PEAK_F16_TFLOPS
-    return {"mode": "codebook on INT8 MFMA (int8 codebook values)" if i8 else "codebook, fp16 LUT on fp16 MFMA",
+    name = ("codebook on INT8 MFMA (int8 codebook values)" + (", tiled operands" if tiled else ", row-major operands")
+            if i8 else "codebook, fp16 LUT on fp16 MFMA")
+    return {"mode": name,
             "T": T, "d": d, "N": N, "bits_w": bits_w, "bits_a": bits_a, "step_ms": wall * 1e3 / steps,
             "quant_ms": quant_burst,
             "quant_event_span_ms": float(tq.mean()),
@@ -564,6 +570,9 @@ def main():
         extra["offline_weight_rotate_quantize"] = bench_offline(args, torch, rtq, workloads)
         extra["w4a4_dit_attn_out_4608x4096x4096"] = bench_codebook(args, torch, rtq, workloads, "w4a4")
         extra["w2a4_dit_mlp_down_4608x16384x4096"] = bench_codebook(args, torch, rtq, workloads, "w2a4")
+        for k, v in (("w4a4_dit_attn_out_4608x4096x4096", "w4a4"), ("w2a4_dit_mlp_down_4608x16384x4096", "w2a4")):
+            rm = bench_codebook(args, torch, rtq, workloads, v, rtq.RTQ_CODEBOOK_I8)
+            extra[k + "_row_major"] = {f: rm[f] for f in ("step_ms", "quant_ms", "gemm_ms", "gemm_frac_peak")}
         extra["w4a4_dit_attn_out_4608x4096x4096_fp16_lut"] = bench_codebook(args, torch, rtq, workloads, "w4a4",
                                                                             rtq.RTQ_CODEBOOK)
         extra["w2a4_dit_mlp_down_4608x16384x4096_fp16_lut"] = bench_codebook(args, torch, rtq, workloads, "w2a4",

@@ -63,7 +63,7 @@ typedef enum {
                          * stay packed codes.  Relative Frobenius error of y against the
                          * exact-centroid product: ~0.9% (W4A4) / ~0.5% (W2A4) on the DiT
                          * synthetic shapes, inside the 2e-2 bound for bf16 outputs.    */
-    RTQ_INT8_TILED = 3 /* RTQ_INT8 codes and scales, with the codes stored in the product's tiled
+    RTQ_INT8_TILED = 3, /* RTQ_INT8 codes and scales, with the codes stored in the product's tiled
                          * layout: rows in tiles of 256 (padded to a multiple of 256; padding rows
                          * are neither written nor read as results), K in slices of 64 bytes;
                          * block (tile, slice) is 16 KB contiguous at
@@ -73,6 +73,21 @@ typedef enum {
                          * LDS stage of the INT8 product, whose operand loads then read whole 1 KB
                          * runs (about 7% faster products at the DiT shapes than row-major codes).
                          * A codes buffer holds ceil(rows / 256) * 256 * d bytes.            */
+    RTQ_CODEBOOK_TILED = 4, /* RTQ_CODEBOOK codes and norms (weights: packed 2-, 3- or 4-bit
+                         * codes), with the codes stored in the tiled code layout: the same tiles
+                         * of 256 rows (padded; padding rows neither written nor read as results)
+                         * and K slices of 64 elements; block (tile, slice) is contiguous at
+                         * ((row / 256) * (d / 64) + j / 64) * 256 * 8 * bits bytes and holds
+                         * [256 rows][8 * bits bytes], a row's bytes being exactly its packed
+                         * codes of elements 64 * (j / 64) .. +64 as in the row-major bit stream.
+                         * It is the image of one raw code slot of the product.  Written by
+                         * rtq_quantize_rows; multiplied in RTQ_CODEBOOK_I8_TILED.  A codes
+                         * buffer holds ceil(rows / 256) * 256 * d * bits / 8 bytes.          */
+    RTQ_CODEBOOK_I8_TILED = 5 /* RTQ_CODEBOOK_I8 with both operands tiled: activations' int8
+                         * codebook values in RTQ_INT8_TILED's layout (rtq_quantize_rows in this
+                         * mode; ceil(rows / 256) * 256 * d bytes), weight codes in
+                         * RTQ_CODEBOOK_TILED's.  Products equal RTQ_CODEBOOK_I8's bit for bit
+                         * and are 7-10% faster at the DiT shapes.                           */
 } rtq_qmode;
 
 /* RPBH descriptor (OrbitQuant article, section 2.3).  perm (int32[d]) and signs (int8[d], +-1)
@@ -126,6 +141,8 @@ rtq_status rtq_rpbh_rotate(const void* x, rtq_dtype xt, void* y, rtq_dtype yt, i
  *              divides: q_j = round-half-even(x'_j / s), clamped to [-127, 127]; s == 0 gives q = 0.
  *              codes: int8[rows][d].  cb must be NULL.  eps is ignored.
  *   INT8_TILED: the same codes and scales, codes written in the tiled layout (RTQ_INT8_TILED).
+ *   CODEBOOK_TILED, CODEBOOK_I8_TILED: the CODEBOOK / CODEBOOK_I8 codes and norms below, codes
+ *              written in the tiled layouts (see the modes); the same kernels and bits.
  *   CODEBOOK:  s = ||x'||_2 (summed in double, rounded to fp32); u_j = x'_j / (s + eps) in fp32
  *              (0 when s + eps == 0); code_j = #{k : boundaries[k] < u_j}.  The norm s is stored as
  *              scale_t: BF16 for weights (eps = 0), F32 for activations (eps > 0, e.g. 1e-8).
@@ -161,6 +178,9 @@ rtq_status rtq_quantize_rows(const void* x, rtq_dtype xt, int64_t rows, int32_t 
  *              exactly in int32, y = acc * a_scale[t] * w_scale[n] / (S_a S_w) in fp32; yt BF16,
  *              or RTQ_I32 for acc itself.  cb_a (centroids, bits 2, 3, 4 or 6) gives S_a; cb_w
  *              (centroids, bits 2, 3 or 4) the weight values.  N <= 2^22 (BF16), 2^21 (I32).
+ *   CODEBOOK_I8_TILED: CODEBOOK_I8 with a_codes in RTQ_INT8_TILED's layout and w_codes in
+ *              RTQ_CODEBOOK_TILED's (each buffer padded to a multiple of 256 rows); same results.
+ *   CODEBOOK_TILED is a weight-code layout only: rtq_qgemm returns RTQ_ERR_UNSUPPORTED for it.
  *   The codebook modes give bf16 output (yt == RTQ_F32 returns RTQ_ERR_UNSUPPORTED): their
  *   centroid rounding (fp16 copies, or int8 values) is sized for the bf16 output bound, not for
  *   an fp32 one.
@@ -169,7 +189,8 @@ rtq_status rtq_qgemm(const void* a_codes, const float* a_scale, int64_t T, const
                      const void* w_scale, rtq_dtype w_scale_t, int64_t N, int32_t d, rtq_qmode mode,
                      const rtq_codebook* cb_a, const rtq_codebook* cb_w, void* y, rtq_dtype yt, void* stream);
 
-/* rtq_qgemm with a workspace for the INT8-core modes (RTQ_INT8, RTQ_CODEBOOK_I8): a partial last
+/* rtq_qgemm with a workspace for the INT8-core modes (RTQ_INT8, RTQ_CODEBOOK_I8 and their tiled
+ * forms): a partial last
  * round of 256 x 256 output tiles is shared along d, so no compute unit idles behind it.  After
  * at least one full round, the last full round and the remainder are dealt out as equal runs of
  * K stages that cross tile edges (stream-K); with fewer tiles than compute units, each tile is
@@ -195,7 +216,8 @@ size_t rtq_qgemm_workspace(void);
 /* The online layer: rtq_quantize_rows(x, R, mode, cb_a, eps = 1e-8 (CODEBOOK) ...) into `workspace`
  * followed by rtq_qgemm on the same stream (OrbitQuant article, section 2.2, steps 1-5 and the
  * cancellation).  Weights come from rtq_quantize_rows with the SAME descriptor R (RTQ_INT8_TILED:
- * weight codes written in that mode, and the activation codes go to the workspace tiled too).
+ * weight codes written in that mode, and the activation codes go to the workspace tiled too;
+ * RTQ_CODEBOOK_I8_TILED: weight codes written in RTQ_CODEBOOK_TILED, activation values tiled).
  *   workspace: device memory of at least rtq_rotated_qlinear_workspace(T, R->d, mode, bits_a) bytes,
  *   16-byte aligned, any contents (the quantiser launch zeroes the product's split counters); on
  *   return it starts with the activation codes and scales.  Calls sharing a workspace must not
@@ -206,7 +228,8 @@ rtq_status rtq_rotated_qlinear(const void* x, rtq_dtype xt, int64_t T, const rtq
                                void* workspace, size_t ws_bytes, void* stream);
 
 /* Bytes of workspace rtq_rotated_qlinear uses: the codes and fp32 scales (each 256-byte aligned;
- * the codes take T*d bytes for RTQ_INT8 and RTQ_CODEBOOK_I8, ceil(T/256)*256*d for RTQ_INT8_TILED,
+ * the codes take T*d bytes for RTQ_INT8 and RTQ_CODEBOOK_I8, ceil(T/256)*256*d for RTQ_INT8_TILED
+ * and RTQ_CODEBOOK_I8_TILED,
  * T*d*bits_a/8 for RTQ_CODEBOOK), then,
  * for the INT8-core modes, rtq_qgemm_workspace() bytes for the product's K-split.  A workspace
  * that holds only the codes and scales is accepted (the product then runs without the split).

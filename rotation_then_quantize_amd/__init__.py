@@ -21,12 +21,23 @@ LIB_PATH = os.path.join(_PKG, "librtq.so")
 RTQ_OK, RTQ_ERR_INVALID_ARG, RTQ_ERR_UNSUPPORTED, RTQ_ERR_MISALIGNED, RTQ_ERR_HIP = 0, -1, -2, -3, -4
 RTQ_F32, RTQ_BF16, RTQ_I32 = 0, 1, 2
 RTQ_INT8, RTQ_CODEBOOK, RTQ_CODEBOOK_I8, RTQ_INT8_TILED = 0, 1, 2, 3
-TILE_ROWS, TILE_K = 256, 64   # the tiled INT8 layout: 256-row tiles, 64-byte K slices
+RTQ_CODEBOOK_TILED, RTQ_CODEBOOK_I8_TILED = 4, 5
+TILE_ROWS, TILE_K = 256, 64   # the tiled layouts: 256-row tiles, K slices of 64 elements
+_CODEBOOK_MODES = (RTQ_CODEBOOK, RTQ_CODEBOOK_I8, RTQ_CODEBOOK_TILED, RTQ_CODEBOOK_I8_TILED)
 
 
 def tiled_rows(rows: int) -> int:
-    """Rows a codes buffer in the tiled INT8 layout holds (rows padded to a multiple of 256)."""
+    """Rows a codes buffer in a tiled layout holds (rows padded to a multiple of 256)."""
     return -(-rows // TILE_ROWS) * TILE_ROWS
+
+
+def tiled_code_bytes(rows: int, d: int, mode: int, bits: int = 8) -> int:
+    """Bytes of a codes buffer in the tiled layout of `mode` (0 for the row-major modes)."""
+    if mode in (RTQ_INT8_TILED, RTQ_CODEBOOK_I8_TILED):
+        return tiled_rows(rows) * d
+    if mode == RTQ_CODEBOOK_TILED:
+        return tiled_rows(rows) * d * bits // 8
+    return 0
 
 EXPORTS = ("rtq_rpbh_make", "rtq_lloyd_max", "rtq_rpbh_rotate", "rtq_quantize_rows", "rtq_qgemm",
            "rtq_qgemm_ws", "rtq_qgemm_workspace", "rtq_rotated_qlinear", "rtq_rotated_qlinear_workspace",
@@ -227,8 +238,9 @@ def quantize_rows(x, codes, scale, R: Rpbh | None = None, mode: int = RTQ_INT8, 
                   eps: float = 0.0, stream=None):
     """Rotate (if R) and quantise each row of x into codes + per-row scale/norm."""
     rows, d = x.shape
-    if mode == RTQ_INT8_TILED and codes.numel() * codes.element_size() < tiled_rows(rows) * d:
-        raise ValueError(f"tiled codes need {tiled_rows(rows) * d} bytes (rows padded to a multiple of 256)")
+    need = tiled_code_bytes(rows, d, mode, cb.bits if cb is not None else 8)
+    if codes.numel() * codes.element_size() < need:
+        raise ValueError(f"tiled codes need {need} bytes (rows padded to a multiple of 256)")
     _check(load_library().rtq_quantize_rows(_ptr(x), _dtype_code(x), rows, d, None if R is None else R.c, mode,
                                             _cb(cb), ctypes.c_float(eps), _ptr(codes), _ptr(scale),
                                             _dtype_code(scale), _stream(stream)))
@@ -276,7 +288,7 @@ def rotated_qlinear(x, R: Rpbh, w_codes, w_scale, y, mode: int = RTQ_INT8, cb_a:
     """The online layer: rotate + quantise x, then the quantised product, on one stream."""
     torch = _torch()
     T = x.shape[0]
-    bits_a = cb_a.bits if (mode in (RTQ_CODEBOOK, RTQ_CODEBOOK_I8) and cb_a is not None) else 8
+    bits_a = cb_a.bits if (mode in _CODEBOOK_MODES and cb_a is not None) else 8
     N = y.shape[1]
     need = rotated_qlinear_workspace(T, R.d, mode, bits_a)
     if workspace is None:

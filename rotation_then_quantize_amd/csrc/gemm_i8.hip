@@ -25,6 +25,8 @@
 // at slot c ^ ((r >> 2) & 3).  A fragment read (16 lanes = 16 consecutive rows, one chunk, per LDS
 // cycle) then touches 16 distinct 16-byte bank groups, and every load instruction writes a
 // contiguous 1 KB (16 rows), with the permutation applied to which global chunk each lane fetches.
+// Operands in the tiled layouts are stored as these stage blocks (int8 operands) or as the raw code
+// slots below (packed weight codes), so each load instruction also reads contiguous bytes.
 //
 // Schedule.  One workgroup per CU runs persistently over tiles.  The tiles are split into 8
 // contiguous ranges, one per XCD (block b runs on XCD b % 8, and each XCD has its own L2); the
@@ -37,6 +39,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "codebook_int8.h"
 #include "rtq_internal.h"
@@ -377,19 +380,22 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
     // Packed weight codes of stage st -> raw slot st % kRawSlots, laid out [row][BK * bits / 8].
     // 4-bit: one 16-byte load per thread (thread t: row t / 2, half t % 2 of the row's 32 bytes);
     // 2-bit: two 4-byte loads per thread (load q, thread t: bytes q * 2048 + 4t of the slot);
-    // 3-bit: three such loads (rows of 24 bytes).
+    // 3-bit: three such loads (rows of 24 bytes).  kTiled: the codes are stored as these slots (the
+    // tiled code layout), so every load instruction reads one contiguous run (1 KB, or 256 bytes).
     const uint32_t raw_base = lds_base + static_cast<uint32_t>(kLds);
     auto issue_codes = [&](int st) {
         const uint32_t slot = raw_base + static_cast<uint32_t>((st % kRawSlots) * kRawStage);
         const int wrow = d * kWBits / 8;
         if constexpr (kWBits == 4) {
-            const uint32_t off = static_cast<uint32_t>((tid >> 1) * wrow + (kbeg + st) * 32 + (tid & 1) * 16);
+            const uint32_t off = kTiled ? static_cast<uint32_t>((kbeg + st) * (BN * 32) + 16 * tid)
+                                        : static_cast<uint32_t>((tid >> 1) * wrow + (kbeg + st) * 32 + (tid & 1) * 16);
             load_to_lds(rsw, off, slot + wave_lds);
         } else if constexpr (kWBits == 2) {
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 const int b = q * 2048 + 4 * tid;                 // byte within the slot
-                const uint32_t off = static_cast<uint32_t>((b >> 4) * wrow + (kbeg + st) * 16 + (b & 15));
+                const uint32_t off = kTiled ? static_cast<uint32_t>((kbeg + st) * (BN * 16) + b)
+                                            : static_cast<uint32_t>((b >> 4) * wrow + (kbeg + st) * 16 + (b & 15));
                 load_to_lds4(rsw, off, slot + q * 2048 + static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave * 256)));
             }
         } else if constexpr (kWBits == 3) {
@@ -397,7 +403,8 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
             for (int q = 0; q < 3; ++q) {
                 const int b = q * 2048 + 4 * tid;                 // byte within the slot
                 const int row = b / 24;
-                const uint32_t off = static_cast<uint32_t>(row * wrow + (kbeg + st) * 24 + (b - 24 * row));
+                const uint32_t off = kTiled ? static_cast<uint32_t>((kbeg + st) * (BN * 24) + b)
+                                            : static_cast<uint32_t>(row * wrow + (kbeg + st) * 24 + (b - 24 * row));
                 load_to_lds4(rsw, off, slot + q * 2048 + static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave * 256)));
             }
         }
@@ -560,18 +567,23 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
             for (int j = 0; j < TN; ++j) acc[i][j] = v16i{};
         read_frags(fa0, fb0, 0, frag_off0);
 
-        for (int s = 0; s < nk; ++s) {
+        // One K stage.  kSteady (s + 4 < nk): every load and decode below is issued, so the stage is
+        // one basic block and the compiler can place the decode's VALU work among the MFMAs (with
+        // the checks, each conditional load or decode was a block of its own between two MFMA
+        // groups); the last four stages take the checked form.
+        auto kstep = [&](int s, auto steady_tag) {
+            constexpr bool kSteady = decltype(steady_tag)::value;
             // stage s + 1 (and codes s + 2) must have landed; what iteration s - 1 issued (stage
             // s + 2, codes s + 3) may still be in flight
             if constexpr (kCoded) {
-                if (s + 3 < nk)
+                if (kSteady || s + 3 < nk)
                     wait_vmcnt<kLoadsPerStage + kCodeLoads>();
                 else if (s + 2 < nk)
                     wait_vmcnt<kLoadsPerStage>();
                 else
                     wait_vmcnt<0>();
             } else {
-                if (s + 2 < nk)
+                if (kSteady || s + 2 < nk)
                     wait_vmcnt<kLoadsPerStage>();
                 else
                     wait_vmcnt<0>();
@@ -579,15 +591,15 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
             RTQ_BARRIER();   // every wave's part of stage s + 1 is in LDS; stage s - 1 is consumed
             RawCodes rc{{0u, 0u, 0u, 0u}};
             if (kCoded) {
-                if (s + 4 < nk) issue_codes(s + 4);   // raw slot of codes s + 1, decoded last iteration
-                if (s + 2 < nk) rc = read_raw(s + 2);
+                if (kSteady || s + 4 < nk) issue_codes(s + 4);   // raw slot of codes s + 1, decoded last iteration
+                if (kSteady || s + 2 < nk) rc = read_raw(s + 2);
             }
             read_frags(fa1, fb1, s, frag_off1);
             mfmas(fa0, fb0);
-            if (kCoded && s + 2 < nk) decode_write(s + 2, rc);   // visible after the next barrier
+            if (kCoded && (kSteady || s + 2 < nk)) decode_write(s + 2, rc);   // visible after the next barrier
             // stage s + 3 into stage s - 1's slot, issued behind the first K step's MFMAs (measured
             // 2% faster than right after the barrier)
-            if (s + 3 < nk) issue_stage(s + 3);
+            if (kSteady || s + 3 < nk) issue_stage(s + 3);
             // (on the last stage this reads an unused slot: unconditional, so the compiler's LDS wait
             // before the next MFMAs does not also cover these reads)
             read_frags(fa0, fb0, s + 1, frag_off0);
@@ -603,7 +615,10 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
                 }
                 __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - (TM + TN), 0);
             }
-        }
+        };
+        int s = 0;
+        for (; s + 4 < nk; ++s) kstep(s, std::true_type{});
+        for (; s < nk; ++s) kstep(s, std::false_type{});
         RTQ_BARRIER();   // every wave is done reading the ring
 
         const int64_t cm0 = m0, cn0 = n0;
@@ -843,7 +858,7 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
 
 template <int kWavesN, int kWBits, bool kAsym, bool kTiled = false>
 hipError_t launch_config(const GemmI8Args& g, hipStream_t stream) {
-    static_assert(!kTiled || (kWBits == 8 && !kAsym), "the tiled layout holds int8 codes");
+    static_assert(!kTiled || !kAsym, "the tiled layouts hold symmetric codes");
     using KernelFn = void (*)(const int8_t*, const float*, const int8_t*, const void*, int64_t, int64_t, int,
                               void*, int, int, const float*, int, const float*, SplitArgs, AsymArgs);
     constexpr int kYKinds = 3;   // fp32, bf16, raw int32 accumulators
@@ -961,18 +976,22 @@ hipError_t launch_gemm_i8(const GemmI8Args& g, hipStream_t stream) {
     if (asym != (g.a_sum != nullptr) || asym != (g.w_zero != nullptr) || asym != (g.w_sum != nullptr))
         return hipErrorInvalidValue;
     if (asym) return g.w_bits == 8 && !g.tiled ? launch_config<kDefaultWavesN, 8, true>(g, stream) : hipErrorInvalidValue;
-    if (g.tiled) return g.w_bits == 8 ? launch_config<kDefaultWavesN, 8, false, true>(g, stream) : hipErrorInvalidValue;
+    const bool coded = g.w_bits != 8;
+    if (coded && (g.cent_a == nullptr || g.cent_w == nullptr || g.a_bits < 1 || g.a_bits > 6)) return hipErrorInvalidValue;
+    if (g.tiled) {
+        switch (g.w_bits) {
+            case 8: return launch_config<kDefaultWavesN, 8, false, true>(g, stream);
+            case 4: return launch_config<kDefaultWavesN, 4, false, true>(g, stream);
+            case 3: return launch_config<kDefaultWavesN, 3, false, true>(g, stream);
+            case 2: return launch_config<kDefaultWavesN, 2, false, true>(g, stream);
+        }
+        return hipErrorInvalidValue;
+    }
     switch (g.w_bits) {
         case 8: return launch_config<kDefaultWavesN, 8, false>(g, stream);
-        case 4:
-            if (g.cent_a == nullptr || g.cent_w == nullptr || g.a_bits < 1 || g.a_bits > 6) return hipErrorInvalidValue;
-            return launch_config<kDefaultWavesN, 4, false>(g, stream);
-        case 3:
-            if (g.cent_a == nullptr || g.cent_w == nullptr || g.a_bits < 1 || g.a_bits > 6) return hipErrorInvalidValue;
-            return launch_config<kDefaultWavesN, 3, false>(g, stream);
-        case 2:
-            if (g.cent_a == nullptr || g.cent_w == nullptr || g.a_bits < 1 || g.a_bits > 6) return hipErrorInvalidValue;
-            return launch_config<kDefaultWavesN, 2, false>(g, stream);
+        case 4: return launch_config<kDefaultWavesN, 4, false>(g, stream);
+        case 3: return launch_config<kDefaultWavesN, 3, false>(g, stream);
+        case 2: return launch_config<kDefaultWavesN, 2, false>(g, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -593,12 +593,22 @@ template <int kOut>
 __device__ __forceinline__ void store_block(const BlockOut& res, void* __restrict__ out, void* __restrict__ scale_out,
                                             int scale_bf16, RowExtra ex, int64_t row, int blk, int d) {
     constexpr int kWords = kH * out_bits<kOut>() / 32;
-    if (kOut == kRowInt8 && ex.tiled) {   // the product's tiled layout: a 64-byte slot, chunks swizzled
-        int8_t* o = static_cast<int8_t*>(out) + tiled_slot_offset(row, blk, d);
+    if (ex.tiled) {
+        if constexpr (out_bits<kOut>() == 8) {   // int8 codes or values: a 64-byte slot, chunks swizzled
+            int8_t* o = static_cast<int8_t*>(out) + tiled_slot_offset(row, blk, d);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            *reinterpret_cast<uint4*>(o + 16 * tiled_chunk(row, q)) =
-                make_uint4(res.w[4 * q], res.w[4 * q + 1], res.w[4 * q + 2], res.w[4 * q + 3]);
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<uint4*>(o + 16 * tiled_chunk(row, q)) =
+                    make_uint4(res.w[4 * q], res.w[4 * q + 1], res.w[4 * q + 2], res.w[4 * q + 3]);
+        } else if constexpr (kWords % 4 == 0) {   // packed codes: the block's 8 * bits bytes, contiguous
+            uint4* o = reinterpret_cast<uint4*>(static_cast<uint8_t*>(out) + tiled_code_offset(row, blk, d, out_bits<kOut>()));
+#pragma unroll
+            for (int q = 0; q < kWords / 4; ++q) o[q] = make_uint4(res.w[4 * q], res.w[4 * q + 1], res.w[4 * q + 2], res.w[4 * q + 3]);
+        } else {
+            uint2* o = reinterpret_cast<uint2*>(static_cast<uint8_t*>(out) + tiled_code_offset(row, blk, d, out_bits<kOut>()));
+#pragma unroll
+            for (int q = 0; q < kWords / 2; ++q) o[q] = make_uint2(res.w[2 * q], res.w[2 * q + 1]);
+        }
     } else if constexpr (kWords % 4 == 0) {
         uint4* o = reinterpret_cast<uint4*>(static_cast<uint8_t*>(out) + (row * d + blk * kH) * out_bits<kOut>() / 8);
 #pragma unroll

@@ -315,7 +315,19 @@ rpbh_rows_kernel(const void* __restrict__ xin, int64_t rows, int d, int log2d, i
 #pragma unroll
                 for (int q = 0; q < kH / kPerWord; ++q) w[q] = k4 ? lut16_x4(lut, w[q]) : lut4_x4(lut, w[q]);
             }
-            if (valid) {
+            if (valid && tiled) {
+                if (kLut) {   // int8 values in the INT8 tiled layout
+                    int8_t* o = static_cast<int8_t*>(out) + tiled_slot_offset(row, blk, d);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        *reinterpret_cast<uint4*>(o + 16 * tiled_chunk(row, q)) =
+                            make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+                } else {      // packed codes in the tiled code layout
+                    uint4* o = reinterpret_cast<uint4*>(static_cast<uint8_t*>(out) + tiled_code_offset(row, blk, d, kBits));
+                    o[0] = make_uint4(w[0], w[1], w[2], w[3]);
+                    if (kBits == 4) o[1] = make_uint4(w[4], w[5], w[6], w[7]);
+                }
+            } else if (valid) {
                 uint32_t* o = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(out) + (row * d + blk * kH) * kSlot / 8);
                 if (kLut) {
 #pragma unroll
@@ -327,12 +339,12 @@ rpbh_rows_kernel(const void* __restrict__ xin, int64_t rows, int d, int log2d, i
                 } else {
                     reinterpret_cast<uint4*>(o)[0] = make_uint4(w[0], w[1], w[2], w[3]);
                 }
-                if (blk == 0) {
-                    if (scale_bf16)
-                        static_cast<uint16_t*>(scale_out)[row] = static_cast<uint16_t>(f32_to_bf16(s));
-                    else
-                        static_cast<float*>(scale_out)[row] = s;
-                }
+            }
+            if (valid && blk == 0) {
+                if (scale_bf16)
+                    static_cast<uint16_t*>(scale_out)[row] = static_cast<uint16_t>(f32_to_bf16(s));
+                else
+                    static_cast<float*>(scale_out)[row] = s;
             }
         }
     }

@@ -116,13 +116,14 @@ rtq_status plan_quantize(const void* x, rtq_dtype xt, int64_t rows, int32_t d, c
         a.out_kind = rtq::kRowInt8;
         a.bounds = nullptr;
         a.tiled = mode == RTQ_INT8_TILED;
-    } else if (mode == RTQ_CODEBOOK) {
+    } else if (mode == RTQ_CODEBOOK || mode == RTQ_CODEBOOK_TILED) {
         RTQ_TRY(check_codebook(cb, "cb", false, true));
         if (!(eps >= 0.0f) || std::isinf(eps)) return fail(RTQ_ERR_INVALID_ARG, "eps must be finite and >= 0");
         if (cb->bits == 6) return fail(RTQ_ERR_UNSUPPORTED, "packed 6-bit codes are not supported (use RTQ_CODEBOOK_I8)");
         a.out_kind = cb->bits == 4 ? rtq::kRowCode4 : (cb->bits == 3 ? rtq::kRowCode3 : rtq::kRowCode2);
         a.bounds = cb->boundaries;
-    } else if (mode == RTQ_CODEBOOK_I8) {
+        a.tiled = mode == RTQ_CODEBOOK_TILED;
+    } else if (mode == RTQ_CODEBOOK_I8 || mode == RTQ_CODEBOOK_I8_TILED) {
         RTQ_TRY(check_codebook(cb, "cb", true, true));
         if (!(eps >= 0.0f) || std::isinf(eps)) return fail(RTQ_ERR_INVALID_ARG, "eps must be finite and >= 0");
         a.out_kind = cb->bits == 4 ? rtq::kRowLut4
@@ -131,6 +132,7 @@ rtq_status plan_quantize(const void* x, rtq_dtype xt, int64_t rows, int32_t d, c
                                      : rtq::kRowLut2;
         a.bounds = cb->boundaries;
         a.centroids = cb->centroids;
+        a.tiled = mode == RTQ_CODEBOOK_I8_TILED;
     } else {
         return fail(RTQ_ERR_INVALID_ARG, "unknown mode %d", static_cast<int>(mode));
     }
@@ -188,7 +190,9 @@ rtq_status plan_gemm(const void* a_codes, const float* a_scale, int64_t T, const
         p.cb = rtq::GemmLutArgs{static_cast<const uint8_t*>(a_codes), a_scale, static_cast<const uint8_t*>(w_codes),
                                 w_scale, w_scale_t == RTQ_BF16, cb_a->centroids, cb_w->centroids, cb_a->bits,
                                 cb_w->bits, T, N, d, y, yt == RTQ_F32 ? 0 : 1};
-    } else if (mode == RTQ_CODEBOOK_I8) {
+    } else if (mode == RTQ_CODEBOOK_TILED) {
+        return fail(RTQ_ERR_UNSUPPORTED, "RTQ_CODEBOOK_TILED is a weight-code layout: multiply in RTQ_CODEBOOK_I8_TILED");
+    } else if (mode == RTQ_CODEBOOK_I8 || mode == RTQ_CODEBOOK_I8_TILED) {
         RTQ_TRY(check_codebook(cb_a, "cb_a", true, false));
         RTQ_TRY(check_codebook(cb_w, "cb_w", true, false));
         if (cb_w->bits == 6) return fail(RTQ_ERR_UNSUPPORTED, "weight codes must be 2-, 3- or 4-bit (got 6)");
@@ -206,6 +210,7 @@ rtq_status plan_gemm(const void* a_codes, const float* a_scale, int64_t T, const
         p.i8.cent_a = cb_a->centroids;
         p.i8.a_bits = cb_a->bits;
         p.i8.cent_w = cb_w->centroids;
+        p.i8.tiled = mode == RTQ_CODEBOOK_I8_TILED;
     } else {
         return fail(RTQ_ERR_INVALID_ARG, "unknown mode %d", static_cast<int>(mode));
     }
@@ -220,7 +225,7 @@ size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 size_t workspace_bytes(int64_t T, int32_t d, rtq_qmode mode, int32_t bits_a, bool with_split = true) {
     if (T < 0 || d <= 0) return 0;
     size_t code_bytes;
-    if (mode == RTQ_INT8_TILED)
+    if (mode == RTQ_INT8_TILED || (mode == RTQ_CODEBOOK_I8_TILED && (bits_a == 2 || bits_a == 3 || bits_a == 4 || bits_a == 6)))
         code_bytes = static_cast<size_t>(rtq::tiled_rows(T)) * static_cast<size_t>(d);
     else if (mode == RTQ_INT8 || (mode == RTQ_CODEBOOK_I8 && (bits_a == 2 || bits_a == 3 || bits_a == 4 || bits_a == 6)))
         code_bytes = static_cast<size_t>(T) * static_cast<size_t>(d);
@@ -261,7 +266,7 @@ size_t asym_workspace_bytes(int64_t T, int32_t d, bool with_split) {
 rtq_status qlinear_need(const rtq_rpbh* R, int64_t T, rtq_qmode mode, const rtq_codebook* cb_a, size_t* need) {
     if (R == nullptr) return fail(RTQ_ERR_INVALID_ARG, "rpbh descriptor is NULL");
     RTQ_TRY(check_d(R->d));
-    const bool cbook = mode == RTQ_CODEBOOK || mode == RTQ_CODEBOOK_I8;
+    const bool cbook = mode == RTQ_CODEBOOK || mode == RTQ_CODEBOOK_I8 || mode == RTQ_CODEBOOK_I8_TILED;
     if (cbook && cb_a == nullptr) return fail(RTQ_ERR_INVALID_ARG, "cb_a is NULL");
     const int32_t bits_a = cbook ? cb_a->bits : 8;
     if (mode == RTQ_CODEBOOK && bits_a != 4)
@@ -280,7 +285,7 @@ rtq_status rotated_qlinear_ws(const void* x, rtq_dtype xt, int64_t T, const rtq_
     RTQ_TRY(qlinear_need(R, T, mode, cb_a, &need));
     const int32_t d = R->d;
     if (yt == RTQ_I32) return fail(RTQ_ERR_UNSUPPORTED, "rtq_rotated_qlinear produces F32 or BF16 output");
-    const bool cbook = mode == RTQ_CODEBOOK || mode == RTQ_CODEBOOK_I8;
+    const bool cbook = mode == RTQ_CODEBOOK || mode == RTQ_CODEBOOK_I8 || mode == RTQ_CODEBOOK_I8_TILED;
     const int32_t bits_a = cbook ? cb_a->bits : 8;
     // (need covers the codes and scales; a larger workspace also carries the product's K-split)
     if (workspace == nullptr) return fail(RTQ_ERR_INVALID_ARG, "workspace is NULL");
@@ -288,9 +293,10 @@ rtq_status rotated_qlinear_ws(const void* x, rtq_dtype xt, int64_t T, const rtq_
     if (ws_bytes < need) return fail(RTQ_ERR_INVALID_ARG, "workspace too small: %zu < %zu bytes", ws_bytes, need);
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     const int64_t rows = T < 0 ? 0 : T;
-    const size_t code_bytes = mode == RTQ_CODEBOOK     ? static_cast<size_t>(rows) * d * bits_a / 8
-                              : mode == RTQ_INT8_TILED ? static_cast<size_t>(rtq::tiled_rows(rows)) * d
-                                                       : static_cast<size_t>(rows) * d;
+    const bool tiled = mode == RTQ_INT8_TILED || mode == RTQ_CODEBOOK_I8_TILED;
+    const size_t code_bytes = mode == RTQ_CODEBOOK ? static_cast<size_t>(rows) * d * bits_a / 8
+                              : tiled              ? static_cast<size_t>(rtq::tiled_rows(rows)) * d
+                                                   : static_cast<size_t>(rows) * d;
     void* a_codes = ws;
     float* a_scale = reinterpret_cast<float*>(ws + align256(code_bytes));
     rtq::RowArgs qa{};

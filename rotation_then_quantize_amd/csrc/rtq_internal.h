@@ -36,6 +36,13 @@ __host__ __device__ inline int64_t tiled_slot_offset(int64_t row, int blk, int d
 }
 // Position (in 16-byte chunks) of chunk c of a row inside its 64-byte slot.
 __host__ __device__ inline int tiled_chunk(int64_t row, int c) { return c ^ static_cast<int>((row >> 2) & 3); }
+// The tiled layout of packed codebook codes (RTQ_CODEBOOK_TILED): the same tiles of 256 rows and K
+// slices of 64 elements; block (tile, slice) is [256 rows][8 * bits bytes], contiguous, and a row's
+// 8 * bits bytes are its packed codes of elements 64 * slice .. +64, as in the row-major bit stream.
+// It is the image of one raw code slot of the product.  Byte offset of row `row`, slice `blk`:
+__host__ __device__ inline int64_t tiled_code_offset(int64_t row, int blk, int d, int bits) {
+    return (((row / kTileRows) * (d / kTileK) + blk) * kTileRows + (row % kTileRows)) * (8 * bits);
+}
 
 struct RowArgs {
     const void* x;          // [rows][d] fp32 or bf16
@@ -53,7 +60,7 @@ struct RowArgs {
     const float* centroids = nullptr;   // codebook centroids (device), 2^bits entries (kRowLut*)
     int32_t* zero = nullptr;            // kRowInt8Asym: per-row zero point
     int32_t* sum = nullptr;             // kRowInt8Asym: per-row sum of the codes
-    bool tiled = false;                 // kRowInt8: codes in the tiled layout (see above)
+    bool tiled = false;                 // codes in a tiled layout (int8 values: the INT8 one; packed: the code one)
     // words zeroed by the launch (the K-split counters of the product that follows on the stream)
     unsigned long long* clear = nullptr;
     int nclear = 0;
@@ -85,7 +92,7 @@ struct GemmI8Args {
     int d;
     void* y;                // [T][N]
     int y_kind;             // 0 fp32, 1 bf16, 2 raw int32
-    bool tiled = false;     // int8 weights and codes: both operands in the tiled layout
+    bool tiled = false;     // both operands tiled: A (int8) in the INT8 layout, W in the INT8 or packed-code one
     // codebook operands on the INT8 matrix cores (w_bits 4 or 2): both codebooks are rounded to
     // int8 as v_k = rint(c_k * S), S = 127 / max_k |c_k|; the product is rescaled by 1/(S_a S_w)
     int w_bits = 8;

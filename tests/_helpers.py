@@ -109,3 +109,28 @@ def untile_codes(buf, rows, d):
     for c in range(4):
         full[:, :, :, c, :] = v[:, :, r, perm[:, c], :].transpose(0, 2, 1, 3)
     return full.reshape(rp, d)[:rows]
+
+
+def tile_packed(codes, bits):
+    """Row-major packed codebook codes [rows][d * bits / 8] (uint8) -> the tiled code layout of
+    RTQ_CODEBOOK_TILED (a flat uint8 array of ceil(rows/256)*256*d*bits/8 bytes; padding rows are
+    zero): block (row // 256, j // 64) holds [256 rows][8 * bits bytes], a row's bytes being its
+    packed codes of elements 64 * (j // 64) .. +64 unchanged."""
+    codes = np.asarray(codes, np.uint8)
+    rows, wrow = codes.shape
+    rb = 8 * bits
+    assert wrow % rb == 0
+    rp = -(-rows // 256) * 256
+    full = np.zeros((rp, wrow), np.uint8)
+    full[:rows] = codes
+    # [tile][256][slice][rb] -> [tile][slice][256][rb]
+    return full.reshape(rp // 256, 256, wrow // rb, rb).transpose(0, 2, 1, 3).reshape(-1).copy()
+
+
+def untile_packed(buf, rows, d, bits):
+    """Inverse of tile_packed: the first `rows` rows as row-major [rows][d * bits / 8] uint8."""
+    buf = np.asarray(buf).view(np.uint8).reshape(-1)
+    rb = 8 * bits
+    rp = -(-rows // 256) * 256
+    v = buf[:rp * d * bits // 8].reshape(rp // 256, d // 64, 256, rb)
+    return v.transpose(0, 2, 1, 3).reshape(rp, d * bits // 8)[:rows]

@@ -10,6 +10,7 @@ import pytest
 
 import oracle
 import rotation_then_quantize_amd as rtq
+from _helpers import tile_codes, tile_packed, untile_codes, untile_packed
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "rtq.h")
@@ -116,6 +117,14 @@ def test_quantize_rows_validation():
     assert call(mode=rtq.RTQ_CODEBOOK_I8, cb=ctypes.byref(_C(6, A, A)), R=None) == rtq.RTQ_ERR_UNSUPPORTED
     assert call(mode=rtq.RTQ_CODEBOOK, cb=ctypes.byref(cb), eps=-1.0) == rtq.RTQ_ERR_INVALID_ARG
     assert call(mode=7) == rtq.RTQ_ERR_INVALID_ARG
+    # tiled codebook layouts: the same checks as their row-major modes
+    assert call(mode=rtq.RTQ_CODEBOOK_TILED) == rtq.RTQ_ERR_INVALID_ARG        # codebook missing
+    assert call(mode=rtq.RTQ_CODEBOOK_TILED, cb=ctypes.byref(_C(6, A, A))) == rtq.RTQ_ERR_UNSUPPORTED
+    assert call(mode=rtq.RTQ_CODEBOOK_TILED, cb=ctypes.byref(_C(3, A, A)), R=None) == rtq.RTQ_ERR_UNSUPPORTED
+    assert call(mode=rtq.RTQ_CODEBOOK_I8_TILED, cb=ctypes.byref(_C(6, A, A)), R=None) == rtq.RTQ_ERR_UNSUPPORTED
+    assert call(mode=rtq.RTQ_CODEBOOK_I8_TILED, cb=ctypes.byref(_C(5, A, A))) == rtq.RTQ_ERR_UNSUPPORTED
+    assert call(mode=rtq.RTQ_CODEBOOK_TILED, cb=ctypes.byref(cb), rows=0) == rtq.RTQ_OK
+    assert call(mode=rtq.RTQ_CODEBOOK_I8_TILED, cb=ctypes.byref(cb), rows=0) == rtq.RTQ_OK
     R_bad_h = _R(256, 32, A, A)
     assert call(R=ctypes.byref(R_bad_h)) == rtq.RTQ_ERR_UNSUPPORTED
     R_misaligned = _R(256, 64, A + 2, A)
@@ -157,6 +166,15 @@ def test_qgemm_and_qlinear_validation():
     assert call({8: rtq.RTQ_CODEBOOK_I8, 9: ctypes.byref(cb4), 10: ctypes.byref(cb4), 12: rtq.RTQ_F32, 2: 0}) == \
         rtq.RTQ_ERR_UNSUPPORTED
     assert call({8: rtq.RTQ_CODEBOOK_I8, 9: ctypes.byref(cb4), 10: ctypes.byref(cb4), 2: 0}) == rtq.RTQ_OK
+    # the tiled codebook product takes the CODEBOOK_I8 arguments; CODEBOOK_TILED is a weight layout only
+    assert call({8: rtq.RTQ_CODEBOOK_I8_TILED, 9: ctypes.byref(cb4), 10: ctypes.byref(cb2), 2: 0}) == rtq.RTQ_OK
+    assert call({8: rtq.RTQ_CODEBOOK_I8_TILED, 9: ctypes.byref(cb4), 10: ctypes.byref(cb4), 12: rtq.RTQ_F32,
+                 2: 0}) == rtq.RTQ_ERR_UNSUPPORTED
+    assert call({8: rtq.RTQ_CODEBOOK_I8_TILED, 9: ctypes.byref(cb4), 10: ctypes.byref(cb6), 2: 0}) == \
+        rtq.RTQ_ERR_UNSUPPORTED
+    assert call({8: rtq.RTQ_CODEBOOK_TILED, 9: ctypes.byref(cb4), 10: ctypes.byref(cb4), 2: 0}) == \
+        rtq.RTQ_ERR_UNSUPPORTED
+    assert "RTQ_CODEBOOK_I8_TILED" in rtq.last_error()
     # output-row limits of the INT8-core product: one 256-row block of y spans at most 2^31 bytes
     assert call({6: (1 << 21) + 8, 12: rtq.RTQ_F32, 2: 0}) == rtq.RTQ_ERR_UNSUPPORTED
     assert call({6: (1 << 21) + 8, 12: rtq.RTQ_I32, 2: 0}) == rtq.RTQ_ERR_UNSUPPORTED
@@ -179,6 +197,10 @@ def test_qgemm_and_qlinear_validation():
     assert ws(4608, 4096, rtq.RTQ_CODEBOOK_I8, 3) == ws(4608, 4096, rtq.RTQ_CODEBOOK_I8, 6) == \
         ws(4608, 4096, rtq.RTQ_CODEBOOK_I8, 4)
     assert ws(4608, 4096, rtq.RTQ_CODEBOOK_I8, 5) == 0
+    assert ws(4608, 4096, rtq.RTQ_CODEBOOK_I8_TILED, 4) == ws(4608, 4096, rtq.RTQ_CODEBOOK_I8, 4)
+    assert ws(100, 256, rtq.RTQ_CODEBOOK_I8_TILED, 2) == 256 * 256 + 512 + split256   # rows padded to 256
+    assert ws(4608, 4096, rtq.RTQ_CODEBOOK_I8_TILED, 5) == 0
+    assert ws(4608, 4096, rtq.RTQ_CODEBOOK_TILED, 4) == 0                        # not a layer mode
     R = _R(256, 64, A, A)
     ql = lib.rtq_rotated_qlinear
     args = [A, rtq.RTQ_BF16, 16, ctypes.byref(R), A, A, rtq.RTQ_BF16, 32, rtq.RTQ_INT8, None, None, A, rtq.RTQ_BF16,
@@ -279,3 +301,30 @@ def test_asym_validation():
     assert ql(*a) == rtq.RTQ_ERR_UNSUPPORTED
     a = list(args); a[2] = 0
     assert ql(*a) == rtq.RTQ_OK
+
+
+def test_tile_helpers_follow_the_declared_layouts():
+    # the tests' host-side tilers against the byte offsets rtq.h defines for the two tiled layouts
+    rng = np.random.default_rng(5)
+    rows, d = 300, 256
+    q = rng.integers(-127, 128, size=(rows, d)).astype(np.int8)
+    t = tile_codes(q)
+    assert t.size == rtq.tiled_rows(rows) * d
+    for r, j in [(0, 0), (5, 17), (255, 255), (256, 64), (299, 130), (4, 200)]:
+        # block ((r/256)*(d/64) + j/64) * 16384, row (r%256) * 64, chunk ((j%64)/16) ^ ((r>>2)&3)
+        off = ((r // 256) * (d // 64) + j // 64) * 16384 + (r % 256) * 64 + \
+            ((((j % 64) // 16) ^ ((r >> 2) & 3)) * 16) + j % 16
+        assert t[off] == q[r, j]
+    assert not untile_codes(t, rtq.tiled_rows(rows), d)[rows:].any()
+    assert np.array_equal(untile_codes(t, rows, d), q)
+    for bits in (2, 3, 4):
+        wrow = d * bits // 8
+        c = rng.integers(0, 256, size=(rows, wrow)).astype(np.uint8)
+        tp = tile_packed(c, bits)
+        assert tp.size == rtq.tiled_code_bytes(rows, d, rtq.RTQ_CODEBOOK_TILED, bits)
+        for r, b in [(0, 0), (7, 3), (255, wrow - 1), (256, 8 * bits), (299, 5 * bits + 1)]:
+            # block ((r/256)*(d/64) + b/(8 bits)) of 256 * 8 bits bytes, row (r%256), byte b % (8 bits)
+            rb = 8 * bits
+            off = (((r // 256) * (d // 64) + b // rb) * 256 + r % 256) * rb + b % rb
+            assert tp[off] == c[r, b]
+        assert np.array_equal(untile_packed(tp, rows, d, bits), c)

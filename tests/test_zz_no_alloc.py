@@ -1,8 +1,8 @@
 """GPU test of the allocation-free layer (rtq_rotated_qlinear_noalloc) against the layer with a
 workspace (rtq_rotated_qlinear), through the C ABI: the same activation codes and the same exact
 int32 sums, so the outputs agree bit for bit.  Two calls in a row, the second on a smaller input
-(the static scratch keeps the first call's contents), in INT8 and codebook modes, at the W8A8 DiT
-shape and at small ragged shapes."""
+(the static scratch keeps the first call's contents), in INT8 and codebook modes (row-major and
+tiled), at the W8A8 DiT shape and at small ragged shapes."""
 import numpy as np
 import pytest
 
@@ -50,15 +50,17 @@ def test_noalloc_int8_matches_workspace_layer(d, N, tokens, mode):
         assert _same_bits(y, y_ref)
 
 
-@pytest.mark.parametrize("mode,bits_w", [(rtq.RTQ_CODEBOOK_I8, 4), (rtq.RTQ_CODEBOOK, 4), (rtq.RTQ_CODEBOOK_I8, 2)])
+@pytest.mark.parametrize("mode,bits_w", [(rtq.RTQ_CODEBOOK_I8, 4), (rtq.RTQ_CODEBOOK, 4), (rtq.RTQ_CODEBOOK_I8, 2),
+                                         (rtq.RTQ_CODEBOOK_I8_TILED, 4), (rtq.RTQ_CODEBOOK_I8_TILED, 2)])
 def test_noalloc_codebook_matches_workspace_layer(mode, bits_w):
     d, N = 4096, 1024
     R = rtq.Rpbh.from_seed(62, d)
     cb_a, cb_w = rtq.Codebook.for_dim(d, 4), rtq.Codebook.for_dim(d, bits_w)
     wh = workloads.f32_to_bf16_bits(workloads.small_case(7300, N, d, "w"))
-    wc = torch.empty((N, d * bits_w // 8), dtype=torch.uint8, device="cuda")
+    wmode = rtq.RTQ_CODEBOOK_TILED if mode == rtq.RTQ_CODEBOOK_I8_TILED else rtq.RTQ_CODEBOOK
+    wc = torch.empty(rtq.tiled_code_bytes(N, d, wmode, bits_w) or N * d * bits_w // 8, dtype=torch.uint8, device="cuda")
     wn = torch.empty(N, dtype=torch.bfloat16, device="cuda")
-    rtq.quantize_rows(to_dev(wh, "bf16"), wc, wn, R, rtq.RTQ_CODEBOOK, cb_w, 0.0)
+    rtq.quantize_rows(to_dev(wh, "bf16"), wc, wn, R, wmode, cb_w, 0.0)
     for T in (2000, 257):
         print(f"noalloc codebook mode={mode} bits_w={bits_w} T={T}", flush=True)
         x = to_dev(workloads.f32_to_bf16_bits(workloads.small_case(7400 + T, T, d, "t3")), "bf16")
