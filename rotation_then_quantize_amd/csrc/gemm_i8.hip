@@ -530,6 +530,19 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
         if (nk > 1) issue_stage(1);
         if (kCoded && nk > 2) issue_codes(2);
     };
+    // Partial tiles of split tiles are kept in the accumulators' own register layout, so a partial
+    // moves between registers and memory with no staging, each instruction covering a contiguous
+    // 1 KB: quad g (int32 elements 4g .. 4g + 3) of lane L's MFMA block (i, j) in wave w sits at
+    // byte ((((w * TM + i) * TN + j) * 4 + g) * 64 + L) * 16 of its 256 KB slot (the wave-uniform
+    // part of the offset goes in the instructions' scalar offset).
+    const int part_lane = 16 * lane;
+    const int part_wave = __builtin_amdgcn_readfirstlane(wave * TM * TN * 4 * 1024);
+    auto part_soff = [&](int i, int j, int g) { return part_wave + ((i * TN + j) * 4 + g) * 1024; };
+    auto part_rsrc = [&](int slot) {
+        return __builtin_amdgcn_make_buffer_rsrc(sp.partials + static_cast<size_t>(slot) * (BM * BN / 4), (short)0,
+                                                 BM * BN * 4, kBufferWord3);
+    };
+
     set_item(in_tail, lin);
     prefetch_early();
     load_scales();
@@ -663,15 +676,13 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
             RTQ_LDS_FENCE();   // the wave's rows are in LDS before they are read back
         };
 
-        // ---- split tile: publish this K range's partial (row-major int32 256 x 256, stored through
-        // the staging as whole rows); the last block of the tile to arrive runs the epilogue and
-        // adds the other partials there
+        // ---- split tile: publish this K range's partial; the last block of the tile to arrive adds
+        // the other partials into its accumulators and runs the epilogue.
         bool epilogue = true;
-        // Partial layout: row-major int32 quads; with bf16 output (where a lane of the epilogue
-        // reads quads 2c and 2c + 1 of a row) a wave's row slice holds its even quads, then its odd
-        // ones, so each load instruction there reads whole lines.
-        constexpr int kQuadsPerRow = WN / 4;
-        auto quad_pos = [](int c) { return kYKind == 1 ? (c & 1) * (kQuadsPerRow / 2) + (c >> 1) : c; };
+        // Partial layout: the accumulators' own register layout, so a partial moves between
+        // registers and memory with no staging, each instruction covering a contiguous 1 KB: quad
+        // g (int32 elements 4g .. 4g + 3) of lane L's MFMA block (i, j) in wave w sits at byte
+        // ((((w * TM + i) * TN + j) * 4 + g) * 64 + L) * 16 of the 256 KB slot.
         // Stream-K tiles have two pieces: the tile's head, the last piece of its run, and the tail,
         // the first piece of the next run, which is nearly always done first.  The tail stores its
         // partial and adds 1.  The head first adds 2: if the tail's 1 is there, the head finishes
@@ -692,22 +703,16 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
             publish = (static_cast<unsigned int>(s_flag[0]) & 1u) == 0u;
         }
         if (publish) {
-            const __amdgpu_buffer_rsrc_t rsm = __builtin_amdgcn_make_buffer_rsrc(
-                sp.partials + static_cast<size_t>(piece_slot(cfirst, cord)) * (BM * BN / 4), (short)0, BM * BN * 4,
-                kBufferWord3);
+            const __amdgpu_buffer_rsrc_t rsm = part_rsrc(piece_slot(cfirst, cord));
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                stage_block(i);
-#pragma unroll 1
-                for (int p = 0; p < kPassRows * kQuadsPerRow / 64; ++p) {
-                    const int q = p * 64 + lane;
-                    const int r = q / kQuadsPerRow, c = q % kQuadsPerRow;
-                    const v4i v = *reinterpret_cast<const v4i*>(stg + r * kPitch + swz(r, c));
-                    __builtin_amdgcn_raw_buffer_store_b128(v, rsm, ((wm * WM + i * 32 + r) * BN + wn * WN + 4 * quad_pos(c)) * 4,
-                                                           0, 0);
-                }
-                RTQ_LDS_FENCE();   // read back before the next block overwrites the region
-            }
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            v4i{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]}, rsm,
+                            part_lane, part_soff(i, j, g), 0);
             // All blocks of a split tile run on one XCD, so its L2 is the point of coherence: the
             // stores have reached it once they are acknowledged, the counter's atomic executes
             // there, and the last block reads the partials with loads that bypass its own L1.
@@ -722,27 +727,31 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
             __syncthreads();
             epilogue = s_flag[0] != 0;
         }
-        // int32 quad (4 consecutive columns) at (row, col) of the tile: mine plus the other K ranges'
-        const __amdgpu_buffer_rsrc_t rsp = __builtin_amdgcn_make_buffer_rsrc(
-            sp.partials, (short)0, static_cast<int>(2 * gridDim.x * (BM * BN * 4)), kBufferWord3);
-        // The other ranges' loads are issued back to back, so their latencies overlap (the branches
-        // are uniform: the split and the block's own range).
-        auto add_others = [&](v4i v, int row, int col) -> v4i {
-            if (ctail) {
-                v4i part[kMaxSplit];
+        // The finishing block adds the other pieces' partials (stored before their arrivals, read
+        // from the XCD's L2 past this block's L1) into its accumulators, one 32 x 32 MFMA block (four
+        // 1 KB loads per wave) at a time.
+        if (epilogue && ctail) {
+            for (int o = 0; o < ccount; ++o) {
+                if (o == cord) continue;
+                const __amdgpu_buffer_rsrc_t rso = part_rsrc(piece_slot(cfirst, o));
 #pragma unroll
-                for (int o = 0; o < kMaxSplit; ++o) {
-                    part[o] = v4i{0, 0, 0, 0};
-                    if (o < ccount && o != cord)
-                        part[o] = __builtin_amdgcn_raw_buffer_load_b128(
-                            rsp, (piece_slot(cfirst, o) * BM * BN + row * BN + wn * WN + 4 * quad_pos((col - wn * WN) >> 2)) * 4,
-                            0, kLoadL2);
-                }
+                for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int o = 0; o < kMaxSplit; ++o) v += part[o];
+                    for (int j = 0; j < TN; ++j) {
+                        v4i part[4];
+#pragma unroll
+                        for (int g = 0; g < 4; ++g)
+                            part[g] = __builtin_amdgcn_raw_buffer_load_b128(rso, part_lane, part_soff(i, j, g), kLoadL2);
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            acc[i][j][4 * g] += part[g].x;
+                            acc[i][j][4 * g + 1] += part[g].y;
+                            acc[i][j][4 * g + 2] += part[g].z;
+                            acc[i][j][4 * g + 3] += part[g].w;
+                        }
+                    }
             }
-            return v;
-        };
+        }
 
         // Zero points: sum_j (qa - za)(qw - zw) = acc - zw * sum(qa) - za * (sum(qw) - d zw), exact
         // in int32 (24-bit multiplies: |zero| <= 128, |sums| <= 2^22).
@@ -802,14 +811,13 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
                     constexpr int kQuads = kPerChunk / 4;               // 16-byte int32 chunks per output chunk
                     v4i out;
                     if (kYKind == 2) {
-                        out = correct(add_others(*reinterpret_cast<const v4i*>(src + swz(r, c)), trow, col), trow, col);
+                        out = correct(*reinterpret_cast<const v4i*>(src + swz(r, c)), trow, col);
                     } else {
                         const float as = s_as[trow];
                         float y[kPerChunk];
 #pragma unroll
                         for (int h4 = 0; h4 < kPerChunk / 4; ++h4) {
-                            const v4i a = correct(add_others(*reinterpret_cast<const v4i*>(src + swz(r, kQuads * c + h4)),
-                                                             trow, col + 4 * h4),
+                            const v4i a = correct(*reinterpret_cast<const v4i*>(src + swz(r, kQuads * c + h4)),
                                                   trow, col + 4 * h4);
                             y[4 * h4 + 0] = static_cast<float>(a.x) * as * wsl[4 * h4 + 0];
                             y[4 * h4 + 1] = static_cast<float>(a.y) * as * wsl[4 * h4 + 1];
