@@ -282,6 +282,7 @@ def bench_codebook(args, torch, rtq, workloads, variant, mode=None):
     quant_burst = _burst_ms(max(20, steps), quant, torch)
     flops = 2.0 * T * d * N
     q_bytes = T * (2 * d + (d if i8 else d * bits_a // 8) + 4)
+    q_bytes_packed = T * (2 * d + d * bits_a // 8 + 4)   # the method's bytes: codes packed to bits_a
     gemm_tflops = flops / (tg.mean() * 1e-3) / 1e12
     peak = PEAK_INT8_TOPS if i8 else PEAK_F16_TFLOPS
     name = ("codebook on INT8 MFMA (int8 codebook values)" + (", tiled operands" if tiled else ", row-major operands")
@@ -293,7 +294,9 @@ def bench_codebook(args, torch, rtq, workloads, variant, mode=None):
             "gemm_ms": float(tg.mean()), "TFLOP/s": flops / (wall / steps) / 1e12,
             "gemm_TFLOP/s": gemm_tflops, "gemm_peak": peak, "gemm_frac_peak": gemm_tflops / peak,
             "rpbh_bytes": q_bytes, "rpbh_GB/s": q_bytes / (quant_burst * 1e-3) / 1e9,
-            "rpbh_frac_hbm": q_bytes / (quant_burst * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+            "rpbh_frac_hbm": q_bytes / (quant_burst * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            "rpbh_bytes_packed_codes": q_bytes_packed,
+            "rpbh_frac_hbm_packed_codes": q_bytes_packed / (quant_burst * 1e-3) / 1e9 / PEAK_HBM_GBPS}
 
 
 def bench_w8a8_asym(args, torch, rtq, workloads):
