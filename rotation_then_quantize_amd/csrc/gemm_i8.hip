@@ -798,65 +798,124 @@ gemm_i8_kernel(const int8_t* __restrict__ A, const float* __restrict__ a_scale, 
             const __amdgpu_buffer_rsrc_t rsy = __builtin_amdgcn_make_buffer_rsrc(
                 static_cast<int8_t*>(Y) + cm0 * N * kOutBytes, (short)0, static_cast<int>(rows_y * N * kOutBytes),
                 kBufferWord3);
+            if constexpr (kYKind == 1 && !kAsym) {
+                // bf16 output: each lane scales and converts its accumulators where they are (token
+                // row fr, columns 8g + 4fh .. +3 of block j), stages them as bf16 rows (half the LDS
+                // bytes of int32 staging) and reads back whole 16-byte chunks to store.  The 16-byte
+                // chunk k of a staged row r sits at chunk k ^ ((r >> 1) & 7): both the 8-byte writes (32
+                // rows at once) and the 16-byte reads (8 rows) then touch every bank equally often.
+                // Same arithmetic as below: (float(acc) * a_t) * w_n, rounded to bf16 once.
+                constexpr int kRowB = WN * 2;                          // a wave's 64 bf16 outputs of a row
+                static_assert(kPassRows * kRowB <= kPassRows * kPitch, "fits the wave's staging region");
+                float4 wsv[TN][4];
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                stage_block(i);
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        wsv[j][g] = *reinterpret_cast<const float4*>(s_ws + wn * WN + j * 32 + 8 * g + 4 * fh);
+#pragma unroll
+                for (int i = 0; i < TM; ++i) {
+                    const float as = s_as[wm * WM + i * 32 + fr];
+                    int8_t* wrow = stg + fr * kRowB;
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            const float y0 = static_cast<float>(acc[i][j][4 * g]) * as * wsv[j][g].x;
+                            const float y1 = static_cast<float>(acc[i][j][4 * g + 1]) * as * wsv[j][g].y;
+                            const float y2 = static_cast<float>(acc[i][j][4 * g + 2]) * as * wsv[j][g].z;
+                            const float y3 = static_cast<float>(acc[i][j][4 * g + 3]) * as * wsv[j][g].w;
+                            *reinterpret_cast<uint2*>(wrow + ((((4 * j + g) ^ ((fr >> 1) & 7)) << 4) + 8 * fh)) =
+                                make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
+                        }
+                    RTQ_LDS_FENCE();   // the wave's rows are in LDS before they are read back
 #pragma unroll 1
-                for (int p = 0; p < kChunksPerLane; ++p) {
-                    const int q = p * 64 + lane;
-                    const int r = q / kChunksPerRow, c = q % kChunksPerRow;
-                    const int trow = wm * WM + i * 32 + r;              // row within the tile
-                    const int col = wn * WN + c * kPerChunk;            // column within the tile
-                    const int8_t* src = stg + r * kPitch;
-                    constexpr int kQuads = kPerChunk / 4;               // 16-byte int32 chunks per output chunk
-                    v4i out;
-                    if (kYKind == 2) {
-                        out = correct(*reinterpret_cast<const v4i*>(src + swz(r, c)), trow, col);
-                    } else {
-                        const float as = s_as[trow];
-                        float y[kPerChunk];
-#pragma unroll
-                        for (int h4 = 0; h4 < kPerChunk / 4; ++h4) {
-                            const v4i a = correct(*reinterpret_cast<const v4i*>(src + swz(r, kQuads * c + h4)),
-                                                  trow, col + 4 * h4);
-                            y[4 * h4 + 0] = static_cast<float>(a.x) * as * wsl[4 * h4 + 0];
-                            y[4 * h4 + 1] = static_cast<float>(a.y) * as * wsl[4 * h4 + 1];
-                            y[4 * h4 + 2] = static_cast<float>(a.z) * as * wsl[4 * h4 + 2];
-                            y[4 * h4 + 3] = static_cast<float>(a.w) * as * wsl[4 * h4 + 3];
-                        }
-                        if (kYKind == 0) {
-                            out = v4i{static_cast<int>(__float_as_uint(y[0])), static_cast<int>(__float_as_uint(y[1])),
-                                      static_cast<int>(__float_as_uint(y[2])), static_cast<int>(__float_as_uint(y[3]))};
+                    for (int p = 0; p < kChunksPerLane; ++p) {
+                        const int q = p * 64 + lane;
+                        const int r = q / kChunksPerRow, c = q % kChunksPerRow;
+                        const int trow = wm * WM + i * 32 + r;
+                        const int col = wn * WN + c * kPerChunk;
+                        const v4i out = *reinterpret_cast<const v4i*>(stg + r * kRowB + ((c ^ ((r >> 1) & 7)) << 4));
+                        const int64_t n = cn0 + col;
+                        const uint32_t off = (static_cast<uint32_t>(trow) * static_cast<uint32_t>(N) +
+                                              static_cast<uint32_t>(n)) * kOutBytes;
+                        if (kVec) {
+                            __builtin_amdgcn_raw_buffer_store_b128(out, rsy, static_cast<int>(n < N ? off : kOob), 0,
+                                                                   kStoreNT);
                         } else {
-                            uint32_t w[4];
+                            const uint32_t w[4] = {static_cast<uint32_t>(out.x), static_cast<uint32_t>(out.y),
+                                                   static_cast<uint32_t>(out.z), static_cast<uint32_t>(out.w)};
 #pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                w[e] = pack_bf16x2(y[2 * e], y[2 * e + 1]);
-                            out = v4i{static_cast<int>(w[0]), static_cast<int>(w[1]), static_cast<int>(w[2]),
-                                      static_cast<int>(w[3])};
+                            for (int e = 0; e < kPerChunk; ++e) {
+                                const int o = static_cast<int>(n + e < N ? off + e * kOutBytes : kOob);
+                                __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1))),
+                                                                      rsy, o, 0, kStoreNT);
+                            }
                         }
                     }
-                    const int64_t n = cn0 + col;
-                    const uint32_t off = (static_cast<uint32_t>(trow) * static_cast<uint32_t>(N) +
-                                          static_cast<uint32_t>(n)) * kOutBytes;
-                    if (kVec) {
-                        __builtin_amdgcn_raw_buffer_store_b128(out, rsy, static_cast<int>(n < N ? off : kOob), 0,
-                                                               kStoreNT);
-                    } else {
-                        const uint32_t w[4] = {static_cast<uint32_t>(out.x), static_cast<uint32_t>(out.y),
-                                               static_cast<uint32_t>(out.z), static_cast<uint32_t>(out.w)};
-#pragma unroll
-                        for (int e = 0; e < kPerChunk; ++e) {
-                            const int o = static_cast<int>(n + e < N ? off + e * kOutBytes : kOob);
-                            if (kOutBytes == 4)
-                                __builtin_amdgcn_raw_buffer_store_b32(w[e], rsy, o, 0, kStoreNT);
-                            else
-                                __builtin_amdgcn_raw_buffer_store_b16(
-                                    static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1))), rsy, o, 0, kStoreNT);
-                        }
-                    }
+                    RTQ_LDS_FENCE();   // read back before the next block overwrites the region
                 }
-                RTQ_LDS_FENCE();   // read back before the next pass overwrites the region
+            } else {
+#pragma unroll
+                for (int i = 0; i < TM; ++i) {
+                    stage_block(i);
+#pragma unroll 1
+                    for (int p = 0; p < kChunksPerLane; ++p) {
+                        const int q = p * 64 + lane;
+                        const int r = q / kChunksPerRow, c = q % kChunksPerRow;
+                        const int trow = wm * WM + i * 32 + r;              // row within the tile
+                        const int col = wn * WN + c * kPerChunk;            // column within the tile
+                        const int8_t* src = stg + r * kPitch;
+                        constexpr int kQuads = kPerChunk / 4;               // 16-byte int32 chunks per output chunk
+                        v4i out;
+                        if (kYKind == 2) {
+                            out = correct(*reinterpret_cast<const v4i*>(src + swz(r, c)), trow, col);
+                        } else {
+                            const float as = s_as[trow];
+                            float y[kPerChunk];
+#pragma unroll
+                            for (int h4 = 0; h4 < kPerChunk / 4; ++h4) {
+                                const v4i a = correct(*reinterpret_cast<const v4i*>(src + swz(r, kQuads * c + h4)),
+                                                      trow, col + 4 * h4);
+                                y[4 * h4 + 0] = static_cast<float>(a.x) * as * wsl[4 * h4 + 0];
+                                y[4 * h4 + 1] = static_cast<float>(a.y) * as * wsl[4 * h4 + 1];
+                                y[4 * h4 + 2] = static_cast<float>(a.z) * as * wsl[4 * h4 + 2];
+                                y[4 * h4 + 3] = static_cast<float>(a.w) * as * wsl[4 * h4 + 3];
+                            }
+                            if (kYKind == 0) {
+                                out = v4i{static_cast<int>(__float_as_uint(y[0])), static_cast<int>(__float_as_uint(y[1])),
+                                          static_cast<int>(__float_as_uint(y[2])), static_cast<int>(__float_as_uint(y[3]))};
+                            } else {
+                                uint32_t w[4];
+#pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    w[e] = pack_bf16x2(y[2 * e], y[2 * e + 1]);
+                                out = v4i{static_cast<int>(w[0]), static_cast<int>(w[1]), static_cast<int>(w[2]),
+                                          static_cast<int>(w[3])};
+                            }
+                        }
+                        const int64_t n = cn0 + col;
+                        const uint32_t off = (static_cast<uint32_t>(trow) * static_cast<uint32_t>(N) +
+                                              static_cast<uint32_t>(n)) * kOutBytes;
+                        if (kVec) {
+                            __builtin_amdgcn_raw_buffer_store_b128(out, rsy, static_cast<int>(n < N ? off : kOob), 0,
+                                                                   kStoreNT);
+                        } else {
+                            const uint32_t w[4] = {static_cast<uint32_t>(out.x), static_cast<uint32_t>(out.y),
+                                                   static_cast<uint32_t>(out.z), static_cast<uint32_t>(out.w)};
+#pragma unroll
+                            for (int e = 0; e < kPerChunk; ++e) {
+                                const int o = static_cast<int>(n + e < N ? off + e * kOutBytes : kOob);
+                                if (kOutBytes == 4)
+                                    __builtin_amdgcn_raw_buffer_store_b32(w[e], rsy, o, 0, kStoreNT);
+                                else
+                                    __builtin_amdgcn_raw_buffer_store_b16(
+                                        static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1))), rsy, o, 0, kStoreNT);
+                            }
+                        }
+                    }
+                    RTQ_LDS_FENCE();   // read back before the next pass overwrites the region
+                }
             }
         }
         RTQ_BARRIER();   // every wave is done with the staging slots and the scales
